@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the tests, the benchmark and the oracle checks.  It
+holds no attention arithmetic: only random draws, dtype casts and the input-side
+quantisers that turn float draws into the low-precision operands (fp8 e4m3
+tensors with a per-tensor scale, an int8 KV cache with per-token-per-head fp16
+scales).  The GPU library never imports it.
+
+Recipe (the same on every device; ``device`` only chooses where the generator
+runs, so CPU and GPU draws differ but each is deterministic for a given seed):
+
+* a torch.Generator on ``device`` seeded with ``seed`` draws float32 N(0,1) in the
+  order Q, K, V (BHSD shapes), then the outlier row indices; casts to bf16/fp16
+  round to nearest even;
+* long-context outlier keys: per (batch, kv head), exactly round(0.01 * Sk)
+  distinct key rows picked by a seeded permutation are multiplied by 8 in float32
+  before the cast (a power-of-two factor, so the multiply is exact);
+* fp8: per-tensor scale s = float32(absmax / 448); codes = E4M3FN(x / s), round to
+  nearest even, clamped to +-448 before the cast;
+* int8 KV cache: per (batch, kv head, token) scale sc = fp16(absmax_over_d / 127);
+  code = clamp(rint(x / float(sc)), -127, 127), 0 where sc == 0.  The decode cache
+  is drawn one batch entry at a time (seed (seed << 20) + b, K then V) so that no
+  full-size float32 temporary is needed; the query uses seed (seed << 20) + B.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+E4M3_MAX = 448.0
+INT8_QMAX = 127
+
+
+@dataclass(frozen=True)
+class FwdConfig:
+    name: str
+    dtype: str  # "f32" | "bf16" | "f16" | "fp8"
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    d: int
+    causal: bool
+    outlier_frac: float = 0.0
+    out_dtype: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    d: int
+    num_splits: int
+    seq_lens: tuple = field(default=())
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The five workloads: a tiny fp32 case, causal bf16 prefill, long-context GQA
+# prefill with outlier keys, fp8 prefill and int8-KV split decode.
+CONFIGS = {
+    "fp32_s128_d64": FwdConfig("fp32_s128_d64", "f32", 1, 1, 1, 128, 128, 64, False),
+    "bf16_b4_h16_s2048_causal": FwdConfig("bf16_b4_h16_s2048_causal", "bf16", 4, 16, 16, 2048, 2048, 128, True),
+    "bf16_gqa32x8_s16384_causal_outlier": FwdConfig(
+        "bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
+    "fp8_b8_h16_s4096": FwdConfig("fp8_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128, False, out_dtype="bf16"),
+    "decode_int8_b64_gqa32x8_L32768": DecodeConfig("decode_int8_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16),
+}
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def quantize_fp8_per_tensor(x: torch.Tensor):
+    """float tensor -> (E4M3FN codes as torch.float8_e4m3fn, float32 scale).
+
+    s = absmax / 448 in float32; codes = RNE(x / s) clamped to +-448."""
+    xf = x.float()
+    amax = xf.abs().max()
+    s = (amax / E4M3_MAX).to(torch.float32)
+    if float(s) == 0.0:
+        s = torch.tensor(1.0, dtype=torch.float32, device=x.device)
+    y = (xf / s).clamp_(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn), float(s)
+
+
+def quantize_int8_tokhead(x: torch.Tensor):
+    """float tensor [..., T, d] -> (int8 codes [..., T, d], fp16 scales [..., T]).
+
+    Symmetric per-token scale sc = fp16(absmax_d / 127); code = clamp(rint(x/sc))."""
+    xf = x.float()
+    amax = xf.abs().amax(dim=-1)
+    sc = (amax / INT8_QMAX).to(torch.float16)
+    scf = sc.float()
+    safe = torch.where(scf > 0, scf, torch.ones_like(scf))
+    qv = torch.round(xf / safe[..., None]).clamp_(-INT8_QMAX, INT8_QMAX)
+    qv = torch.where(scf[..., None] > 0, qv, torch.zeros_like(qv))
+    return qv.to(torch.int8), sc
+
+
+def make_fwd_inputs(cfg: FwdConfig, seed: int = 0, device="cpu"):
+    """Returns a dict with q, k, v (in the config's input dtype) and, for fp8,
+    the float32 per-tensor scales q_scale, k_scale, v_scale."""
+    g = _gen(device, seed)
+    qf = torch.randn(cfg.B, cfg.Hq, cfg.Sq, cfg.d, generator=g, device=device, dtype=torch.float32)
+    kf = torch.randn(cfg.B, cfg.Hkv, cfg.Sk, cfg.d, generator=g, device=device, dtype=torch.float32)
+    vf = torch.randn(cfg.B, cfg.Hkv, cfg.Sk, cfg.d, generator=g, device=device, dtype=torch.float32)
+    if cfg.outlier_frac > 0:
+        n_out = int(round(cfg.outlier_frac * cfg.Sk))
+        for b in range(cfg.B):
+            for h in range(cfg.Hkv):
+                idx = torch.randperm(cfg.Sk, generator=g, device=device)[:n_out]
+                kf[b, h, idx] *= 8.0
+    if cfg.dtype == "fp8":
+        q8, qs = quantize_fp8_per_tensor(qf)
+        k8, ks = quantize_fp8_per_tensor(kf)
+        v8, vs = quantize_fp8_per_tensor(vf)
+        return {"q": q8, "k": k8, "v": v8, "q_scale": qs, "k_scale": ks, "v_scale": vs}
+    dt = _TORCH_DT[cfg.dtype]
+    return {"q": qf.to(dt), "k": kf.to(dt), "v": vf.to(dt)}
+
+
+def make_decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):
+    """Returns q [B,Hq,d] bf16, k/v codes [B,Hkv,L,d] int8, k/v scales [B,Hkv,L]
+    fp16 and seq_lens [B] int32 (all L unless the config lists lengths)."""
+    B, Hkv, L, d = cfg.B, cfg.Hkv, cfg.L, cfg.d
+    kc = torch.empty(B, Hkv, L, d, dtype=torch.int8, device=device)
+    vc = torch.empty(B, Hkv, L, d, dtype=torch.int8, device=device)
+    ks = torch.empty(B, Hkv, L, dtype=torch.float16, device=device)
+    vs = torch.empty(B, Hkv, L, dtype=torch.float16, device=device)
+    for b in range(B):
+        g = _gen(device, (seed << 20) + b)
+        kf = torch.randn(Hkv, L, d, generator=g, device=device, dtype=torch.float32)
+        kc[b], ks[b] = quantize_int8_tokhead(kf)
+        del kf
+        vf = torch.randn(Hkv, L, d, generator=g, device=device, dtype=torch.float32)
+        vc[b], vs[b] = quantize_int8_tokhead(vf)
+        del vf
+    g = _gen(device, (seed << 20) + B)
+    q = torch.randn(B, cfg.Hq, d, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    if cfg.seq_lens:
+        lens = torch.tensor(cfg.seq_lens, dtype=torch.int32, device=device)
+    else:
+        lens = torch.full((B,), L, dtype=torch.int32, device=device)
+    return {"q": q, "k": kc, "v": vc, "k_scale": ks, "v_scale": vs, "seq_lens": lens}

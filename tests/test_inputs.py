@@ -1,0 +1,80 @@
+"""The seeded input generators and input-side quantisers (CPU only)."""
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import fa_inputs
+from oracle.e4m3 import e4m3_decode
+
+
+def test_int8_tokhead_quantiser_bounds():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(2, 3, 50, 128, generator=g)
+    x[0, 0, 7] = 0.0  # an all-zero token gets scale 0 and codes 0
+    codes, sc = fa_inputs.quantize_int8_tokhead(x)
+    assert codes.dtype == torch.int8 and sc.dtype == torch.float16
+    assert int(codes.abs().max()) <= 127
+    assert float(sc[0, 0, 7]) == 0.0 and int(codes[0, 0, 7].abs().max()) == 0
+    assert torch.equal(sc, (x.abs().amax(-1) / 127).to(torch.float16))
+    err = (x.double() - codes.double() * sc.double()[..., None]).abs()
+    assert bool((err <= sc.double()[..., None] / 2 * (1 + 1e-6) + 1e-12).all())
+
+
+def test_fp8_quantiser_scale_absmax_and_rounding():
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(4, 1000, generator=g)
+    codes, s = fa_inputs.quantize_fp8_per_tensor(x)
+    assert s == float((x.abs().max() / 448.0).to(torch.float32))
+    vals = e4m3_decode(codes)
+    i = int(x.abs().argmax())
+    assert abs(vals.reshape(-1)[i]) == 448.0
+    # round-to-nearest against the decoded table, brute force over all codes
+    table = e4m3_decode(np.arange(256, dtype=np.uint8))
+    finite = ~np.isnan(table)
+    y = (x.double() / s).numpy().reshape(-1)[:2000]
+    got = vals.reshape(-1)[:2000]
+    dist = np.abs(y[:, None] - table[None, finite])
+    best = dist.min(axis=1)
+    assert np.all(np.abs(np.abs(y - got) - best) <= 1e-12 * np.maximum(1, np.abs(y)))
+
+
+def test_outlier_rows_exactly_one_percent_times_eight():
+    cfg = dataclasses.replace(fa_inputs.CONFIGS["bf16_gqa32x8_s16384_causal_outlier"],
+                              Hq=4, Hkv=2, Sq=300, Sk=300, d=16)
+    a = fa_inputs.make_fwd_inputs(cfg, seed=0)
+    plain = dataclasses.replace(cfg, outlier_frac=0.0)
+    b = fa_inputs.make_fwd_inputs(plain, seed=0)
+    assert torch.equal(a["q"], b["q"])
+    ratio = a["k"].float() / b["k"].float()
+    rows = (ratio.abs() > 4).all(dim=-1)  # outlier rows are x8 in every channel
+    assert rows.sum(dim=-1).tolist() == [[3, 3]]  # round(0.01 * 300) per kv head
+    assert torch.allclose(ratio[rows], torch.full_like(ratio[rows], 8.0), rtol=0.02)
+    assert torch.equal(a["k"][~rows], b["k"][~rows])
+
+
+def test_generators_are_deterministic():
+    cfg = dataclasses.replace(fa_inputs.CONFIGS["fp8_b8_h16_s4096"], B=1, Hq=2, Hkv=2, Sq=64, Sk=64)
+    a = fa_inputs.make_fwd_inputs(cfg, seed=5)
+    b = fa_inputs.make_fwd_inputs(cfg, seed=5)
+    assert torch.equal(a["q"].view(torch.uint8), b["q"].view(torch.uint8)) and a["v_scale"] == b["v_scale"]
+    dc = dataclasses.replace(fa_inputs.CONFIGS["decode_int8_b64_gqa32x8_L32768"], B=2, L=64)
+    x = fa_inputs.make_decode_inputs(dc, seed=1)
+    y = fa_inputs.make_decode_inputs(dc, seed=1)
+    assert all(torch.equal(x[n], y[n]) for n in x)
+    assert x["q"].shape == (2, 32, 128) and x["k"].shape == (2, 8, 64, 128)
+    assert x["seq_lens"].tolist() == [64, 64]
+
+
+def test_config_table_matches_workloads():
+    c = fa_inputs.CONFIGS
+    assert (c["fp32_s128_d64"].Sq, c["fp32_s128_d64"].d, c["fp32_s128_d64"].causal) == (128, 64, False)
+    x = c["bf16_b4_h16_s2048_causal"]
+    assert (x.B, x.Hq, x.Sq, x.d, x.causal) == (4, 16, 2048, 128, True)
+    x = c["bf16_gqa32x8_s16384_causal_outlier"]
+    assert (x.Hq, x.Hkv, x.Sq, x.outlier_frac) == (32, 8, 16384, 0.01)
+    x = c["fp8_b8_h16_s4096"]
+    assert (x.B, x.Hq, x.Sq, x.causal, x.dtype) == (8, 16, 4096, False, "fp8")
+    x = c["decode_int8_b64_gqa32x8_L32768"]
+    assert (x.B, x.Hq, x.Hkv, x.L, x.num_splits) == (64, 32, 8, 32768, 16)
