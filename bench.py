@@ -1,0 +1,296 @@
+"""Throughput of the exact tiled attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--extra all|none|NAME,...] [--no-cpu-baseline]
+
+A step is one call of the hot path over one batch of synthetic input already
+resident in HBM.  The headline workload is causal bf16 prefill, B=4, H=16,
+S=2048, d=128 with LSE output; its TFLOP/s counts 4*d flops per visible
+(query, key) pair (S*(S+1)/2 pairs per head under the causal mask).  The other
+workloads are timed the same way and reported under "workloads": long-context
+GQA prefill and fp8 prefill in TFLOP/s, int8-KV split decode in GB/s of the
+bytes the method must move (K/V codes + scales + query + output + LSE).
+
+Timing uses HIP events on the stream the kernels are launched on (torch's
+current stream), bracketed by device synchronisations.  The CPU baseline is the
+float64 oracle timed on this host's cores over a bounded sample of the headline
+workload, rescaled to the same unit.  Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fa_inputs  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % MFMA peak; decode KV GB/s and % HBM peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "bf16_b4_h16_s2048_causal"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ---- algorithmic work ---------------------------------------------------------
+
+def visible_pairs(Sq: int, Sk: int, causal: bool) -> int:
+    """(query, key) pairs the mask leaves visible in one head."""
+    if not causal:
+        return Sq * Sk
+    # row i sees min(Sk, max(0, i + Sk - Sq + 1)) keys
+    off = Sk - Sq
+    return sum(min(Sk, max(0, i + off + 1)) for i in range(Sq))
+
+
+def fwd_flops(cfg) -> int:
+    """2*d flops for S = Q K^T plus 2*d for O = P V, per visible pair per head."""
+    return 4 * cfg.d * visible_pairs(cfg.Sq, cfg.Sk, cfg.causal) * cfg.B * cfg.Hq
+
+
+def fwd_hbm_bytes(cfg) -> int:
+    """Compulsory HBM bytes of one prefill: Q, K, V read once, O (and LSE) written."""
+    es = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}[cfg.dtype]
+    oes = 4 if cfg.dtype == "f32" else 2
+    q = cfg.B * cfg.Hq * cfg.Sq * cfg.d * es
+    kv = 2 * cfg.B * cfg.Hkv * cfg.Sk * cfg.d * es
+    o = cfg.B * cfg.Hq * cfg.Sq * cfg.d * oes
+    lse = cfg.B * cfg.Hq * cfg.Sq * 4
+    return q + kv + o + lse
+
+
+def decode_bytes(cfg) -> int:
+    """KV bytes = 2 * layers * batch * tokens * kv_heads * head_dim * bytes_per_elem
+    with one layer and 1-byte codes, plus the per-token fp16 scales of K and V,
+    the bf16 query, the bf16 output and the float32 LSE."""
+    kv = 2 * 1 * cfg.B * cfg.L * cfg.Hkv * cfg.d * 1
+    scales = 2 * cfg.B * cfg.Hkv * cfg.L * 2
+    q = cfg.B * cfg.Hq * cfg.d * 2
+    o = cfg.B * cfg.Hq * cfg.d * 2
+    lse = cfg.B * cfg.Hq * 4
+    return kv + scales + q + o + lse
+
+
+# ---- GPU timing ---------------------------------------------------------------
+
+def _time_region(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall
+
+
+def _fwd_runner(cfg, seed=0):
+    import torch
+
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_fwd_inputs(cfg, seed=seed, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.bfloat16}[cfg.dtype]
+    o = torch.empty(q.shape, dtype=odt, device="cuda")
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda")
+    ds = (x.get("q_scale", 1.0), x.get("k_scale", 1.0), x.get("v_scale", 1.0))
+
+    def run():
+        fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale,
+                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
+
+    return run
+
+
+def _decode_runner(cfg, seed=0):
+    import torch
+
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_decode_inputs(cfg, seed=seed, device="cuda")
+    o = torch.empty(cfg.B, cfg.Hq, cfg.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(cfg.B, cfg.Hq, dtype=torch.float32, device="cuda")
+    ws = fa.decode_workspace(cfg.B, cfg.Hq, cfg.d, cfg.num_splits)
+
+    def run():
+        fa.fa_decode_kvq(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], o, lse,
+                         seq_lens=x["seq_lens"], num_splits=cfg.num_splits,
+                         softmax_scale=cfg.scale, workspace=ws)
+
+    return run
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources, to tie stored counter readings to a build."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_exact_attention_fa_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def measure(name, steps, warmup):
+    cfg = fa_inputs.CONFIGS[name]
+    import torch
+
+    if isinstance(cfg, fa_inputs.DecodeConfig):
+        run = _decode_runner(cfg)
+        ms, wall = _time_region(run, steps, warmup)
+        work = decode_bytes(cfg)
+        gbs = work / (ms * 1e-3) / 1e9
+        res = {"unit": "GB/s", "value": gbs, "ms_per_call": ms, "bytes_per_call": work,
+               "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic(name)}}
+    else:
+        run = _fwd_runner(cfg)
+        ms, wall = _time_region(run, steps, warmup)
+        work = fwd_flops(cfg)
+        tf = work / (ms * 1e-3) / 1e12
+        peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+        res = {"unit": "TFLOP/s", "value": tf, "ms_per_call": ms, "flops_per_call": work,
+               "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                            "frac": tf / peak, "traffic": stored_traffic(name)}}
+        if cfg.dtype == "fp8":
+            res["frac_of_fp8_peak"] = tf / PEAK_FP8_TFLOPS
+    res["wall_s"] = wall
+    del run
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---- CPU baseline -------------------------------------------------------------
+
+def cpu_baseline(name, budget_s=12.0):
+    """The float64 oracle on this host's cores over whole heads of the workload,
+    as many as fit the time budget; reported in the workload's own unit."""
+    import oracle
+
+    cfg = fa_inputs.CONFIGS[name]
+    cores = len(os.sched_getaffinity(0))
+    x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cpu")
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    # calibrate on as many heads as there are cores, then scale up to the budget
+    n = min(len(heads), cores)
+    t0 = time.perf_counter()
+    oracle.attention_fp64(x["q"], x["k"], x["v"], cfg.causal, cfg.scale, heads=heads[:n], threads=cores)
+    dt = time.perf_counter() - t0
+    done, elapsed = n, dt
+    while done < len(heads) and elapsed + dt * 1.2 < budget_s:
+        m = min(len(heads) - done, n)
+        t0 = time.perf_counter()
+        oracle.attention_fp64(x["q"], x["k"], x["v"], cfg.causal, cfg.scale,
+                              heads=heads[done:done + m], threads=cores)
+        dt = time.perf_counter() - t0
+        done += m
+        elapsed += dt
+    flops = fwd_flops(cfg) * done / len(heads)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) pairs of {name}, float64 numpy two-pass, "
+                      f"{elapsed:.1f} s wall"}
+
+
+# ---- main ---------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--extra", default="all", help="other workloads to time: all, none or a comma list")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the path runs on a single device and has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_exact_attention_fa_amd as fa
+
+    fa.load()
+    torch.cuda.set_device(0)
+    head = measure(a.workload, a.steps, a.warmup)
+    cfg = fa_inputs.CONFIGS[a.workload]
+
+    extras = {}
+    names = [n for n in fa_inputs.CONFIGS if n != a.workload]
+    if a.extra == "none":
+        names = []
+    elif a.extra != "all":
+        names = [n for n in a.extra.split(",") if n]
+    for n in names:
+        try:
+            extras[n] = measure(n, max(3, a.steps // 5), max(2, a.warmup // 2))
+        except Exception as e:  # an unbuilt kernel is reported, not hidden
+            extras[n] = {"error": f"{type(e).__name__}: {e}"}
+        print(f"# {n}: {json.dumps(extras[n])}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not a.no_cpu_baseline and isinstance(cfg, fa_inputs.FwdConfig):
+        cpu = cpu_baseline(a.workload)
+
+    dtype = {"f32": "f32", "bf16": "bf16", "f16": "f16", "fp8": "fp8_e4m3"}.get(getattr(cfg, "dtype", ""), "bf16")
+    conf = {"workload": a.workload}
+    if isinstance(cfg, fa_inputs.FwdConfig):
+        conf.update({"B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "seq_len": cfg.Sq, "d": cfg.d,
+                     "causal": cfg.causal, "lse": True})
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": conf,
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "workloads": extras,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

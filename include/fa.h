@@ -1,0 +1,164 @@
+/*
+ * fa.h — C ABI of libfa: exact tiled attention for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The textbook attention of the FlashAttention interview
+ * canvas (panel 1, "standard attention" box) — scores S = Q K^T scaled by
+ * softmax_scale, P = softmax(S) per query row, O = P V — evaluated tile by tile
+ * with the online-softmax state (running max m, rescaled sum l, accumulator O;
+ * panel 1 "online softmax key state" box and panel 3, Q2) so that the score
+ * matrix never reaches device memory.  The tiled result equals the textbook one
+ * up to floating-point rounding (panel 1, "one-sentence answer" box).  The
+ * forward also returns the per-row statistic LSE_i = ln sum_j exp(s_ij) that a
+ * recomputing backward needs (panel 3, Q3).
+ *
+ * Two entry points do work:
+ *   fa_fwd         prefill (KV-cache quantisation overview, section 1, "prefill"):
+ *                  every query row of a sequence against its keys, optional
+ *                  causal mask, grouped-query heads, optional LSE output;
+ *                  fp32, bf16, fp16 or fp8-e4m3 inputs.
+ *   fa_decode_kvq  one decode step (same page, section 1, "decode step"): one new
+ *                  query token per sequence against the whole cache, read from an
+ *                  int8 cache with per-token-per-head scales and dequantised inside
+ *                  the kernel (section 3, "read path"); the cache is split into
+ *                  chunks processed in parallel and merged by their log-sum-exps.
+ *
+ * Conventions shared by every call.
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
+ *     caller owns every buffer; the library allocates nothing and keeps no state,
+ *     so calls from several host threads are safe.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy default
+ *     stream) and return after enqueueing.  Nothing synchronises implicitly.
+ *   - Parameters are validated on the host before anything is launched; on a
+ *     validation error the call returns a negative fa_status and launches
+ *     nothing.  A failed launch returns FA_ERR_HIP.  Faults inside a kernel are
+ *     reported by the runtime at the caller's next synchronisation.
+ *   - fa_last_error() gives a human-readable reason for the last failing call on
+ *     the calling thread.
+ *   - Tensors are described by element strides for the batch, head and sequence
+ *     axes; the head-dimension stride is always 1.  Base pointers must be 16-byte
+ *     aligned and the strides must keep every row 16-byte aligned
+ *     (FA_ERR_ALIGNMENT otherwise).  Rows of one sequence must not overlap
+ *     (sequence stride >= d), and one (batch, head) slice must span less than
+ *     2^31 bytes (FA_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t passed as an opaque handle, so this header needs no HIP include. */
+typedef void *fa_stream_t;
+
+typedef enum {
+  FA_F32 = 0,      /* IEEE binary32 */
+  FA_F16 = 1,      /* IEEE binary16 */
+  FA_BF16 = 2,     /* bfloat16 */
+  FA_FP8_E4M3 = 3, /* OCP FP8 E4M3FN (bias 7, max 448, no inf) */
+  FA_INT8 = 4      /* signed 8-bit integer codes */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
+  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head dim, dtype pair, size limit */
+  FA_ERR_ALIGNMENT = -3,   /* pointer or stride breaks the 16-byte row alignment */
+  FA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  FA_ERR_HIP = -5          /* the HIP runtime rejected a launch */
+} fa_status;
+
+/*
+ * Prefill forward.  Shapes (logical, any strides as described above):
+ *   q [B, Hq,  Sq, d]   k, v [B, Hkv, Sk, d]   o [B, Hq, Sq, d]   lse [B, Hq, Sq]
+ * Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention;
+ * Hq % Hkv == 0).  d is 64 or 128.
+ * Dtype pairs (in_dtype -> out_dtype): F32->F32, BF16->BF16, F16->F16,
+ * FP8_E4M3->BF16.  For FP8 the true operands are code * descale (one float32
+ * descale per tensor); q/k/v_descale are ignored for the other dtypes.
+ * causal != 0 masks key j for query i unless j <= i + Sk - Sq (the mask is
+ * aligned to the last query and last key; with Sq == Sk it is the usual lower
+ * triangle).  A query row that sees no key gets O = 0 and LSE = -inf.
+ * lse may be NULL; otherwise it receives float32 natural-log LSE values.
+ * softmax_scale multiplies Q K^T before the softmax (1/sqrt(d) for the usual
+ * scaled dot-product attention); it must be finite and > 0.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int32_t in_dtype, out_dtype; /* fa_dtype values */
+  int32_t B, Hq, Hkv, Sq, Sk, d;
+  int64_t q_strides[3]; /* batch, head, sequence — in elements */
+  int64_t k_strides[3];
+  int64_t v_strides[3];
+  int64_t o_strides[3];
+  int64_t lse_strides[2]; /* batch, head; the sequence stride is 1 */
+  float softmax_scale;
+  int32_t causal;
+  float q_descale, k_descale, v_descale;
+} fa_fwd_params;
+
+int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
+
+/*
+ * One-token decode over a quantised cache.
+ *   q [B, Hq, d] bf16                         o [B, Hq, d] bf16
+ *   k_cache, v_cache [B, Hkv, L, d] int8      lse [B, Hq] float32 (may be NULL)
+ *   k_scale, v_scale [B, Hkv, L] fp16 (token stride 1)
+ *   seq_lens [B] int32 on the device, or NULL meaning every sequence has L tokens
+ * The dequantised key/value of token t is code * scale (symmetric, no zero
+ * point).  Query head h reads cache head h / (Hq / Hkv).  d must be 128 and
+ * Hq / Hkv at most 16.  Each sequence's first seq_lens[b] tokens are attended
+ * (0 <= seq_lens[b] <= L; a value outside that range is clamped into it;
+ * zero tokens give O = 0 and LSE = -inf).
+ * The L positions are cut into num_splits chunks of ceil(L / num_splits)
+ * tokens (1 <= num_splits <= 64); every chunk yields a normalised partial output
+ * and its log-sum-exp, and a second kernel merges them.  The partials live in
+ * the caller's workspace, of at least fa_decode_workspace_size(...) bytes
+ * (16-byte aligned); its contents on entry do not matter.
+ */
+typedef enum { FA_KV_INT8_TOKHEAD_F16SCALE = 0 } fa_kv_format;
+
+typedef struct {
+  const void *q;
+  const void *k_cache, *v_cache;
+  const void *k_scale, *v_scale;
+  const int32_t *seq_lens;
+  void *o;
+  float *lse;
+  int32_t B, Hq, Hkv, L, d, num_splits;
+  int64_t q_strides[2];     /* batch, head — in elements */
+  int64_t kv_strides[3];    /* batch, head, token — shared by k_cache and v_cache */
+  int64_t scale_strides[2]; /* batch, head — shared by k_scale and v_scale */
+  int64_t o_strides[2];     /* batch, head */
+  int64_t lse_strides[2];   /* batch, head */
+  int32_t kv_format;        /* fa_kv_format */
+  float softmax_scale;
+  void *workspace;
+  size_t workspace_bytes;
+} fa_decode_params;
+
+/* Bytes of workspace fa_decode_kvq needs for these sizes (0 on invalid sizes). */
+size_t fa_decode_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t num_splits);
+
+int fa_decode_kvq(const fa_decode_params *p, fa_stream_t stream);
+
+/* Host-only validation used by the two calls above; makes no HIP call, so it
+ * can run on a machine without a GPU.  Returns FA_OK or a negative fa_status. */
+int fa_check_fwd_params(const fa_fwd_params *p);
+int fa_check_decode_params(const fa_decode_params *p);
+
+/* Static description of a status code. */
+const char *fa_status_string(int status);
+
+/* Reason for the last non-FA_OK return on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,162 @@
+"""GPU parity of fa_fwd against the float64 oracle (through the C ABI).
+
+Small shapes cover several tiles, ragged tails, Sq != Sk, grouped-query heads
+and both head dims; every output buffer is pre-filled with NaN and surrounded
+by guard bands, so unwritten or out-of-bounds elements are caught.
+"""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {  # max abs error bars: O, LSE
+    "f32": (1e-4, 1e-4),
+    "bf16": (2e-2, 1e-3),
+    "f16": (2e-2, 1e-3),
+}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+GUARD = 256
+
+
+def guarded(shape, dtype, fill=float("nan")):
+    """A tensor of `shape` inside a larger buffer whose guard bands hold a sentinel."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * GUARD,), fill, dtype=dtype, device="cuda")
+    return buf, buf[GUARD:GUARD + n].view(shape)
+
+
+def guards_intact(buf, fill_is_nan=True):
+    g = torch.cat([buf[:GUARD], buf[-GUARD:]]).float()
+    return bool(torch.isnan(g).all()) if fill_is_nan else True
+
+
+def run_fwd(fa, q, k, v, causal, out_dtype, scale=None, lse_wanted=True):
+    B, Hq, Sq, d = q.shape
+    obuf, o = guarded((B, Hq, Sq, d), out_dtype)
+    lbuf, lse = guarded((B, Hq, Sq), torch.float32) if lse_wanted else (None, None)
+    print(f"fa_fwd q={tuple(q.shape)} k={tuple(k.shape)} {q.dtype} causal={causal}", flush=True)
+    fa.fa_fwd(q, k, v, o, lse, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert guards_intact(obuf), "write outside O"
+    if lbuf is not None:
+        assert guards_intact(lbuf), "write outside LSE"
+    return o, lse
+
+
+def check(o, lse, q, k, v, causal, dt, scale=None):
+    ro, rl = oracle.attention_fp64(q.cpu(), k.cpu(), v.cpu(), causal, scale)
+    og = o.double().cpu().numpy()
+    assert not np.isnan(og).any(), "unwritten O elements"
+    tol_o, tol_l = TOL[dt]
+    err_o = np.max(np.abs(og - ro)) if og.size else 0.0
+    assert err_o <= tol_o, f"O max abs err {err_o}"
+    if lse is not None:
+        lg = lse.double().cpu().numpy()
+        assert not np.isnan(lg).any(), "unwritten LSE elements"
+        assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        err_l = np.max(np.abs(lg[fin] - rl[fin])) if fin.any() else 0.0
+        assert err_l <= tol_l, f"LSE max abs err {err_l}"
+    return err_o
+
+
+def make(B, Hq, Hkv, Sq, Sk, d, dt, seed=0):
+    cfg = fa_inputs.FwdConfig("t", dt, B, Hq, Hkv, Sq, Sk, d, False)
+    x = fa_inputs.make_fwd_inputs(cfg, seed=seed)
+    return [x[n].cuda() for n in ("q", "k", "v")]
+
+
+SHAPES = [
+    # B, Hq, Hkv, Sq, Sk
+    (1, 1, 1, 1, 1),
+    (1, 2, 2, 17, 17),
+    (2, 2, 1, 64, 64),
+    (1, 4, 1, 127, 127),
+    (1, 1, 1, 128, 128),
+    (1, 2, 2, 129, 129),
+    (1, 8, 2, 300, 300),
+    (2, 2, 2, 100, 260),   # Sq < Sk
+    (1, 2, 2, 260, 100),   # Sq > Sk: causal leaves leading rows empty
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_small_shapes(gpu, dt, d, causal, shape):
+    B, Hq, Hkv, Sq, Sk = shape
+    q, k, v = make(B, Hq, Hkv, Sq, Sk, d, dt, seed=Sq * 7 + d)
+    o, lse = run_fwd(gpu, q, k, v, causal, TDT[dt])
+    check(o, lse, q, k, v, causal, dt)
+
+
+def test_fwd_config_fp32_s128_d64(gpu):
+    cfg = fa_inputs.CONFIGS["fp32_s128_d64"]
+    x = fa_inputs.make_fwd_inputs(cfg, seed=0)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = run_fwd(gpu, q, k, v, cfg.causal, torch.float32, cfg.scale)
+    err = check(o, lse, q, k, v, cfg.causal, "f32", cfg.scale)
+    print("fp32 config max abs err", err)
+
+
+def test_fwd_no_lse_and_strided_layout(gpu):
+    # BSHD storage viewed as BHSD: sequence stride H*d, head stride d
+    B, H, S, d = 2, 4, 150, 128
+    base = torch.randn(B, S, H, d, device="cuda").to(torch.bfloat16)
+    q = base.transpose(1, 2)
+    k = torch.randn(B, S, H, d, device="cuda").to(torch.bfloat16).transpose(1, 2)
+    v = torch.randn(B, S, H, d, device="cuda").to(torch.bfloat16).transpose(1, 2)
+    o = torch.full((B, S, H, d), float("nan"), device="cuda", dtype=torch.bfloat16).transpose(1, 2)
+    gpu.fa_fwd(q, k, v, o, None, causal=True)
+    torch.cuda.synchronize()
+    check(o, None, q, k, v, True, "bf16")
+
+
+def test_fwd_deterministic(gpu):
+    q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
+    o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
+    o2, l2 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_fwd_gqa_equals_repeated_heads(gpu):
+    q, k, v = make(1, 8, 2, 200, 200, 128, "bf16", seed=12)
+    o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = run_fwd(gpu, q, kr, vr, True, torch.bfloat16)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_fwd_constant_v_and_zero_q(gpu):
+    B, H, S, d = 1, 2, 190, 64
+    q = torch.zeros(B, H, S, d, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(B, H, S, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, H, 1, d, device="cuda").to(torch.bfloat16).expand(B, H, S, d).contiguous()
+    o, lse = run_fwd(gpu, q, k, v, True, torch.bfloat16)
+    assert torch.equal(o, v), "constant V must come back exactly"
+    want = torch.log(torch.arange(1, S + 1, device="cuda", dtype=torch.float32))
+    assert float((lse[0, 0] - want).abs().max()) < 1e-5
+
+
+def test_fwd_rejects_bad_params(gpu):
+    q, k, v = make(1, 4, 3, 16, 16, 128, "bf16")[0], None, None
+    k = torch.zeros(1, 3, 16, 128, device="cuda", dtype=torch.bfloat16)
+    o = torch.empty_like(q)
+    with pytest.raises(gpu.FaError) as e:
+        gpu.fa_fwd(q, k, k, o)  # 4 query heads over 3 kv heads
+    assert e.value.status == gpu.FA_ERR_INVALID_ARG
+    q96 = torch.zeros(1, 1, 8, 96, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(gpu.FaError) as e:
+        gpu.fa_fwd(q96, q96, q96, torch.empty_like(q96))
+    assert e.value.status == gpu.FA_ERR_UNSUPPORTED

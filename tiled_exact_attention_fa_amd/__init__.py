@@ -1,0 +1,233 @@
+"""Python binding of libfa, the MI355X exact tiled attention library.
+
+Argument marshalling only: each function below has the name of the C entry
+point it calls (declared in include/fa.h), turns torch tensors into device
+pointers and element strides, passes torch's current HIP stream, and raises
+FaError on a negative status.  Every step of the computation runs in the HIP
+kernels of libfa.so; there is no fallback of any kind — if the library has not
+been built, load() raises.
+
+    fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None, ...)
+    fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, ...)
+    fa_decode_workspace_size(B, Hq, d, num_splits)
+    fa_check_fwd_params(params) / fa_check_decode_params(params)
+    fa_status_string(status) / fa_last_error()
+
+Build with ``python -m tiled_exact_attention_fa_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3, FA_INT8 = 0, 1, 2, 3, 4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGNMENT, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4, -5
+FA_KV_INT8_TOKHEAD_F16SCALE = 0
+
+I64x3 = ctypes.c_int64 * 3
+I64x2 = ctypes.c_int64 * 2
+
+
+class FaFwdParams(ctypes.Structure):
+    """Mirror of fa_fwd_params."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("q_strides", I64x3), ("k_strides", I64x3), ("v_strides", I64x3), ("o_strides", I64x3),
+        ("lse_strides", I64x2),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+    ]
+
+
+class FaDecodeParams(ctypes.Structure):
+    """Mirror of fa_decode_params."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("q_strides", I64x2), ("kv_strides", I64x3), ("scale_strides", I64x2),
+        ("o_strides", I64x2), ("lse_strides", I64x2),
+        ("kv_format", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ["fa_fwd", "fa_decode_kvq", "fa_decode_workspace_size", "fa_check_fwd_params",
+           "fa_check_decode_params", "fa_status_string", "fa_last_error"]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {fa_status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Loads libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it with `python -m tiled_exact_attention_fa_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.fa_fwd.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_void_p]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_decode_kvq.argtypes = [ctypes.POINTER(FaDecodeParams), ctypes.c_void_p]
+    lib.fa_decode_kvq.restype = ctypes.c_int
+    lib.fa_decode_workspace_size.argtypes = [ctypes.c_int32] * 4
+    lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fa_check_fwd_params.argtypes = [ctypes.POINTER(FaFwdParams)]
+    lib.fa_check_fwd_params.restype = ctypes.c_int
+    lib.fa_check_decode_params.argtypes = [ctypes.POINTER(FaDecodeParams)]
+    lib.fa_check_decode_params.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def fa_check_fwd_params(params: FaFwdParams) -> int:
+    return load().fa_check_fwd_params(ctypes.byref(params))
+
+
+def fa_check_decode_params(params: FaDecodeParams) -> int:
+    return load().fa_check_decode_params(ctypes.byref(params))
+
+
+def fa_decode_workspace_size(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(load().fa_decode_workspace_size(B, Hq, d, num_splits))
+
+
+# ---- torch marshalling -------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+
+    table = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
+             torch.float8_e4m3fn: FA_FP8_E4M3, torch.int8: FA_INT8}
+    if t.dtype not in table:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return table[t.dtype]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require_dense_d(name, t):
+    if t is not None and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last (head) dimension must have stride 1")
+
+
+def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
+               q_descale=1.0, k_descale=1.0, v_descale=1.0) -> FaFwdParams:
+    """fa_fwd_params for BHSD-indexed tensors q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d],
+    o [B,Hq,Sq,d], lse [B,Hq,Sq] (any strides with a unit head-dim stride)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _require_dense_d(n, t)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    p = FaFwdParams()
+    p.q, p.k, p.v, p.o, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
+    p.in_dtype, p.out_dtype = _dtype_code(q), _dtype_code(o)
+    p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d = B, Hq, Hkv, Sq, Sk, d
+    p.q_strides = I64x3(*q.stride()[:3])
+    p.k_strides = I64x3(*k.stride()[:3])
+    p.v_strides = I64x3(*v.stride()[:3])
+    p.o_strides = I64x3(*o.stride()[:3])
+    p.lse_strides = I64x2(*(lse.stride()[:2] if lse is not None else (0, 0)))
+    p.softmax_scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    p.causal = 1 if causal else 0
+    p.q_descale, p.k_descale, p.v_descale = float(q_descale), float(k_descale), float(v_descale)
+    return p
+
+
+def fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None,
+           q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None) -> None:
+    """Enqueue the prefill forward on torch's current stream (or ``stream``)."""
+    p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale)
+    st = load().fa_fwd(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd", fa_last_error())
+
+
+def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,
+                  num_splits=16, softmax_scale=None, workspace=None) -> FaDecodeParams:
+    """fa_decode_params for q [B,Hq,d], caches [B,Hkv,L,d], scales [B,Hkv,L],
+    o [B,Hq,d], lse [B,Hq]; k and v caches (and their scales) must share strides."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o),
+                 ("k_scale", k_scale), ("v_scale", v_scale)):
+        _require_dense_d(n, t)
+    if k_cache.stride() != v_cache.stride() or k_scale.stride() != v_scale.stride():
+        raise ValueError("k and v caches (and their scales) must have identical strides")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    p = FaDecodeParams()
+    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    p.k_scale, p.v_scale, p.seq_lens = _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens)
+    p.o, p.lse = _ptr(o), _ptr(lse)
+    p.B, p.Hq, p.Hkv, p.L, p.d, p.num_splits = B, Hq, Hkv, L, d, int(num_splits)
+    p.q_strides = I64x2(*q.stride()[:2])
+    p.kv_strides = I64x3(*k_cache.stride()[:3])
+    p.scale_strides = I64x2(*k_scale.stride()[:2])
+    p.o_strides = I64x2(*o.stride()[:2])
+    p.lse_strides = I64x2(*(lse.stride()[:2] if lse is not None else (0, 0)))
+    p.kv_format = FA_KV_INT8_TOKHEAD_F16SCALE
+    p.softmax_scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def decode_workspace(B, Hq, d, num_splits, device="cuda"):
+    """A torch byte tensor big enough for fa_decode_kvq's partial results."""
+    import torch
+
+    return torch.empty(fa_decode_workspace_size(B, Hq, d, num_splits), dtype=torch.uint8, device=device)
+
+
+def fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,
+                  num_splits=16, softmax_scale=None, workspace=None, stream=None) -> None:
+    """Enqueue one decode step over the int8 cache on torch's current stream."""
+    if workspace is None:
+        workspace = decode_workspace(q.shape[0], q.shape[1], q.shape[2], num_splits, q.device)
+    p = decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse, seq_lens, num_splits,
+                      softmax_scale, workspace)
+    st = load().fa_decode_kvq(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_kvq", fa_last_error())

@@ -1,0 +1,85 @@
+// Kernel arguments and workgroup scheduling shared by the prefill kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int B, Hq, G, Sq, Sk, nq;
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh;  // element strides
+  long long o_sb, o_sh, o_ss;
+  long long lse_sb, lse_sh;
+  unsigned q_ss, k_ss, v_ss;     // row strides in bytes (below 2^31 after validation)
+  unsigned q_ext, k_ext, v_ext;  // bytes spanned by one (batch, head) slice
+  float c;                       // softmax scale * log2(e) [* q and k descale]
+  float o_mul;                   // output multiplier (v descale for fp8, else 1)
+};
+
+// blockIdx -> (batch*head, query tile).  Workgroups are handed to the 8 XCDs
+// round-robin (XCD = blockIdx % 8).  When the (batch, head) count divides by 8,
+// each XCD gets a contiguous range of (batch, head) pairs — consecutive query
+// heads share one K/V head under GQA — so every K/V stream is read through one
+// XCD's L2.  Within an XCD the last query tiles (the longest under a causal
+// mask) are issued first.
+__device__ __forceinline__ void map_block(int bid, int nq, int nbh, int &bh, int &qt) {
+  if ((nbh & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3, per = nbh >> 3;
+    bh = xcd * per + slot % per;
+    qt = nq - 1 - slot / per;
+  } else {
+    bh = bid % nbh;
+    qt = nq - 1 - bid / nbh;
+  }
+}
+
+inline unsigned slice_bytes(int rows, long long ss, int d, int es) {
+  if (rows <= 0) return 0;
+  return static_cast<unsigned>((static_cast<long long>(rows - 1) * ss + d) * es);
+}
+
+inline FwdArgs make_fwd_args(const fa_fwd_params *p, int br, int es) {
+  FwdArgs a{};
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.o = p->o;
+  a.lse = p->lse;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.G = p->Hq / p->Hkv;
+  a.Sq = p->Sq;
+  a.Sk = p->Sk;
+  a.nq = (p->Sq + br - 1) / br;
+  a.q_sb = p->q_strides[0];
+  a.q_sh = p->q_strides[1];
+  a.k_sb = p->k_strides[0];
+  a.k_sh = p->k_strides[1];
+  a.v_sb = p->v_strides[0];
+  a.v_sh = p->v_strides[1];
+  a.o_sb = p->o_strides[0];
+  a.o_sh = p->o_strides[1];
+  a.o_ss = p->o_strides[2];
+  a.lse_sb = p->lse_strides[0];
+  a.lse_sh = p->lse_strides[1];
+  a.q_ss = p->Sq > 1 ? static_cast<unsigned>(p->q_strides[2] * es) : 0u;
+  a.k_ss = p->Sk > 1 ? static_cast<unsigned>(p->k_strides[2] * es) : 0u;
+  a.v_ss = p->Sk > 1 ? static_cast<unsigned>(p->v_strides[2] * es) : 0u;
+  a.q_ext = slice_bytes(p->Sq, p->q_strides[2], p->d, es);
+  a.k_ext = slice_bytes(p->Sk, p->k_strides[2], p->d, es);
+  a.v_ext = slice_bytes(p->Sk, p->v_strides[2], p->d, es);
+  a.c = p->softmax_scale * 1.4426950408889634f;
+  a.o_mul = 1.f;
+  if (p->in_dtype == FA_FP8_E4M3) {
+    a.c *= p->q_descale * p->k_descale;
+    a.o_mul = p->v_descale;
+  }
+  return a;
+}
+
+}  // namespace fa

@@ -1,0 +1,18 @@
+// Internal declarations shared by the host-side translation units of libfa.
+#pragma once
+
+#include "../../include/fa.h"
+
+#define FA_DECODE_MAX_SPLITS 64
+#define FA_DECODE_MAX_GROUP 16
+
+// Records a reason for the calling thread's fa_last_error() and returns status.
+int fa_set_error(int status, const char *fmt, ...);
+void fa_clear_error();
+int fa_dtype_size(int dt);
+
+// Kernel launchers, one per kernel family (defined in the .hip files).  They
+// assume validated parameters and return FA_OK or FA_ERR_HIP.
+int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream);
+int fa_launch_fwd_fp8(const fa_fwd_params *p, void *stream);
+int fa_launch_decode(const fa_decode_params *p, void *stream);
