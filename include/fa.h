@@ -108,7 +108,8 @@ int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
  * One-token decode over a quantised cache.
  *   q [B, Hq, d] bf16                         o [B, Hq, d] bf16
  *   k_cache, v_cache [B, Hkv, L, d] int8      lse [B, Hq] float32 (may be NULL)
- *   k_scale, v_scale [B, Hkv, L] fp16 (token stride 1)
+ *   k_scale, v_scale [B, Hkv, L] fp16 (token stride 1; 2-byte alignment is
+ *                    enough, 16-byte aligned scale rows take the faster loads)
  *   seq_lens [B] int32 on the device, or NULL meaning every sequence has L tokens
  * The dequantised key/value of token t is code * scale (symmetric, no zero
  * point).  Query head h reads cache head h / (Hq / Hkv).  d must be 128 and
@@ -116,8 +117,9 @@ int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
  * (0 <= seq_lens[b] <= L; a value outside that range is clamped into it;
  * zero tokens give O = 0 and LSE = -inf).
  * The L positions are cut into num_splits chunks of ceil(L / num_splits)
- * tokens (1 <= num_splits <= 64); every chunk yields a normalised partial output
- * and its log-sum-exp, and a second kernel merges them.  The partials live in
+ * tokens rounded up to a multiple of 32 (1 <= num_splits <= 64; trailing chunks
+ * may be empty); every chunk yields a normalised partial output and its
+ * log-sum-exp, and a second kernel merges them.  The partials live in
  * the caller's workspace, of at least fa_decode_workspace_size(...) bytes
  * (16-byte aligned); its contents on entry do not matter.
  */

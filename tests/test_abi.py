@@ -134,8 +134,8 @@ def test_decode_validator(lib):
     (lambda p: setattr(p, "kv_format", 7), fa.FA_ERR_UNSUPPORTED),
     (lambda p: setattr(p, "workspace_bytes", 100), fa.FA_ERR_WORKSPACE),
     (lambda p: setattr(p, "workspace", 0), fa.FA_ERR_WORKSPACE),
-    (lambda p: setattr(p, "v_scale", 0x20004), fa.FA_ERR_ALIGNMENT),
-    (lambda p: setattr(p, "scale_strides", fa.I64x2(8 * 1000, 1001)), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "v_scale", 0x20001), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "scale_strides", fa.I64x2(8 * 1000, -1)), fa.FA_ERR_INVALID_ARG),
     (lambda p: setattr(p, "softmax_scale", -1.0), fa.FA_ERR_INVALID_ARG),
 ])
 def test_decode_validator_errors(lib, mutate, status):

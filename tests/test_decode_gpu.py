@@ -1,0 +1,119 @@
+"""GPU parity of fa_decode_kvq (int8 KV cache, split-KV + LSE combine) against
+the float64 oracle fed the same quantised cache."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 8e-2   # quantised-KV path, against an oracle with the same quantisation
+TOL_LSE = 1e-3
+
+
+def run_decode(fa, x, num_splits, lse_wanted=True):
+    B, Hq, d = x["q"].shape
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), device="cuda") if lse_wanted else None
+    print(f"fa_decode_kvq q={tuple(x['q'].shape)} cache={tuple(x['k'].shape)} splits={num_splits} "
+          f"lens={x['seq_lens'].tolist()[:8]}", flush=True)
+    fa.fa_decode_kvq(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], o, lse,
+                     seq_lens=x["seq_lens"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o, lse, xc, heads=None):
+    ro, rl = oracle.decode_fp64(xc["q"], xc["k"].numpy(), xc["k_scale"].numpy(), xc["v"].numpy(),
+                                xc["v_scale"].numpy(), xc["seq_lens"].numpy(), heads=heads)
+    og = o.double().cpu().numpy()
+    sel = heads if heads is not None else [(b, h) for b in range(og.shape[0]) for h in range(og.shape[1])]
+    bi = [b for b, _ in sel]
+    hi = [h for _, h in sel]
+    assert not np.isnan(og[bi, hi]).any()
+    err_o = float(np.max(np.abs(og[bi, hi] - ro[bi, hi])))
+    assert err_o <= TOL_O, f"O err {err_o}"
+    if lse is not None:
+        lg = lse.double().cpu().numpy()
+        assert np.array_equal(np.isneginf(lg[bi, hi]), np.isneginf(rl[bi, hi]))
+        fin = np.isfinite(rl[bi, hi])
+        err_l = float(np.max(np.abs(lg[bi, hi][fin] - rl[bi, hi][fin]), initial=0.0))
+        assert err_l <= TOL_LSE, f"LSE err {err_l}"
+    return err_o
+
+
+def make(B, Hq, Hkv, L, lens=None, seed=0):
+    cfg = fa_inputs.DecodeConfig("t", B, Hq, Hkv, L, 128, 16, tuple(lens) if lens else ())
+    xc = fa_inputs.make_decode_inputs(cfg, seed=seed)
+    return xc, {k: v.cuda() for k, v in xc.items()}
+
+
+CASES = [
+    # B, Hq, Hkv, L, lens, splits
+    (1, 4, 1, 1, None, 1),
+    (2, 4, 1, 31, None, 3),
+    (2, 8, 2, 100, [100, 37], 16),
+    (3, 4, 4, 1000, [1000, 0, 513], 4),
+    (2, 16, 1, 3000, [2999, 64], 16),
+    (1, 32, 8, 4096, None, 16),
+    (2, 2, 2, 700, [1, 699], 64),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,lens,splits", CASES)
+def test_decode_small(gpu, B, Hq, Hkv, L, lens, splits):
+    xc, x = make(B, Hq, Hkv, L, lens, seed=L + Hq)
+    o, lse = run_decode(gpu, x, splits)
+    err = compare(o, lse, xc)
+    print("max |dO|", err)
+
+
+def test_decode_split_count_invariance(gpu):
+    xc, x = make(2, 8, 2, 2048, [2048, 1500], seed=3)
+    o1, l1 = run_decode(gpu, x, 1)
+    o16, l16 = run_decode(gpu, x, 16)
+    assert float((o1.float() - o16.float()).abs().max()) <= 1.6e-2
+    assert float((l1 - l16).abs().max()) <= 1e-4
+
+
+def test_decode_no_lse_and_deterministic(gpu):
+    xc, x = make(2, 8, 2, 777, None, seed=4)
+    o1, _ = run_decode(gpu, x, 5, lse_wanted=False)
+    o2, _ = run_decode(gpu, x, 5, lse_wanted=False)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    compare(o1, None, xc)
+
+
+def test_decode_workspace_too_small(gpu):
+    xc, x = make(1, 4, 1, 64, None)
+    o = torch.empty(1, 4, 128, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu.FaError) as e:
+        gpu.fa_decode_kvq(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], o, None,
+                          num_splits=4, workspace=ws)
+    assert e.value.status == gpu.FA_ERR_WORKSPACE
+
+
+def test_decode_full_size_sampled(gpu):
+    """The int8 cache workload at full size (B=64, 32/8 heads, L=32768, 16
+    splits), inputs drawn on the GPU; outputs checked on sampled heads."""
+    cfg = fa_inputs.CONFIGS["decode_int8_b64_gqa32x8_L32768"]
+    x = fa_inputs.make_decode_inputs(cfg, seed=0, device="cuda")
+    o, lse = run_decode(gpu, x, cfg.num_splits)
+    samples = [(0, 0), (0, 31), (17, 5), (33, 12), (63, 30), (40, 19)]
+    for b, h in samples:
+        kvh = h // (cfg.Hq // cfg.Hkv)
+        sub = {
+            "q": x["q"][b:b + 1, h:h + 1].cpu(),
+            "k": x["k"][b:b + 1, kvh:kvh + 1].cpu(),
+            "v": x["v"][b:b + 1, kvh:kvh + 1].cpu(),
+            "k_scale": x["k_scale"][b:b + 1, kvh:kvh + 1].cpu(),
+            "v_scale": x["v_scale"][b:b + 1, kvh:kvh + 1].cpu(),
+            "seq_lens": x["seq_lens"][b:b + 1].cpu(),
+        }
+        compare(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], sub)

@@ -152,11 +152,12 @@ extern "C" int fa_check_decode_params(const fa_decode_params *p) {
     if ((st = check_tensor("v_cache", p->v_cache, p->kv_strides, 3, p->L, p->d, 1)) != FA_OK) return st;
     for (const void *sp : {p->k_scale, p->v_scale}) {
       if (sp == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "k_scale/v_scale is NULL");
-      if (!aligned16(sp)) return fa_set_error(FA_ERR_ALIGNMENT, "k_scale/v_scale not 16-byte aligned");
+      if ((reinterpret_cast<uintptr_t>(sp) & 1u) != 0)
+        return fa_set_error(FA_ERR_ALIGNMENT, "k_scale/v_scale not 2-byte aligned");
     }
     for (int i = 0; i < 2; ++i)
-      if (p->scale_strides[i] < 0 || (p->scale_strides[i] * 2) % 16 != 0)
-        return fa_set_error(FA_ERR_ALIGNMENT, "scale stride %d is not a non-negative multiple of 16 bytes", i);
+      if (p->scale_strides[i] < 0)
+        return fa_set_error(FA_ERR_INVALID_ARG, "scale stride %d is negative", i);
     const int64_t sext = static_cast<int64_t>(p->L) * 2;
     if (sext >= (int64_t(1) << 31)) return fa_set_error(FA_ERR_UNSUPPORTED, "scale slice too large");
   }

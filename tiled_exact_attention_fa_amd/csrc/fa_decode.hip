@@ -1,2 +1,427 @@
+// One-token decode over an int8 KV cache with per-token-per-head fp16 scales,
+// split over the cache length and merged by log-sum-exp.
+//
+// What is computed (KV-cache quantisation overview, section 1 "decode step" and
+// section 3 "read path"; FlashAttention interview canvas, panel 1 "online
+// softmax key state"): for each sequence b and query head h, the new query
+// attends to the first seq_len[b] cached tokens of cache head h / G, whose keys
+// and values are code * scale.  Decode reads every cached byte once per step
+// and so is bound by HBM bandwidth (same overview, section 2).
+//
+// MI355X design.
+//   * Kernel 1 (decode_split_kernel): one workgroup per (batch, cache head,
+//     split).  All G query heads that share the cache head are served by the
+//     same pass over the chunk, so every K/V byte is read from HBM once.  The
+//     chunk is cut into four contiguous quarters, one per wavefront; each
+//     wavefront streams 32-token tiles with a one-tile register prefetch and
+//     no barrier, and the four partial states are merged through LDS at the end.
+//   * The dequantisation is fused into the tile load and folded into the math:
+//     int8 codes become exact fp16 values with two byte permutes and a packed
+//     subtract (1024 + u in fp16 is 0x6400 | u), the key scale multiplies the
+//     score, and the value scale multiplies the probability before it is
+//     rounded, so no dequantised tile is ever stored.
+//   * S^T = K Q^T and O^T = V^T P^T run on 16x16x32 fp16 MFMA.  The value
+//     operand needs 8 tokens of one head-dim column per lane; lanes load 8
+//     bytes of each token row and the byte permutes of the fp16 conversion
+//     also transpose, so V^T costs nothing extra.  The head-dim order inside a
+//     16-row output block is permuted (row m of block j is column 8m + j),
+//     which lets each lane load one contiguous 8-byte piece per token.
+//   * The bf16 query is prescaled by a power of two per head so it converts to
+//     fp16 exactly; the probabilities times value scales are prescaled by a
+//     power of two per wavefront, chosen from the largest value scale of its
+//     range, so they neither overflow nor lose range in fp16.  Both factors are
+//     undone in fp32.
+//   * Kernel 2 (decode_combine_kernel) merges the splits of one (batch, head):
+//     LSE = M + log2 sum_s 2^(lse_s - M), O = sum_s 2^(lse_s - LSE) O_s, in the
+//     log2 domain, and writes bf16 O and natural-log LSE.
+#include "fa_device.hpp"
 #include "fa_internal.h"
-int fa_launch_decode(const fa_decode_params *, void *) { return fa_set_error(FA_ERR_UNSUPPORTED, "decode not built yet"); }
+
+namespace fa {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDecodeThreads = 256;
+constexpr int kTile = 32;  // tokens per step of one wavefront
+constexpr int kD = 128;
+
+struct DecodeArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  const void *ks;
+  const void *vs;
+  const int *seq_lens;
+  void *o;
+  float *lse;
+  float *ws_o;  // [split][B][Hq][d] normalised partial outputs
+  float *ws_l;  // [split][B][Hq]   partial log2-sum-exp (log2 units)
+  int B, Hq, Hkv, G, L, nsplit, chunk;
+  long long q_sb, q_sh, kv_sb, kv_sh, sc_sb, sc_sh, o_sb, o_sh, lse_sb, lse_sh;
+  unsigned kv_ss;   // token stride in bytes
+  unsigned kv_ext;  // bytes of one (batch, head) cache slice
+  unsigned sc_ext;  // bytes of one (batch, head) scale slice
+  int sc_vec;       // scale rows 16-byte aligned: vector loads, else 2-byte loads
+  float c;          // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// fp16 pair minus 1152: turns (1152 + x) back into x exactly.
+__device__ __forceinline__ unsigned unbias(unsigned w) {
+  f16x2 h = __builtin_bit_cast(f16x2, w);
+  h = h + f16x2{(_Float16)-1152.0f, (_Float16)-1152.0f};
+  return __builtin_bit_cast(unsigned, h);
+}
+
+constexpr unsigned kMagic = 0x64646464u;  // fp16 high byte of 1024 + u
+
+// Four int8 codes -> two dwords of exact fp16 pairs (d0,d1) and (d2,d3).
+__device__ __forceinline__ void i8x4_to_f16(unsigned w, unsigned &lo, unsigned &hi) {
+  const unsigned u = w ^ 0x80808080u;  // x + 128 as unsigned bytes
+  lo = unbias(perm(kMagic, u, 0x04010400u));
+  hi = unbias(perm(kMagic, u, 0x04030402u));
+}
+
+// Two tokens' codes for the same four head-dim columns (a from token t, b from
+// token t') -> four dwords, one per column, each the fp16 pair (t, t').
+__device__ __forceinline__ void i8_pair_transpose(unsigned a, unsigned b, unsigned out[4]) {
+  const unsigned m01 = perm(b, a, 0x05010400u) ^ 0x80808080u;  // a0 b0 a1 b1
+  const unsigned m23 = perm(b, a, 0x07030602u) ^ 0x80808080u;  // a2 b2 a3 b3
+  out[0] = unbias(perm(kMagic, m01, 0x04010400u));
+  out[1] = unbias(perm(kMagic, m01, 0x04030402u));
+  out[2] = unbias(perm(kMagic, m23, 0x04010400u));
+  out[3] = unbias(perm(kMagic, m23, 0x04030402u));
+}
+
+// Exponent E with x = m * 2^E, m in [0.5, 1); 0 for x == 0.
+__device__ __forceinline__ int exp_of(float x) {
+  int e;
+  (void)frexpf(x, &e);
+  return x > 0.f ? e : 0;
+}
+
+// Four fp16 scales of consecutive tokens starting at token t (a multiple of 4).
+__device__ __forceinline__ u32x2 load_scales4(__amdgpu_buffer_rsrc_t r, int t, bool vec) {
+  const unsigned off = static_cast<unsigned>(t) * 2u;
+  if (vec) return buf_load8(r, off);
+  unsigned short e[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * i, 0, 0);
+  return u32x2{e[0] | (static_cast<unsigned>(e[1]) << 16), e[2] | (static_cast<unsigned>(e[3]) << 16)};
+}
+
+struct TileRegs {
+  u32x4 k[2][2];   // [token block][16-byte half]: 32 codes of one token row
+  u32x2 v[8];      // 8 tokens x 8 codes of one 8-column chunk
+  u32x2 ks[2];     // 4 fp16 key scales per token block
+  u32x2 vs[2];     // 4 fp16 value scales per token block
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void decode_split_kernel(const DecodeArgs a) {
+  __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
+  __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15;   // query column (S^T, O^T) or row within a 16-row block
+  const int g = lane >> 4;   // lane group: reduction slots 8g..8g+7
+
+  const int split = blockIdx.x % a.nsplit;
+  const int kvh = (blockIdx.x / a.nsplit) % a.Hkv;
+  const int b = blockIdx.x / (a.nsplit * a.Hkv);
+  const int G = a.G;
+
+  int len = a.seq_lens != nullptr ? a.seq_lens[b] : a.L;
+  len = min(max(len, 0), a.L);
+  const int c0 = split * a.chunk;
+  const int c1 = min(c0 + a.chunk, len);
+  const int quarter = ((a.chunk + 3) / 4 + kTile - 1) / kTile * kTile;
+  const int w0 = c0 + wave * quarter;
+  const int w1 = min(w0 + quarter, c1);
+  const int ntiles = w1 > w0 ? (w1 - w0 + kTile - 1) / kTile : 0;
+
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(static_cast<const char *>(a.k) + b * a.kv_sb + kvh * a.kv_sh, a.kv_ext);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(static_cast<const char *>(a.v) + b * a.kv_sb + kvh * a.kv_sh, a.kv_ext);
+  const __amdgpu_buffer_rsrc_t rks =
+      make_rsrc(static_cast<const _Float16 *>(a.ks) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
+  const __amdgpu_buffer_rsrc_t rvs =
+      make_rsrc(static_cast<const _Float16 *>(a.vs) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
+
+  // ---- query: lane (n, g) holds q[n][32g + 8s + j], prescaled into fp16 ----
+  f16x8 qf[4];
+  float cq;  // score multiplier for query n: softmax scale * log2 e / 2^eq
+  {
+    float qv[32];
+    const bool real = n < G;
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + b * a.q_sb + (kvh * G + (real ? n : 0)) * a.q_sh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 raw = real ? *reinterpret_cast<const u32x4 *>(qrow + 32 * g + 8 * c) : u32x4{0, 0, 0, 0};
+      const bf16x8 hv = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[8 * c + e] = static_cast<float>(hv[e]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(qv[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const int eq = amax > 0.f ? min(14 - exp_of(amax), 100) : 0;  // amax * 2^eq in [2^13, 2^14)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<_Float16>(ldexpf(qv[8 * c + e], eq));
+    cq = ldexpf(a.c, -eq);
+  }
+
+  // ---- value-scale prescale of this wavefront: w = p * vs * 2^fw <= 2^14 ----
+  int fw = 0;
+  {
+    float vmax = 0.f;
+    // w0 is a multiple of 32 tokens, so every 16-byte load is aligned
+    for (int t = w0 + 8 * lane; t < w1; t += 8 * 64) {
+      const u32x2 lo = load_scales4(rvs, t, a.sc_vec != 0);
+      const u32x2 hi = load_scales4(rvs, t + 4, a.sc_vec != 0);
+      const f16x8 sv = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t + e < w1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    fw = vmax > 0.f ? min(14 - exp_of(vmax), 100) : 0;
+  }
+  const float wmul = ldexpf(1.f, fw);
+
+  // ---- tile loads ----
+  const bool sreal = n < G;
+  auto load_tile = [&](TileRegs &r, int t0) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tok = t0 + 16 * tb + n;
+      const unsigned off = tok < w1 ? static_cast<unsigned>(tok) * a.kv_ss + 32u * g : kOOB;
+      r.k[tb][0] = buf_load16(rk, off);
+      r.k[tb][1] = buf_load16(rk, off + 16u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = t0 + 4 * g + (j & 3) + 16 * (j >> 2);
+      const unsigned off = tok < w1 ? static_cast<unsigned>(tok) * a.kv_ss + 8u * n : kOOB;
+      r.v[j] = buf_load8(rv, off);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = t0 + 16 * tb + 4 * g;
+      r.ks[tb] = sreal ? load_scales4(rks, t, a.sc_vec != 0) : u32x2{0, 0};
+      r.vs[tb] = sreal ? load_scales4(rvs, t, a.sc_vec != 0) : u32x2{0, 0};
+    }
+  };
+
+  float m_run = neg_inf();
+  float l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) oacc[j] = f32x4{};
+
+  auto compute_tile = [&](const TileRegs &r, int t0) {
+    // S^T = K Q^T, two 16-token blocks
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sacc[tb] = f32x4{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 raw = r.k[tb][s >> 1];
+        unsigned w[4];
+        i8x4_to_f16(raw[2 * (s & 1)], w[0], w[1]);
+        i8x4_to_f16(raw[2 * (s & 1) + 1], w[2], w[3]);
+        const f16x8 kf = __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], sacc[tb], 0, 0, 0);
+      }
+    }
+    // scores in log2 units; tokens t0 + 16tb + 4g + i
+    float sc[8];
+    float mx = neg_inf();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const f16x4 kscale = __builtin_bit_cast(f16x4, r.ks[tb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * tb + 4 * g + i;
+        float s = sacc[tb][i] * (static_cast<float>(kscale[i]) * cq);
+        s = tok < w1 ? s : neg_inf();
+        sc[4 * tb + i] = s;
+        mx = fmaxf(mx, s);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == neg_inf() ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float lsum = 0.f;
+    f16x8 pf;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const f16x4 vscale = __builtin_bit_cast(f16x4, r.vs[tb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(sc[4 * tb + i] - m_use);
+        lsum += p;
+        pf[4 * tb + i] = static_cast<_Float16>(p * (static_cast<float>(vscale[i]) * wmul));
+      }
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    // V^T operands: block j holds head-dim column 8n + j of tokens
+    // {4g..4g+3, 16+4g..16+4g+3}; built pairwise from the 8-byte rows
+    unsigned vt[8][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        unsigned out[4];
+        i8_pair_transpose(r.v[2 * p][hd], r.v[2 * p + 1][hd], out);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vt[4 * hd + k][p] = out[k];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      oacc[j] *= alpha;
+      const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{vt[j][0], vt[j][1], vt[j][2], vt[j][3]});
+      oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[j], 0, 0, 0);
+    }
+  };
+
+  // ---- stream this wavefront's range, one tile of prefetch ----
+  if (ntiles > 0) {
+    TileRegs ra, rb;
+    load_tile(ra, w0);
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      load_tile(rb, w0 + (t + 1) * kTile);
+      compute_tile(ra, w0 + t * kTile);
+      if (t + 2 < ntiles) load_tile(ra, w0 + (t + 2) * kTile);
+      compute_tile(rb, w0 + (t + 1) * kTile);
+    }
+    if (t < ntiles) compute_tile(ra, w0 + t * kTile);
+  }
+
+  // ---- wavefront partial: O_w = O_acc / (l 2^fw), lse2_w = m + log2 l ----
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (n < G) {
+    const float inv = l_tot > 0.f ? ldexpf(1.f / l_tot, -fw) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[wave][n][32 * g + 8 * i + j] = oacc[j][i] * inv;
+    if (g == 0) s_l[wave][n] = l_tot > 0.f ? m_run + __log2f(l_tot) : neg_inf();
+  }
+  __syncthreads();
+
+  // ---- merge the four wavefronts into this split's partial ----
+  for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
+    const int qn = idx / kD, d = idx % kD;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_l[w][qn]);
+    float lse2 = neg_inf(), o = 0.f;
+    if (M != neg_inf()) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) tot += fast_exp2(s_l[w][qn] - M);
+      lse2 = M + __log2f(tot);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o += fast_exp2(s_l[w][qn] - lse2) * s_o[w][qn][d];
+    }
+    const long long row = (static_cast<long long>(split) * a.B + b) * a.Hq + kvh * G + qn;
+    a.ws_o[row * kD + d] = o;
+    if (d == 0) a.ws_l[row] = lse2;
+  }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
+void decode_combine_kernel(const DecodeArgs a) {
+  const int d = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const long long stride = static_cast<long long>(a.B) * a.Hq;
+  float M = neg_inf();
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_l[s * stride + bh]);
+  float lse2 = neg_inf(), o = 0.f;
+  if (M != neg_inf()) {
+    float tot = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) tot += fast_exp2(a.ws_l[s * stride + bh] - M);
+    lse2 = M + __log2f(tot);
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float wgt = fast_exp2(a.ws_l[s * stride + bh] - lse2);
+      o += wgt * a.ws_o[(s * stride + bh) * kD + d];
+    }
+  }
+  __bf16 *orow = static_cast<__bf16 *>(a.o) + b * a.o_sb + h * a.o_sh;
+  orow[d] = static_cast<__bf16>(o);
+  if (d == 0 && a.lse != nullptr) a.lse[b * a.lse_sb + h * a.lse_sh] = lse2 * kLn2;
+}
+
+}  // namespace fa
+
+int fa_launch_decode(const fa_decode_params *p, void *stream) {
+  using namespace fa;
+  DecodeArgs a{};
+  a.q = p->q;
+  a.k = p->k_cache;
+  a.v = p->v_cache;
+  a.ks = p->k_scale;
+  a.vs = p->v_scale;
+  a.seq_lens = p->seq_lens;
+  a.o = p->o;
+  a.lse = p->lse;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.G = p->Hq / p->Hkv;
+  a.L = p->L;
+  a.nsplit = p->num_splits;
+  // chunk length rounded up to whole 32-token tiles: every tile then starts on
+  // a 64-byte boundary of the scale arrays
+  a.chunk = ((p->L + p->num_splits - 1) / p->num_splits + kTile - 1) / kTile * kTile;
+  a.q_sb = p->q_strides[0];
+  a.q_sh = p->q_strides[1];
+  a.kv_sb = p->kv_strides[0];
+  a.kv_sh = p->kv_strides[1];
+  a.sc_sb = p->scale_strides[0];
+  a.sc_sh = p->scale_strides[1];
+  a.o_sb = p->o_strides[0];
+  a.o_sh = p->o_strides[1];
+  a.lse_sb = p->lse_strides[0];
+  a.lse_sh = p->lse_strides[1];
+  a.kv_ss = p->L > 1 ? static_cast<unsigned>(p->kv_strides[2]) : 0u;
+  a.kv_ext = p->L > 0 ? static_cast<unsigned>((static_cast<long long>(p->L - 1) * p->kv_strides[2] + p->d)) : 0u;
+  a.sc_ext = static_cast<unsigned>(p->L) * 2u;
+  a.sc_vec = (reinterpret_cast<uintptr_t>(p->k_scale) % 16 == 0 && reinterpret_cast<uintptr_t>(p->v_scale) % 16 == 0 &&
+              (p->scale_strides[0] * 2) % 16 == 0 && (p->scale_strides[1] * 2) % 16 == 0)
+                 ? 1 : 0;
+  a.c = p->softmax_scale * 1.4426950408889634f;
+  const size_t rows = static_cast<size_t>(p->num_splits) * p->B * p->Hq;
+  a.ws_o = static_cast<float *>(p->workspace);
+  a.ws_l = reinterpret_cast<float *>(static_cast<char *>(p->workspace) +
+                                     ((rows * kD * sizeof(float) + 255) & ~size_t(255)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
+  hipLaunchKernelGGL(decode_split_kernel, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode split launch: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(p->B) * p->Hq), dim3(kD), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode combine launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
