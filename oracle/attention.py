@@ -91,11 +91,13 @@ def _two_pass_rows(qh, kh, vh, scale, n_vis, row_block):
 
 
 def attention_fp64(q, k, v, causal: bool = False, scale: float | None = None,
-                   heads=None, row_block: int = 512, threads: int | None = None):
+                   heads=None, row_block: int = 512, threads: int | None = None, rows=None):
     """Exact attention in float64.
 
     q [B,Hq,Sq,d]; k [B,Hkv,Sk,d]; v [B,Hkv,Sk,dv]; Hq % Hkv == 0.
-    Returns (O [B,Hq,Sq,dv] float64, LSE [B,Hq,Sq] float64).
+    Returns (O [B,Hq,R,dv] float64, LSE [B,Hq,R] float64) with R = Sq, or
+    R = len(rows) when ``rows`` lists the query rows to evaluate (absolute
+    positions, so the causal rule is unchanged) — for sampled checks.
     ``heads``: optional iterable of (b, h) pairs; only those are computed (the
     other entries stay O = 0, LSE = -inf) — for sampled checks at full size.
     """
@@ -108,15 +110,16 @@ def attention_fp64(q, k, v, causal: bool = False, scale: float | None = None,
     assert Hq % Hkv == 0
     G = Hq // Hkv
     tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
-    n_vis = np.array([visible_keys(i, Sq, Sk, causal) for i in range(Sq)], dtype=np.int64)
-    o = np.zeros((B, Hq, Sq, v.shape[3]), dtype=np.float64)
-    lse = np.full((B, Hq, Sq), -np.inf, dtype=np.float64)
+    sel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    n_vis = np.array([visible_keys(int(i), Sq, Sk, causal) for i in sel], dtype=np.int64)
+    o = np.zeros((B, Hq, len(sel), v.shape[3]), dtype=np.float64)
+    lse = np.full((B, Hq, len(sel)), -np.inf, dtype=np.float64)
     work = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
 
     def one(bh):
         b, h = bh
         kvh = h // G
-        o[b, h], lse[b, h] = _two_pass_rows(q[b, h], k[b, kvh], v[b, kvh], tau, n_vis, row_block)
+        o[b, h], lse[b, h] = _two_pass_rows(q[b, h][sel], k[b, kvh], v[b, kvh], tau, n_vis, row_block)
 
     nthreads = threads or _default_threads()
     if nthreads <= 1 or len(work) <= 1:

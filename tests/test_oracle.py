@@ -192,6 +192,19 @@ def test_two_tile_exercise_golden():
     assert np.allclose(o2[0, 0], g["final"]["o"], atol=1e-12)
 
 
+def test_row_selection_matches_full_evaluation():
+    q = rnd((1, 4, 40, 8), 60)
+    k = rnd((1, 2, 40, 8), 61)
+    v = rnd((1, 2, 40, 8), 62)
+    rows = [0, 5, 17, 39]
+    for causal in (False, True):
+        o, lse = oracle.attention_fp64(q, k, v, causal)
+        o2, lse2 = oracle.attention_fp64(q, k, v, causal, rows=rows, heads=[(0, 1), (0, 3)])
+        for h in (1, 3):
+            assert np.array_equal(o2[0, h], o[0, h, rows]) and np.array_equal(lse2[0, h], lse[0, h, rows])
+        assert np.all(o2[0, 0] == 0) and np.all(np.isneginf(lse2[0, 2]))
+
+
 def test_key_value_permutation_invariance():
     q = rnd((1, 2, 8, 6), 31)
     k = rnd((1, 2, 15, 6), 32)
