@@ -49,4 +49,28 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).  Used after
+// loads that must be complete on every path into a loop: it keeps the
+// compiler's wait analysis at the loop head from re-waiting on them behind
+// the loop's own prefetches.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// True if pred holds in any lane of the wavefront (wave-uniform result).
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Sum / max of 16 floats as a balanced tree (short dependency chains).
+__device__ __forceinline__ float tree_sum16(const float *x) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[i] + x[i + 8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] += a[i + 4];
+  return (a[0] + a[2]) + (a[1] + a[3]);
+}
+
+// Online-softmax lazy rescale threshold (log2 units): the running max moves
+// only when a row's new max exceeds it by more than this, so probabilities
+// stay below 2^kRescaleSlack and most tiles skip the O rescale entirely.
+constexpr float kRescaleSlack = 8.0f;
+
 }  // namespace fa

@@ -67,9 +67,11 @@ inline FwdArgs make_fwd_args(const fa_fwd_params *p, int br, int es) {
   a.o_ss = p->o_strides[2];
   a.lse_sb = p->lse_strides[0];
   a.lse_sh = p->lse_strides[1];
-  a.q_ss = p->Sq > 1 ? static_cast<unsigned>(p->q_strides[2] * es) : 0u;
-  a.k_ss = p->Sk > 1 ? static_cast<unsigned>(p->k_strides[2] * es) : 0u;
-  a.v_ss = p->Sk > 1 ? static_cast<unsigned>(p->v_strides[2] * es) : 0u;
+  // a one-row tensor gets the virtual stride d: any row past the first then
+  // starts at or beyond the slice end and reads as zero
+  a.q_ss = static_cast<unsigned>((p->Sq > 1 ? p->q_strides[2] : p->d) * es);
+  a.k_ss = static_cast<unsigned>((p->Sk > 1 ? p->k_strides[2] : p->d) * es);
+  a.v_ss = static_cast<unsigned>((p->Sk > 1 ? p->v_strides[2] : p->d) * es);
   a.q_ext = slice_bytes(p->Sq, p->q_strides[2], p->d, es);
   a.k_ext = slice_bytes(p->Sk, p->k_strides[2], p->d, es);
   a.v_ext = slice_bytes(p->Sk, p->v_strides[2], p->d, es);

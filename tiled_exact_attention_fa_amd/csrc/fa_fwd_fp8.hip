@@ -14,10 +14,10 @@
 //     order that makes lane half h's 32 score accumulators the keys
 //     32h .. 32h+31 of the tile, i.e. exactly the 32 P^T bytes it feeds to the
 //     next product; the matching V^T bytes are one contiguous 32-byte LDS read.
-//   * P = exp2(s - m) is scaled by 256 before it is rounded to e4m3, so that
-//     probabilities down to 2^-14 stay normal numbers; the factor is removed
-//     with the row sum in the epilogue.  The row sum itself uses the unrounded
-//     fp32 probabilities.
+//   * P = exp2(s - m) is scaled by kPScale before it is rounded to e4m3, so
+//     that small probabilities stay normal numbers; the factor is removed with
+//     the row sum in the epilogue.  The row sum itself uses the unrounded fp32
+//     probabilities.
 //   * V is transposed in registers (4 keys x 8 columns per thread, byte
 //     permutes) on its way into a double-buffered LDS stage.
 #include "fa_device.hpp"
@@ -39,7 +39,12 @@ constexpr int K_TILE = BC * KROW;
 constexpr int V_TILE = D * VROW;
 constexpr int STAGE = K_TILE + V_TILE;
 constexpr int LDS_BYTES = 2 * STAGE;
-constexpr float kPScale = 256.f;
+// P is multiplied by kPScale before rounding to e4m3 (max 448).  With the
+// lazy running max, P itself can reach 2^kSlack8, so kPScale * 2^kSlack8 = 256
+// keeps every scaled probability at or below 256, and probabilities down to
+// 2^-10 of the running max stay normal e4m3 numbers.
+constexpr float kSlack8 = 4.0f;
+constexpr float kPScale = 16.f;
 
 // LDS row of key kr of a tile: block mb = (kr >> 4) & 1, half h = kr >> 5,
 // register i = kr & 15 of that block's accumulator, whose C row is
@@ -91,6 +96,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
       const u32x4 hi = buf_load16(rq, ok ? base + 16u : kOOB);
       qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
+    wait_vmem_all();
   }
 
   const int coff = a.Sk - a.Sq;
@@ -180,37 +186,45 @@ void fwd_fp8_kernel(const FwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (32 * h + 16 * mb + i > lim) sacc[mb][i] = neg_inf();
     }
-    float mx = neg_inf();
+    // lazy running max as in the 16-bit kernel, with the smaller slack kSlack8
+    float mxv[16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < 16; ++i) mxv[i] = fmaxf(sacc[0][i], sacc[1][i]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * cscale);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float lsum = 0.f;
+    for (int i = 0; i < 8; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 4]);
+    float mx = fmaxf(fmaxf(mxv[0], mxv[1]), fmaxf(mxv[2], mxv[3]));
+    mx = fmaxf(mx, swap_halves(mx)) * cscale;
+    const bool move = mx > m_run + kSlack8;
+    if (wave_any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
     int pw[8];
+    float ps[16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; i += 4) {
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(sacc[mb][i + e], cscale, -m_use));
-          lsum += p[e];
-        }
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[mb][i + e], cscale, -m_use));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps[i + e] = mb == 0 ? p[e] : ps[i + e] + p[e];
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
         pw[4 * mb + i / 4] = w;
       }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    l_run += tree_sum16(ps);
     const i32x8 pf{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      oacc[db] *= alpha;
       const unsigned char *vrow = vt + (32 * db + l32) * VROW + 32 * h;
       const u32x4 lo = *reinterpret_cast<const u32x4 *>(vrow);
       const u32x4 hi = *reinterpret_cast<const u32x4 *>(vrow + 16);

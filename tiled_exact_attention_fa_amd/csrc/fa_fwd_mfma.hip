@@ -147,6 +147,7 @@ void fwd_mfma_kernel(const FwdArgs a) {
         for (int e = 0; e < 4; ++e) qf[4 * c + e] = vf[e];
       }
     }
+    wait_vmem_all();
   }
 
   // ---- tile range of this workgroup and of this wavefront ----
@@ -246,29 +247,40 @@ void fwd_mfma_kernel(const FwdArgs a) {
           if (acc_key<KW>(mb, i, h) > lim) sacc[mb][i] = neg_inf();
     }
 
-    // online softmax: new running max, rescale factor, probabilities
-    float mx = neg_inf();
+    // online softmax.  The running max m moves only when this tile's max
+    // exceeds it by more than kRescaleSlack (log2 units); otherwise the stale
+    // m is kept and P may reach 2^kRescaleSlack.  O / l and the LSE do not
+    // depend on the m used, so this is exact, and the O rescale runs only on
+    // tiles where some row of the wavefront moved its m.
+    float mxv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mxv[i] = C::MB == 2 ? fmaxf(sacc[0][i], sacc[C::MB - 1][i]) : sacc[0][i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 4]);
+    float mx = fmaxf(fmaxf(mxv[0], mxv[1]), fmaxf(mxv[2], mxv[3]));
+    mx = fmaxf(mx, swap_halves(mx)) * cscale;
+    const bool move = mx > m_run + kRescaleSlack;  // also true on the first live tile
+    if (wave_any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * cscale);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float lsum = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[mb][i] = fast_exp2(__builtin_fmaf(sacc[mb][i], cscale, -m_use));
+    {
+      float ps[16];
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[mb][i], cscale, -m_use));
-        sacc[mb][i] = p;
-        lsum += p;
-      }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      for (int i = 0; i < 16; ++i) ps[i] = C::MB == 2 ? sacc[0][i] + sacc[C::MB - 1][i] : sacc[0][i];
+      l_run += tree_sum16(ps);
+    }
 
     // O^T += V^T P^T
     if constexpr (KW == 8) {
@@ -339,10 +351,264 @@ void fwd_mfma_kernel(const FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel for the 16-bit types.  Per K/V tile a wavefront computes S^T = K Q^T,
+// the online softmax and O^T += V^T P^T.  Global loads go through a buffer
+// resource placed at the tile's first row, so per-lane offsets are loop
+// constants and rows past the end of the keys (or tiles past the workgroup's
+// range) read as zero without any per-lane address arithmetic.  LDS fragments
+// are read a full 32-key block ahead of the MFMAs that consume them.
+// ---------------------------------------------------------------------------
+#ifndef FA16_WAVES_PER_EU
+#define FA16_WAVES_PER_EU 2
+#endif
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+template <typename T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
+void fwd_mfma16_kernel(const FwdArgs a) {
+  using C = Cfg<T, D>;
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int BC = C::BC, EPC = C::EPC, CH = C::CH, ES = C::ES;
+  constexpr int QS = D / 16;
+  static_assert(C::KW == 8 && BC == 64, "16-bit kernel expects 64-key tiles");
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T *kbuf = reinterpret_cast<T *>(smem);   // [2][BC][KROW]
+  T *vbuf = kbuf + 2 * C::K_TILE;          // [2][D][VROW]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  int bh, qt;
+  map_block(blockIdx.x, a.nq, a.B * a.Hq, bh, qt);
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, hk = hq / a.G;
+  const int i0 = qt * C::BR;
+  const int wrow0 = i0 + 32 * wave;
+  const int row = wrow0 + l32;
+
+  // ---- Q rows into registers: lane half h holds d in [D/2*h, D/2*h + D/2) ----
+  frag qf[QS];
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
+    const bool ok = row < a.Sq;
+#pragma unroll
+    for (int c = 0; c < QS; ++c)
+      qf[c] = __builtin_bit_cast(frag, buf_load16(rq, ok ? row * a.q_ss + ((D / 2) * h + c * EPC) * ES : kOOB));
+    wait_vmem_all();
+  }
+
+  const int coff = a.Sk - a.Sq;
+  int n_kt = (a.Sk + BC - 1) / BC;
+  int w_kt = n_kt;
+  if (CAUSAL) {
+    const int last_wg = i0 + C::BR - 1 + coff;
+    n_kt = min(n_kt, last_wg < 0 ? 0 : last_wg / BC + 1);
+    const int last_w = wrow0 + 31 + coff;
+    w_kt = min(n_kt, last_w < 0 ? 0 : last_w / BC + 1);
+  }
+
+  // ---- per-tile buffer resources, loop-constant lane offsets ----
+  const char *kbase = reinterpret_cast<const char *>(static_cast<const T *>(a.k) + b * a.k_sb + hk * a.k_sh);
+  const char *vbase = reinterpret_cast<const char *>(static_cast<const T *>(a.v) + b * a.v_sb + hk * a.v_sh);
+  auto tile_rsrc = [&](const char *base, unsigned ss, unsigned ext, int j) {
+    const unsigned long long shift = static_cast<unsigned long long>(j) * BC * ss;
+    const unsigned recs = (j < n_kt && shift < ext) ? ext - static_cast<unsigned>(shift) : 0u;
+    return make_rsrc(base + shift, recs);
+  };
+  const int k_c = tid % CH, k_r = tid / CH;
+  const int v_g = tid % C::NG, v_c = tid / C::NG;
+  unsigned koff[C::PASSES], voff[C::PASSES];
+#pragma unroll
+  for (int p = 0; p < C::PASSES; ++p) {
+    koff[p] = (k_r + (256 / CH) * p) * a.k_ss + k_c * 16;
+    voff[p] = (v_g * C::KPT + p) * a.v_ss + v_c * 16;
+  }
+  u32x4 kreg[C::PASSES], vreg[C::PASSES];
+  auto load_k = [&](int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) kreg[p] = buf_load16(r, koff[p]);
+  };
+  auto load_v = [&](int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) vreg[p] = buf_load16(r, voff[p]);
+  };
+  auto store_k = [&](int buf) {
+    T *ks = kbuf + buf * C::K_TILE;
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p)
+      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (256 / CH) * p) * C::KROW + k_c * EPC) = kreg[p];
+  };
+  auto store_v = [&](int buf) {
+    T *vt = vbuf + buf * C::V_TILE;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      T col[C::KPT];
+#pragma unroll
+      for (int p = 0; p < C::KPT; ++p) col[p] = reinterpret_cast<const T *>(&vreg[p])[e];
+      T *dst = vt + (v_c * EPC + e) * C::VROW + v_g * C::KPT;
+      if constexpr (C::KPT * ES == 8) *reinterpret_cast<u32x2 *>(dst) = __builtin_bit_cast(u32x2, col);
+      else *reinterpret_cast<unsigned *>(dst) = __builtin_bit_cast(unsigned, col);
+    }
+  };
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+
+  // S^T = K Q^T from K buffer `buf`.  All 8 fragments of one 32-key block are
+  // read before its MFMAs, and the next block's reads are issued as the
+  // current block's fragments are consumed, so LDS latency hides behind MFMAs.
+  auto qk = [&](int buf, f32x16 s[2]) {
+    const T *kt = kbuf + buf * C::K_TILE + l32 * C::KROW + (D / 2) * h;
+    u32x4 kf[QS];
+#pragma unroll
+    for (int c = 0; c < QS; ++c) kf[c] = *reinterpret_cast<const u32x4 *>(kt + c * EPC);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < QS; ++c) {
+      s[0] = M::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s[0]);
+      kf[c] = *reinterpret_cast<const u32x4 *>(kt + 32 * C::KROW + c * EPC);
+    }
+#pragma unroll
+    for (int c = 0; c < QS; ++c) s[1] = M::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s[1]);
+    // keep the reads QS fragments ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);
+#pragma unroll
+    for (int c = 0; c < QS; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);
+  };
+  // O^T += V^T P^T from V buffer `buf`, same read-ahead scheme
+  auto pv = [&](int buf, const frag pf[4]) {
+    const T *vt = vbuf + buf * C::V_TILE + l32 * C::VROW + 8 * h;
+    u32x4 vf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const u32x4 *>(vt + (i >> 2) * 32 * C::VROW + 16 * (i & 3));
+#pragma unroll
+    for (int i = 0; i < 4 * C::DB; ++i) {
+      const int db = i >> 2, tt = i & 3;
+      oacc[db] = M::mma(__builtin_bit_cast(frag, vf[i & 7]), pf[tt], oacc[db]);
+      if (i + 8 < 4 * C::DB)
+        vf[i & 7] = *reinterpret_cast<const u32x4 *>(vt + ((i + 8) >> 2) * 32 * C::VROW + 16 * ((i + 8) & 3));
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i + 8 < 4 * C::DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  float m_run = neg_inf();
+  float l_run = 0.f;
+  const float cscale = a.c;
+
+  // ---- prologue: tile 0 into stage 0 ----
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_kt; ++j) {
+    const int st = j & 1;
+    load_k(j + 1);  // tiles past the workgroup's range read as zeros
+    load_v(j + 1);
+    if (j < w_kt) {
+      f32x16 s_cur[2];
+      qk(st, s_cur);
+      const int j0 = j * BC;
+      // mask (tiles that cross the diagonal or the end of the keys)
+      const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
+      if (edge) {
+        const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (acc_key<8>(mb, i, h) > lim) s_cur[mb][i] = neg_inf();
+      }
+      // row max of the tile (max3 tree, then the other lane half)
+      float t[11];
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
+        t[i] = max3f(s_cur[x >> 4][x & 15], s_cur[y >> 4][y & 15], s_cur[z >> 4][z & 15]);
+      }
+      t[10] = fmaxf(s_cur[1][14], s_cur[1][15]);
+      float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
+      mx = fmaxf(mx, swap_halves(mx)) * cscale;
+      // lazy running max: move only when the tile max exceeds it by the slack
+      const bool move = mx > m_run + kRescaleSlack;
+      const float m_new = move ? mx : m_run;
+      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+      m_run = m_new;
+      if (wave_any(move)) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      }
+      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+      frag pf[4];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        unsigned w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(s_cur[tt >> 1][8 * (tt & 1) + 2 * e], cscale, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(s_cur[tt >> 1][8 * (tt & 1) + 2 * e + 1], cscale, -m_use));
+          typedef T v2 __attribute__((ext_vector_type(2)));
+          w[e] = __builtin_bit_cast(unsigned, v2{static_cast<T>(p0), static_cast<T>(p1)});
+          // the row sum uses the unrounded probabilities: the LSE must not
+          // carry the rounding of P to 16 bits
+          ls[e] += p0 + p1;
+        }
+        pf[tt] = __builtin_bit_cast(frag, u32x4{w[0], w[1], w[2], w[3]});
+      }
+      l_run = __builtin_fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+      pv(st, pf);
+    }
+    store_k(st ^ 1);
+    store_v(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l) ----
+  const float l_tot = l_run + swap_halves(l_run);
+  if (row < a.Sq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    T *orow = static_cast<T *>(a.o) + b * a.o_sb + hq * a.o_sh + static_cast<long long>(row) * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        T out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * g + e] * inv);
+        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 int launch_one(const FwdArgs &args, hipStream_t stream) {
   using C = Cfg<T, D>;
-  auto kern = fwd_mfma_kernel<T, D, CAUSAL>;
+  void (*kern)(FwdArgs);
+  if constexpr (sizeof(T) == 2) kern = fwd_mfma16_kernel<T, D, CAUSAL>;
+  else kern = fwd_mfma_kernel<T, D, CAUSAL>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
