@@ -45,6 +45,7 @@ constexpr int LDS_BYTES = 2 * STAGE;
 // 2^-10 of the running max stay normal e4m3 numbers.
 constexpr float kSlack8 = 4.0f;
 constexpr float kPScale = 16.f;
+constexpr float kLog2PScale = 4.f;
 
 // LDS row of key kr of a tile: block mb = (kr >> 4) & 1, half h = kr >> 5,
 // register i = kr & 15 of that block's accumulator, whose C row is
@@ -80,10 +81,6 @@ void fwd_fp8_kernel(const FwdArgs a) {
 
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(static_cast<const unsigned char *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(static_cast<const unsigned char *>(a.k) + b * a.k_sb + hk * a.k_sh, a.k_ext);
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(static_cast<const unsigned char *>(a.v) + b * a.v_sb + hk * a.v_sh, a.v_ext);
 
   // Q: lane half h holds bytes [64h, 64h + 64) of its row; step s uses 32 of them
   i32x8 qf[2];
@@ -111,22 +108,31 @@ void fwd_fp8_kernel(const FwdArgs a) {
 
   // K: thread t loads rows t/8 and t/8 + 32, 16-byte chunk t%8.
   // V: thread t loads keys 4*(t%16) .. +3 of the 8-byte column chunk t/16.
+  // Loads go through a buffer resource placed at the tile's first row, so the
+  // lane offsets are loop constants and rows past the keys read as zero.
   u32x4 kreg[2];
   u32x2 vreg[4];
   const int k_c = tid & 7, k_r = tid >> 3;
   const int v_g = tid & 15, v_c = tid >> 4;
+  const unsigned char *kbase = static_cast<const unsigned char *>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const unsigned char *vbase = static_cast<const unsigned char *>(a.v) + b * a.v_sb + hk * a.v_sh;
+  auto tile_rsrc = [&](const unsigned char *base, unsigned ss, unsigned ext, int j) {
+    const unsigned long long shift = static_cast<unsigned long long>(j) * BC * ss;
+    const unsigned recs = (j < n_kt && shift < ext) ? ext - static_cast<unsigned>(shift) : 0u;
+    return make_rsrc(base + shift, recs);
+  };
+  unsigned koff[2], voff[4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) koff[p] = (k_r + 32 * p) * a.k_ss + 16u * k_c;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) voff[p] = (4 * v_g + p) * a.v_ss + 8u * v_c;
   auto load_tile = [&](int j) {
-    const int j0 = j * BC;
+    const __amdgpu_buffer_rsrc_t rkj = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
+    const __amdgpu_buffer_rsrc_t rvj = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int kk = j0 + k_r + 32 * p;
-      kreg[p] = buf_load16(rk, kk < a.Sk ? kk * a.k_ss + 16u * k_c : kOOB);
-    }
+    for (int p = 0; p < 2; ++p) kreg[p] = buf_load16(rkj, koff[p]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int vk = j0 + 4 * v_g + p;
-      vreg[p] = buf_load8(rv, vk < a.Sk ? vk * a.v_ss + 8u * v_c : kOOB);
-    }
+    for (int p = 0; p < 4; ++p) vreg[p] = buf_load8(rvj, voff[p]);
   };
   auto store_tile = [&](int st) {
     unsigned char *ks = lds + st * STAGE;
@@ -164,18 +170,26 @@ void fwd_fp8_kernel(const FwdArgs a) {
     const unsigned char *vt = ks + K_TILE;
     const int j0 = j * BC;
     f32x16 sacc[2];
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        kr[mb][q] = *reinterpret_cast<const u32x4 *>(ks + (32 * mb + l32) * KROW + 64 * h + 16 * q);
+    __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves compete
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       sacc[mb] = f32x16{};
-      const unsigned char *krow = ks + (32 * mb + l32) * KROW + 64 * h;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const u32x4 lo = *reinterpret_cast<const u32x4 *>(krow + 32 * s);
-        const u32x4 hi = *reinterpret_cast<const u32x4 *>(krow + 32 * s + 16);
+        const u32x4 lo = kr[mb][2 * s], hi = kr[mb][2 * s + 1];
         const i32x8 kf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         sacc[mb] = mma(kf, qf[s], sacc[mb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // accumulator (block mb, register i, half h) is key 32h + 16mb + i
     const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
     if (edge) {
@@ -205,7 +219,8 @@ void fwd_fp8_kernel(const FwdArgs a) {
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+    // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
+    const float m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale;
     int pw[8];
     float ps[16];
 #pragma unroll
@@ -217,20 +232,25 @@ void fwd_fp8_kernel(const FwdArgs a) {
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[mb][i + e], cscale, -m_use));
 #pragma unroll
         for (int e = 0; e < 4; ++e) ps[i + e] = mb == 0 ? p[e] : ps[i + e] + p[e];
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[4 * mb + i / 4] = w;
       }
     l_run += tree_sum16(ps);
     const i32x8 pf{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    u32x4 vr[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) vr[db][q] = *reinterpret_cast<const u32x4 *>(vt + (32 * db + l32) * VROW + 32 * h + 16 * q);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const unsigned char *vrow = vt + (32 * db + l32) * VROW + 32 * h;
-      const u32x4 lo = *reinterpret_cast<const u32x4 *>(vrow);
-      const u32x4 hi = *reinterpret_cast<const u32x4 *>(vrow + 16);
+      const u32x4 lo = vr[db][0], hi = vr[db][1];
       const i32x8 vf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       oacc[db] = mma(vf, pf, oacc[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (n_kt > 0) {
@@ -248,7 +268,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
 
   const float l_tot = l_run + swap_halves(l_run);
   if (row < a.Sq) {
-    const float inv = l_tot > 0.f ? a.o_mul / (l_tot * kPScale) : 0.f;
+    const float inv = l_tot > 0.f ? a.o_mul / l_tot : 0.f;  // l_tot = kPScale * l: the factor cancels
     __bf16 *orow = static_cast<__bf16 *>(a.o) + b * a.o_sb + hq * a.o_sh + static_cast<long long>(row) * a.o_ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -260,7 +280,8 @@ void fwd_fp8_kernel(const FwdArgs a) {
         *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+      a.lse[b * a.lse_sb + hq * a.lse_sh + row] =
+          l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PScale) * kLn2 : neg_inf();
   }
 }
 

@@ -527,7 +527,9 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     load_v(j + 1);
     if (j < w_kt) {
       f32x16 s_cur[2];
+      __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves compete
       qk(st, s_cur);
+      __builtin_amdgcn_s_setprio(0);
       const int j0 = j * BC;
       // mask (tiles that cross the diagonal or the end of the keys)
       const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
@@ -577,7 +579,9 @@ void fwd_mfma16_kernel(const FwdArgs a) {
         pf[tt] = __builtin_bit_cast(frag, u32x4{w[0], w[1], w[2], w[3]});
       }
       l_run = __builtin_fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+      __builtin_amdgcn_s_setprio(1);
       pv(st, pf);
+      __builtin_amdgcn_s_setprio(0);
     }
     store_k(st ^ 1);
     store_v(st ^ 1);
