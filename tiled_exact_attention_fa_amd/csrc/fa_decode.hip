@@ -29,11 +29,13 @@
 //   * The bf16 query is prescaled by a power of two per head so it converts to
 //     fp16 exactly; the probabilities times value scales are prescaled by a
 //     power of two per wavefront, chosen from the largest value scale of its
-//     range, so they neither overflow nor lose range in fp16.  Both factors are
+//     range, so they neither overflow nor lose range in fp16 (probabilities
+//     reach 2^8 under the lazy running max, see kRescaleSlack).  Both factors are
 //     undone in fp32.
 //   * Kernel 2 (decode_combine_kernel) merges the splits of one (batch, head):
-//     LSE = M + log2 sum_s 2^(lse_s - M), O = sum_s 2^(lse_s - LSE) O_s, in the
-//     log2 domain, and writes bf16 O and natural-log LSE.
+//     with M = max_s lse_s and w_s = 2^(lse_s - M), LSE = M + log2 sum_s w_s and
+//     O = sum_s w_s O_s / sum_s w_s, in the log2 domain; it writes bf16 O and
+//     natural-log LSE.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -120,7 +122,7 @@ struct TileRegs {
   u32x2 vs[2];     // 4 fp16 value scales per token block
 };
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
@@ -180,7 +182,8 @@ void decode_split_kernel(const DecodeArgs a) {
     cq = ldexpf(a.c, -eq);
   }
 
-  // ---- value-scale prescale of this wavefront: w = p * vs * 2^fw <= 2^14 ----
+  // ---- value-scale prescale of this wavefront: vs * 2^fw < 2^6, so with
+  // p < 2^kRescaleSlack (= 2^8) every w = p * vs * 2^fw stays below 2^14 ----
   int fw = 0;
   {
     float vmax = 0.f;
@@ -195,7 +198,7 @@ void decode_split_kernel(const DecodeArgs a) {
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
-    fw = vmax > 0.f ? min(14 - exp_of(vmax), 100) : 0;
+    fw = vmax > 0.f ? min(6 - exp_of(vmax), 100) : 0;
   }
   const float wmul = ldexpf(1.f, fw);
 
@@ -262,9 +265,12 @@ void decode_split_kernel(const DecodeArgs a) {
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    // lazy running max: the O rescale runs only when some row's max moved by
+    // more than the slack (probabilities stay below 2^kRescaleSlack)
+    const bool move = mx > m_run + kRescaleSlack;
+    const float m_new = move ? mx : m_run;
+    const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
     const float m_use = m_new == neg_inf() ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
     float lsum = 0.f;
     f16x8 pf;
 #pragma unroll
@@ -292,9 +298,12 @@ void decode_split_kernel(const DecodeArgs a) {
         for (int k = 0; k < 4; ++k) vt[4 * hd + k][p] = out[k];
       }
     }
+    if (wave_any(move)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      oacc[j] *= alpha;
       const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{vt[j][0], vt[j][1], vt[j][2], vt[j][3]});
       oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[j], 0, 0, 0);
     }
@@ -351,21 +360,41 @@ void decode_split_kernel(const DecodeArgs a) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
 void decode_combine_kernel(const DecodeArgs a) {
+  // one workgroup per (batch, query head); thread d owns output column d.
+  // Splits are taken 16 at a time with all loads of a group in flight.
   const int d = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const long long stride = static_cast<long long>(a.B) * a.Hq;
+  constexpr int kGroup = 16;
   float M = neg_inf();
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_l[s * stride + bh]);
+  for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+    float l[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) l[i] = s0 + i < a.nsplit ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) M = fmaxf(M, l[i]);
+  }
   float lse2 = neg_inf(), o = 0.f;
   if (M != neg_inf()) {
-    float tot = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) tot += fast_exp2(a.ws_l[s * stride + bh] - M);
-    lse2 = M + __log2f(tot);
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float wgt = fast_exp2(a.ws_l[s * stride + bh] - lse2);
-      o += wgt * a.ws_o[(s * stride + bh) * kD + d];
+    float tot = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+      float l[kGroup], v[kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const bool ok = s0 + i < a.nsplit;
+        l[i] = ok ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
+        v[i] = ok ? a.ws_o[((s0 + i) * stride + bh) * kD + d] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const float w = fast_exp2(l[i] - M);  // 0 for empty splits
+        tot += w;
+        acc += w * v[i];
+      }
     }
+    lse2 = M + __log2f(tot);
+    o = acc / tot;
   }
   __bf16 *orow = static_cast<__bf16 *>(a.o) + b * a.o_sb + h * a.o_sh;
   orow[d] = static_cast<__bf16>(o);
