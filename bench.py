@@ -223,6 +223,62 @@ def cpu_baseline(name, budget_s=12.0):
                       f"{elapsed:.1f} s wall"}
 
 
+# ---- HBM traffic from rocprofv3 counters ------------------------------------
+
+def copy_calibration(nbytes: int, reps: int = 3):
+    """A plain device copy of nbytes (read nbytes, write nbytes), for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)  # an elementwise kernel: reads x once, writes y once
+    torch.cuda.synchronize()
+
+
+def _pmc_per_dispatch(csv_dir: str, counter: str, kernel_substr: str):
+    import csv
+    import glob
+
+    vals = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} under {csv_dir}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_pmc(a):
+    """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the
+    workload, and of the copy calibration) into bytes per launch, records them
+    in profiles/hbm_traffic.json with the kernel-source digest, and prints a
+    markdown summary."""
+    nbytes = a.calib_bytes
+    cf, _ = _pmc_per_dispatch(a.calib_fetch, "FETCH_SIZE", a.calib_kernel)
+    cw, _ = _pmc_per_dispatch(a.calib_write, "WRITE_SIZE", a.calib_kernel)
+    f_scale = nbytes / (cf * 1024.0)
+    w_scale = nbytes / (cw * 1024.0)
+    wf, nf = _pmc_per_dispatch(a.pmc_fetch, "FETCH_SIZE", a.kernel)
+    ww, nw = _pmc_per_dispatch(a.pmc_write, "WRITE_SIZE", a.kernel)
+    fetch = wf * 1024.0 * f_scale
+    write = ww * 1024.0 * w_scale
+    cfg = fa_inputs.CONFIGS[a.workload]
+    algo = decode_bytes(cfg) if isinstance(cfg, fa_inputs.DecodeConfig) else fwd_hbm_bytes(cfg)
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[a.workload] = {"kernel": a.kernel, "bytes_per_launch": fetch + write, "fetch_bytes": fetch,
+                        "write_bytes": write, "algorithmic_bytes": algo, "fetch_scale": f_scale,
+                        "write_scale": w_scale, "source_digest": source_digest()}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(f"| {a.workload} | {a.kernel} | {nf} | {wf:.0f} | {ww:.0f} | {f_scale:.4f} | {w_scale:.4f} | "
+          f"{fetch / 1e6:.1f} | {write / 1e6:.1f} | {algo / 1e6:.1f} | {(fetch + write) / algo:.3f} |")
+
+
 # ---- main ---------------------------------------------------------------------
 
 def main():
@@ -233,7 +289,24 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default="all", help="other workloads to time: all, none or a comma list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/hbm_traffic.json")
+    ap.add_argument("--pmc-fetch")
+    ap.add_argument("--pmc-write")
+    ap.add_argument("--calib-fetch")
+    ap.add_argument("--calib-write")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30)
+    ap.add_argument("--calib-kernel", default="MulFunctor")
+    ap.add_argument("--kernel", default="fwd_mfma16_kernel")
     a = ap.parse_args()
+    if a.summarize_pmc:
+        summarize_pmc(a)
+        return
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the path runs on a single device and has no multi-GPU mode)", file=sys.stderr)

@@ -23,18 +23,26 @@ struct FwdArgs {
 
 // blockIdx -> (batch*head, query tile).  Workgroups are handed to the 8 XCDs
 // round-robin (XCD = blockIdx % 8).  When the (batch, head) count divides by 8,
-// each XCD gets a contiguous range of (batch, head) pairs — consecutive query
-// heads share one K/V head under GQA — so every K/V stream is read through one
-// XCD's L2.  Within an XCD the last query tiles (the longest under a causal
-// mask) are issued first.
-__device__ __forceinline__ void map_block(int bid, int nq, int nbh, int &bh, int &qt) {
+// each XCD gets a contiguous range of (batch, head) pairs (consecutive query
+// heads share one K/V head under GQA), so every K/V stream is read through one
+// XCD's L2.  Within an XCD:
+//   * causal (tiles of unequal length): longest tiles first across all heads of
+//     the range, so the short tiles fill the tail of the launch;
+//   * non-causal (equal tiles): head by head, so the workgroups resident at
+//     any time read the K/V of only one or two heads, which stay in L2.
+__device__ __forceinline__ void map_block(int bid, int nq, int nbh, bool longest_first, int &bh, int &qt) {
+  int base = 0, per = nbh, slot = bid;
   if ((nbh & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3, per = nbh >> 3;
-    bh = xcd * per + slot % per;
+    per = nbh >> 3;
+    base = (bid & 7) * per;
+    slot = bid >> 3;
+  }
+  if (longest_first) {
+    bh = base + slot % per;
     qt = nq - 1 - slot / per;
   } else {
-    bh = bid % nbh;
-    qt = nq - 1 - bid / nbh;
+    bh = base + slot / nq;
+    qt = slot % nq;
   }
 }
 
