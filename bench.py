@@ -12,7 +12,8 @@ GQA prefill and fp8 prefill in TFLOP/s, int8-KV split decode in GB/s of the
 bytes the method must move (K/V codes + scales + query + output + LSE).
 
 Timing uses HIP events on the stream the kernels are launched on (torch's
-current stream), bracketed by device synchronisations.  The CPU baseline is the
+current stream), bracketed by device synchronisations, after at least W
+untimed calls and at least 0.3 s of untimed work, so the clocks have settled.  The CPU baseline is the
 float64 oracle timed on this host's cores over a bounded sample of the headline
 workload, rescaled to the same unit.  Prints ONE JSON line.
 """
@@ -82,11 +83,21 @@ def decode_bytes(cfg) -> int:
 
 # ---- GPU timing ---------------------------------------------------------------
 
+WARMUP_SECONDS = 0.3
+
+
 def _time_region(fn, steps, warmup):
+    """Mean per-call time (ms) of `steps` calls after at least `warmup` untimed
+    calls and at least WARMUP_SECONDS of untimed work (the clocks settle first)."""
     import torch
 
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARMUP_SECONDS:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)

@@ -29,6 +29,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 HIPFLAGS = COMMON + [
     "--offload-arch=gfx950",
     "-munsafe-fp-atomics",
+    # the kernels never rely on NaN propagation (masked scores are -inf, which
+    # stays honoured); without this, every fmaxf gets a canonicalising max
+    "-fno-honor-nans",
     # packed fp32 VALU forms are avoided on this hardware: keep the compiler
     # from selecting them for ordinary float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -42,8 +42,17 @@ __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// Value held by lane (lane ^ 32): the other half of the wavefront.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Value held by lane (lane ^ 32): the other half of the wavefront.  One
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with x in both, the first result holds x's lower
+// half in both halves and the second x's upper half, so lane l picks the
+// second result when l < 32 and the first otherwise.  No LDS round trip.
+__device__ __forceinline__ float swap_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const bool low = (threadIdx.x & 32) == 0;
+  return __builtin_bit_cast(float, low ? r[1] : r[0]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -33,6 +33,7 @@
 #include "fa_internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace fa {
 
@@ -82,6 +83,29 @@ template <typename T, int D> struct Cfg {
   static constexpr int DB = D / 32;             // 32-column blocks of O^T
   static constexpr int LDS_BYTES = 2 * STAGE * ES;
   static_assert(BC * CH % 256 == 0, "tile must split evenly over 256 threads");
+};
+
+
+// Configuration of the 16-bit kernel: 8 wavefronts (two per SIMD) own 256 query
+// rows, so each K/V tile is fetched and staged once for twice as many rows.
+template <typename T, int D> struct Cfg16 {
+  static constexpr int ES = sizeof(T);
+  static constexpr int KW = 8;
+  static constexpr int NT = 512;                // threads per workgroup
+  static constexpr int BR = 256;                // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int EPC = 8;                 // elements per 16-byte chunk
+  static constexpr int CH = D / EPC;            // chunks per row
+  static constexpr int PASSES = BC * CH / NT;   // 16-byte loads per thread per tile (K or V)
+  static constexpr int KPT = PASSES;            // keys per thread in the V transpose
+  static constexpr int NG = BC / KPT;           // V key groups
+  static constexpr int KROW = D + EPC;          // K row in LDS, +16 bytes
+  static constexpr int VROW = BC + EPC;         // V^T row in LDS, +16 bytes
+  static constexpr int K_TILE = BC * KROW;
+  static constexpr int V_TILE = D * VROW;
+  static constexpr int DB = D / 32;
+  static constexpr int LDS_BYTES = 2 * (K_TILE + V_TILE) * ES;
+  static_assert(BC * CH % NT == 0, "tile must split evenly over the workgroup");
 };
 
 // LDS row of key kr within a tile.  For 16-bit types bits 2 and 3 are swapped,
@@ -366,14 +390,13 @@ void fwd_mfma_kernel(const FwdArgs a) {
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
 void fwd_mfma16_kernel(const FwdArgs a) {
-  using C = Cfg<T, D>;
+  using C = Cfg16<T, D>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
   constexpr int BC = C::BC, EPC = C::EPC, CH = C::CH, ES = C::ES;
   constexpr int QS = D / 16;
-  static_assert(C::KW == 8 && BC == 64, "16-bit kernel expects 64-key tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T *kbuf = reinterpret_cast<T *>(smem);   // [2][BC][KROW]
@@ -425,36 +448,34 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   unsigned koff[C::PASSES], voff[C::PASSES];
 #pragma unroll
   for (int p = 0; p < C::PASSES; ++p) {
-    koff[p] = (k_r + (256 / CH) * p) * a.k_ss + k_c * 16;
+    koff[p] = (k_r + (C::NT / CH) * p) * a.k_ss + k_c * 16;
     voff[p] = (v_g * C::KPT + p) * a.v_ss + v_c * 16;
   }
-  u32x4 kreg[C::PASSES], vreg[C::PASSES];
-  auto load_k = [&](int j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
+  // two register sets: tile j is fetched two iterations before it is staged
+  u32x4 kreg[2][C::PASSES], vreg[2][C::PASSES];
+  auto load_kv = [&](int set, int j) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) kreg[p] = buf_load16(r, koff[p]);
-  };
-  auto load_v = [&](int j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
+    for (int p = 0; p < C::PASSES; ++p) kreg[set][p] = buf_load16(rk, koff[p]);
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) vreg[p] = buf_load16(r, voff[p]);
+    for (int p = 0; p < C::PASSES; ++p) vreg[set][p] = buf_load16(rv, voff[p]);
   };
-  auto store_k = [&](int buf) {
+  auto store_kv = [&](int set, int buf) {
     T *ks = kbuf + buf * C::K_TILE;
 #pragma unroll
     for (int p = 0; p < C::PASSES; ++p)
-      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (256 / CH) * p) * C::KROW + k_c * EPC) = kreg[p];
-  };
-  auto store_v = [&](int buf) {
+      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (C::NT / CH) * p) * C::KROW + k_c * EPC) = kreg[set][p];
     T *vt = vbuf + buf * C::V_TILE;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       T col[C::KPT];
 #pragma unroll
-      for (int p = 0; p < C::KPT; ++p) col[p] = reinterpret_cast<const T *>(&vreg[p])[e];
+      for (int p = 0; p < C::KPT; ++p) col[p] = reinterpret_cast<const T *>(&vreg[set][p])[e];
       T *dst = vt + (v_c * EPC + e) * C::VROW + v_g * C::KPT;
       if constexpr (C::KPT * ES == 8) *reinterpret_cast<u32x2 *>(dst) = __builtin_bit_cast(u32x2, col);
-      else *reinterpret_cast<unsigned *>(dst) = __builtin_bit_cast(unsigned, col);
+      else if constexpr (C::KPT * ES == 4) *reinterpret_cast<unsigned *>(dst) = __builtin_bit_cast(unsigned, col);
+      else *reinterpret_cast<unsigned short *>(dst) = __builtin_bit_cast(unsigned short, col);
     }
   };
 
@@ -514,17 +535,19 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   float l_run = 0.f;
   const float cscale = a.c;
 
-  // ---- prologue: tile 0 into stage 0 ----
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
+  // ---- prologue: tile 0 staged, tiles 1 and 2 in flight ----
+  load_kv(0, 0);
+  load_kv(1, 1);
+  store_kv(0, 0);
+  load_kv(0, 2);
   __syncthreads();
 
-  for (int j = 0; j < n_kt; ++j) {
+  // iteration j computes tile j from stage j&1, stages tile j+1 (register set
+  // (j+1)&1, fetched two iterations earlier) into stage (j+1)&1, which held
+  // tile j-1, and refills that register set with tile j+3
+  auto iter = [&](auto set_tag, int j) {
+    constexpr int nset = decltype(set_tag)::value;  // (j + 1) & 1
     const int st = j & 1;
-    load_k(j + 1);  // tiles past the workgroup's range read as zeros
-    load_v(j + 1);
     if (j < w_kt) {
       f32x16 s_cur[2];
       __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves compete
@@ -583,9 +606,13 @@ void fwd_mfma16_kernel(const FwdArgs a) {
       pv(st, pf);
       __builtin_amdgcn_s_setprio(0);
     }
-    store_k(st ^ 1);
-    store_v(st ^ 1);
+    store_kv(nset, st ^ 1);
+    load_kv(nset, j + 3);
     __syncthreads();
+  };
+  for (int j = 0; j < n_kt; j += 2) {
+    iter(std::integral_constant<int, 1>{}, j);
+    if (j + 1 < n_kt) iter(std::integral_constant<int, 0>{}, j + 1);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l) ----
@@ -613,16 +640,18 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
   void (*kern)(FwdArgs);
   if constexpr (sizeof(T) == 2) kern = fwd_mfma16_kernel<T, D, CAUSAL>;
   else kern = fwd_mfma_kernel<T, D, CAUSAL>;
+  constexpr int threads = sizeof(T) == 2 ? Cfg16<T, D>::NT : 256;
+  constexpr int lds_bytes = sizeof(T) == 2 ? Cfg16<T, D>::LDS_BYTES : C::LDS_BYTES;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
     attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   });
   if (attr_err != hipSuccess)
     return fa_set_error(FA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), C::LDS_BYTES, stream, args);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_bytes, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "launch: %s", hipGetErrorString(e));
   return FA_OK;
@@ -641,7 +670,7 @@ template <typename T> int launch_dtype(const FwdArgs &args, int d, bool causal, 
 int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream) {
   using namespace fa;
   const int es = fa_dtype_size(p->in_dtype);
-  const FwdArgs args = make_fwd_args(p, 128, es);
+  const FwdArgs args = make_fwd_args(p, es == 2 ? 256 : 128, es);  // query rows per workgroup
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (p->in_dtype) {
     case FA_F32: return launch_dtype<float>(args, p->d, p->causal != 0, s);
