@@ -4,9 +4,9 @@
 // "online softmax key state" boxes; panel 2, v1 card): K/V tiles are staged in
 // on-chip memory, and for every tile the scores, the online-softmax update and
 // the P V accumulation are done in registers, so the score matrix never reaches
-// HBM.  One workgroup owns 128 query rows of one (batch, head) — the v2 card's
-// partitioning of a single head across workgroups — and each of its four
-// wavefronts owns 32 rows end to end, so no reduction crosses wavefronts.
+// HBM.  A workgroup owns a block of query rows of one (batch, head) — the v2
+// card's partitioning of a single head across workgroups — and each wavefront
+// owns 32 rows end to end, so no reduction crosses wavefronts.
 //
 // MI355X design.
 //   * Scores are formed transposed, S^T = K Q^T, with 32x32 MFMA (K-depth 16 for
@@ -20,10 +20,13 @@
 //   * V is transposed in registers on its way to LDS, so every V^T operand is a
 //     single 16-byte LDS read; both tiles are padded by 16 bytes per row, which
 //     keeps 8-lane phases of 16-byte reads free of bank conflicts.
-//   * K/V tiles are double-buffered in LDS: tile j+1 is fetched from HBM into
-//     registers while tile j is computed, with one barrier per tile.
 //   * Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
-//     exponentiated with the hardware exp2.
+//     exponentiated with the hardware exp2; the running max moves lazily.
+//   * 16-bit kernel: 8 wavefronts over 256 rows, software-pipelined so that
+//     every wavefront has MFMA, vector and LDS work in flight at once: P V of
+//     tile t carries the first half of tile t+1's softmax between its MFMAs,
+//     and S^T of tile t+2 the second half; K/V staging rides along too, with
+//     one barrier per tile.
 //   * Causal tiles past a wavefront's last row are skipped; the mask is applied
 //     only on tiles that cross the diagonal or the end of the keys.  Workgroups
 //     are issued heaviest first and grouped so each XCD works on a contiguous
@@ -34,6 +37,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 namespace fa {
 
@@ -88,11 +92,11 @@ template <typename T, int D> struct Cfg {
 
 // Configuration of the 16-bit kernel: 8 wavefronts (two per SIMD) own 256 query
 // rows, so each K/V tile is fetched and staged once for twice as many rows.
-template <typename T, int D> struct Cfg16 {
+template <typename T, int D, int NT_> struct Cfg16 {
   static constexpr int ES = sizeof(T);
   static constexpr int KW = 8;
-  static constexpr int NT = 512;                // threads per workgroup
-  static constexpr int BR = 256;                // query rows per workgroup
+  static constexpr int NT = NT_;                // threads per workgroup
+  static constexpr int BR = NT / 2;             // query rows per workgroup (32 per wavefront)
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int EPC = 8;                 // elements per 16-byte chunk
   static constexpr int CH = D / EPC;            // chunks per row
@@ -377,11 +381,12 @@ void fwd_mfma_kernel(const FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Kernel for the 16-bit types.  Per K/V tile a wavefront computes S^T = K Q^T,
-// the online softmax and O^T += V^T P^T.  Global loads go through a buffer
-// resource placed at the tile's first row, so per-lane offsets are loop
-// constants and rows past the end of the keys (or tiles past the workgroup's
-// range) read as zero without any per-lane address arithmetic.  LDS fragments
-// are read a full 32-key block ahead of the MFMAs that consume them.
+// the online softmax and O^T += V^T P^T, software-pipelined over three tiles
+// (see the main loop).  Global loads go through a buffer resource placed at
+// the tile's first row, so per-lane offsets are loop constants and rows past
+// the end of the keys (or tiles past the workgroup's range) read as zero
+// without any per-lane address arithmetic.  LDS fragments are read four MFMAs
+// ahead of the MFMAs that consume them.
 // ---------------------------------------------------------------------------
 #ifndef FA16_WAVES_PER_EU
 #define FA16_WAVES_PER_EU 2
@@ -389,10 +394,21 @@ void fwd_mfma_kernel(const FwdArgs a) {
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, fully unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <typename T, int D, bool CAUSAL, int NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
 void fwd_mfma16_kernel(const FwdArgs a) {
-  using C = Cfg16<T, D>;
+  using C = Cfg16<T, D, NT>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
   constexpr int BC = C::BC, EPC = C::EPC, CH = C::CH, ES = C::ES;
@@ -413,18 +429,6 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   const int wrow0 = i0 + 32 * wave;
   const int row = wrow0 + l32;
 
-  // ---- Q rows into registers: lane half h holds d in [D/2*h, D/2*h + D/2) ----
-  frag qf[QS];
-  {
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
-    const bool ok = row < a.Sq;
-#pragma unroll
-    for (int c = 0; c < QS; ++c)
-      qf[c] = __builtin_bit_cast(frag, buf_load16(rq, ok ? row * a.q_ss + ((D / 2) * h + c * EPC) * ES : kOOB));
-    wait_vmem_all();
-  }
-
   const int coff = a.Sk - a.Sq;
   int n_kt = (a.Sk + BC - 1) / BC;
   int w_kt = n_kt;
@@ -438,10 +442,13 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   // ---- per-tile buffer resources, loop-constant lane offsets ----
   const char *kbase = reinterpret_cast<const char *>(static_cast<const T *>(a.k) + b * a.k_sb + hk * a.k_sh);
   const char *vbase = reinterpret_cast<const char *>(static_cast<const T *>(a.v) + b * a.v_sb + hk * a.v_sh);
+  // a tile at or past n_kt gets zero records (its loads return zeros); for a
+  // live tile the first row (j * BC <= Sk - 1) starts inside the slice, so the
+  // 32-bit shift cannot overflow and the records stay positive
   auto tile_rsrc = [&](const char *base, unsigned ss, unsigned ext, int j) {
-    const unsigned long long shift = static_cast<unsigned long long>(j) * BC * ss;
-    const unsigned recs = (j < n_kt && shift < ext) ? ext - static_cast<unsigned>(shift) : 0u;
-    return make_rsrc(base + shift, recs);
+    const bool live = j < n_kt;
+    const unsigned shift = live ? static_cast<unsigned>(j * BC) * ss : 0u;
+    return make_rsrc(base + shift, live ? ext - shift : 0u);
   };
   const int k_c = tid % CH, k_r = tid / CH;
   const int v_g = tid % C::NG, v_c = tid / C::NG;
@@ -451,21 +458,26 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     koff[p] = (k_r + (C::NT / CH) * p) * a.k_ss + k_c * 16;
     voff[p] = (v_g * C::KPT + p) * a.v_ss + v_c * 16;
   }
-  // two register sets: tile j is fetched two iterations before it is staged
   u32x4 kreg[2][C::PASSES], vreg[2][C::PASSES];
-  auto load_kv = [&](int set, int j) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
+  auto load_k_to = [&](u32x4 *dst, int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) kreg[set][p] = buf_load16(rk, koff[p]);
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) vreg[set][p] = buf_load16(rv, voff[p]);
+    for (int p = 0; p < C::PASSES; ++p) dst[p] = buf_load16(r, koff[p]);
   };
-  auto store_kv = [&](int set, int buf) {
+  auto load_k = [&](int set, int j) { load_k_to(kreg[set], j); };
+  auto load_v = [&](int set, int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) vreg[set][p] = buf_load16(r, voff[p]);
+  };
+  auto store_k_from = [&](const u32x4 *src, int buf) {
     T *ks = kbuf + buf * C::K_TILE;
 #pragma unroll
     for (int p = 0; p < C::PASSES; ++p)
-      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (C::NT / CH) * p) * C::KROW + k_c * EPC) = kreg[set][p];
+      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (C::NT / CH) * p) * C::KROW + k_c * EPC) = src[p];
+  };
+  auto store_k = [&](int set, int buf) { store_k_from(kreg[set], buf); };
+  auto store_v = [&](int set, int buf) {
     T *vt = vbuf + buf * C::V_TILE;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
@@ -482,144 +494,281 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
+  frag qf[QS];  // this lane's query row; lane half h holds d in [D/2*h, D/2*h + D/2)
 
-  // S^T = K Q^T from K buffer `buf`.  All 8 fragments of one 32-key block are
-  // read before its MFMAs, and the next block's reads are issued as the
-  // current block's fragments are consumed, so LDS latency hides behind MFMAs.
-  auto qk = [&](int buf, f32x16 s[2]) {
-    const T *kt = kbuf + buf * C::K_TILE + l32 * C::KROW + (D / 2) * h;
-    u32x4 kf[QS];
-#pragma unroll
-    for (int c = 0; c < QS; ++c) kf[c] = *reinterpret_cast<const u32x4 *>(kt + c * EPC);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < QS; ++c) {
-      s[0] = M::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s[0]);
-      kf[c] = *reinterpret_cast<const u32x4 *>(kt + 32 * C::KROW + c * EPC);
-    }
-#pragma unroll
-    for (int c = 0; c < QS; ++c) s[1] = M::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s[1]);
-    // keep the reads QS fragments ahead of the MFMAs that consume them
-    __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);
-#pragma unroll
-    for (int c = 0; c < QS; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);
+  // ---- blocks of the main loop: MFMAs with LDS operands read RA ahead, and
+  // softmax work of the neighbouring tile dealt out over the MFMA slots ----
+  constexpr int RA = 4;
+  constexpr int NQK = 2 * QS;     // MFMAs of S^T = K Q^T per tile
+  constexpr int NPV = 4 * C::DB;  // MFMAs of O^T += V^T P^T per tile
+  constexpr int STEPS = 16;       // steps of each softmax half
+  static_assert(STEPS % NQK == 0 && STEPS % NPV == 0, "softmax steps must split evenly over the MFMA slots");
+  const T *k_lane = kbuf + l32 * C::KROW + (D / 2) * h;
+  const T *v_lane = vbuf + l32 * C::VROW + 8 * h;
+  // MFMA i of S^T: key block i & 1, head-dim step i >> 1 (two independent chains)
+  auto kfrag = [&](int buf, int i) {
+    return *reinterpret_cast<const u32x4 *>(k_lane + buf * C::K_TILE + (i & 1) * 32 * C::KROW + (i >> 1) * EPC);
   };
-  // O^T += V^T P^T from V buffer `buf`, same read-ahead scheme
-  auto pv = [&](int buf, const frag pf[4]) {
-    const T *vt = vbuf + buf * C::V_TILE + l32 * C::VROW + 8 * h;
-    u32x4 vf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vf[i] = *reinterpret_cast<const u32x4 *>(vt + (i >> 2) * 32 * C::VROW + 16 * (i & 3));
-#pragma unroll
-    for (int i = 0; i < 4 * C::DB; ++i) {
-      const int db = i >> 2, tt = i & 3;
-      oacc[db] = M::mma(__builtin_bit_cast(frag, vf[i & 7]), pf[tt], oacc[db]);
-      if (i + 8 < 4 * C::DB)
-        vf[i & 7] = *reinterpret_cast<const u32x4 *>(vt + ((i + 8) >> 2) * 32 * C::VROW + 16 * ((i + 8) & 3));
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i + 8 < 4 * C::DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  // MFMA i of O^T: head-dim block i >> 2, key step i & 3
+  auto vfrag = [&](int buf, int i) {
+    return *reinterpret_cast<const u32x4 *>(v_lane + buf * C::V_TILE + (i >> 2) * 32 * C::VROW + 16 * (i & 3));
   };
 
+  // ---- online softmax state ----
   float m_run = neg_inf();
   float l_run = 0.f;
+  float alpha_p = 1.f;  // rescale factor of the tile last through the first half
+  bool move_p = false;  // whether it differs from 1 in this lane
+  float m_use = 0.f;    // the running max its exponents are taken against
   const float cscale = a.c;
 
-  // ---- prologue: tile 0 staged, tiles 1 and 2 in flight ----
-  load_kv(0, 0);
-  load_kv(1, 1);
-  store_kv(0, 0);
-  load_kv(0, 2);
+  // mask the keys of tile j past the end of the keys or the diagonal
+  auto mask = [&](f32x16 s[2], int j) {
+    const int j0 = j * BC;
+    const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
+    if (edge) {
+      const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_key<8>(mb, i, h) > lim) s[mb][i] = neg_inf();
+    }
+  };
+  // First half, in 16 steps: tile max (max3 tree, then the other lane half),
+  // lazy running-max update, exponents of s[0].
+  float ta[11], ua[4], mxa;
+  auto soft_a_step = [&](auto step_tag, f32x16 s[2]) {
+    constexpr int st = decltype(step_tag)::value;
+    auto sv = [&](int x) { return s[x >> 4][x & 15]; };
+    if constexpr (st < 3) {
+#pragma unroll
+      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
+      if constexpr (st == 2) ta[10] = fmaxf(sv(30), sv(31));
+    } else if constexpr (st == 3) {
+      ua[0] = max3f(ta[0], ta[1], ta[2]);
+      ua[1] = max3f(ta[3], ta[4], ta[5]);
+      ua[2] = max3f(ta[6], ta[7], ta[8]);
+      ua[3] = fmaxf(ta[9], ta[10]);
+    } else if constexpr (st == 4) {
+      mxa = max3f(ua[0], ua[1], fmaxf(ua[2], ua[3]));
+      mxa = fmaxf(mxa, swap_halves(mxa));
+    } else if constexpr (st == 5) {
+      mxa *= cscale;
+      // lazy running max: move only when the tile max exceeds it by the slack
+      move_p = mxa > m_run + kRescaleSlack;
+    } else if constexpr (st == 6) {
+      const float m_new = move_p ? mxa : m_run;
+      alpha_p = move_p ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+      m_run = m_new;
+      m_use = (m_run == neg_inf()) ? 0.f : m_run;
+    } else if constexpr (st < 15) {
+      constexpr int e = 2 * (st - 7);
+      s[0][e] = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
+      s[0][e + 1] = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+    }
+  };
+  // Second half, in 16 steps: exponents of s[1]; P^T rounded to 16 bits, two
+  // scores per word; row sum of the unrounded probabilities (the LSE must not
+  // carry the rounding of P) as a balanced tree; l update.
+  float ps[16], qa[8];
+  unsigned pw[16];
+  auto pack2 = [&](float x0, float x1) {
+    typedef T v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, v2{static_cast<T>(x0), static_cast<T>(x1)});
+  };
+  auto soft_b_step = [&](auto step_tag, f32x16 s[2]) {
+    constexpr int st = decltype(step_tag)::value;
+    if constexpr (st < 8) {
+      s[1][2 * st] = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
+      s[1][2 * st + 1] = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      pw[st] = pack2(s[0][2 * st], s[0][2 * st + 1]);
+    } else {
+      pw[st] = pack2(s[1][2 * (st - 8)], s[1][2 * (st - 8) + 1]);
+      if constexpr (st < 12) {
+        constexpr int mb = (st - 8) >> 1, base = 4 * ((st - 8) & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps[8 * mb + base + i] = s[mb][2 * (base + i)] + s[mb][2 * (base + i) + 1];
+      } else if constexpr (st < 14) {
+        constexpr int base = 4 * (st - 12);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qa[base + i] = ps[base + i] + ps[base + i + 8];
+      } else if constexpr (st == 14) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qa[i] += qa[i + 4];
+      } else {
+        l_run = __builtin_fmaf(l_run, alpha_p, (qa[0] + qa[2]) + (qa[1] + qa[3]));
+      }
+    }
+  };
+  auto p_pack = [&](f32x16 s[2]) {
+    s[0] = __builtin_bit_cast(f32x16, i32x16{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5],
+                                             (int)pw[6], (int)pw[7], (int)pw[8], (int)pw[9], (int)pw[10], (int)pw[11],
+                                             (int)pw[12], (int)pw[13], (int)pw[14], (int)pw[15]});
+  };
+  auto rescale_o = [&]() {
+    if (wave_any(move_p)) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha_p;
+    }
+  };
+
+  // S^T of K buffer `buf` into s; softmax work on `sn` rides along: none
+  // (SOFT = 0), its second half (1) or both halves (2)
+  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra) {
+    constexpr int SOFT = decltype(soft_tag)::value;
+    u32x4 kf[RA];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) kf[i] = kfrag(buf, i);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    static_for<NQK>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      s[i & 1] = M::mma(__builtin_bit_cast(frag, kf[i % RA]), qf[i >> 1], s[i & 1]);
+      if constexpr (i + RA < NQK) kf[i % RA] = kfrag(buf, i + RA);
+      if constexpr (SOFT == 1)
+        static_for<STEPS / NQK>([&](auto K) {
+          soft_b_step(std::integral_constant<int, i * (STEPS / NQK) + decltype(K)::value>{}, sn);
+        });
+      if constexpr (SOFT == 2)
+        static_for<2 * STEPS / NQK>([&](auto K) {
+          constexpr int st = i * (2 * STEPS / NQK) + decltype(K)::value;
+          if constexpr (st < STEPS) soft_a_step(std::integral_constant<int, st>{}, sn);
+          else soft_b_step(std::integral_constant<int, st - STEPS>{}, sn);
+        });
+      extra(I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (SOFT != 0) p_pack(sn);
+  };
+  // O^T += V^T P^T of V buffer `buf`, P^T in p[0]; the first softmax half of
+  // `sn` rides along
+  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra) {
+    frag pf[4];
+    pf[0] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 0, 1, 2, 3));
+    pf[1] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 4, 5, 6, 7));
+    pf[2] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 8, 9, 10, 11));
+    pf[3] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 12, 13, 14, 15));
+    u32x4 vf[RA];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) vf[i] = vfrag(buf, i);
+    static_for<NPV>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      oacc[i >> 2] = M::mma(__builtin_bit_cast(frag, vf[i % RA]), pf[i & 3], oacc[i >> 2]);
+      if constexpr (i + RA < NPV) vf[i % RA] = vfrag(buf, i + RA);
+      static_for<STEPS / NPV>([&](auto K) {
+        soft_a_step(std::integral_constant<int, i * (STEPS / NPV) + decltype(K)::value>{}, sn);
+      });
+      extra(I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Two score register sets: sc[j & 1] holds S^T of tile j from its QK^T
+  // until its softmax is done, then P^T (in its first half) until its P V.
+  f32x16 sc[2][2];
+
+  // ---- prologue: K of tiles 0-2 and V of tile 0 staged, tile 0 through its
+  // softmax, S^T of tile 1 formed, staging units 0 and 1 in flight.  The
+  // first tiles and the Q rows are fetched together, so the prologue waits
+  // on one memory round trip.  (K of tile 2 waits in the second V register
+  // set until tile 0's buffer is free.) ----
+  // unit u = (K of tile u+3, V of tile u+1), written to LDS in iteration u
+  auto load_unit = [&](int set, int u) {
+    load_k(set, u + 3);
+    load_v(set, u + 1);
+  };
+  load_k(0, 0);
+  load_k(1, 1);
+  load_v(0, 0);
+  load_k_to(vreg[1], 2);
+  // Q rows into registers
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
+    const bool ok = row < a.Sq;
+#pragma unroll
+    for (int c = 0; c < QS; ++c)
+      qf[c] = __builtin_bit_cast(frag, buf_load16(rq, ok ? row * a.q_ss + ((D / 2) * h + c * EPC) * ES : kOOB));
+  }
+  store_k(0, 0);
+  store_k(1, 1);
+  store_v(0, 0);
+  load_unit(0, 0);
+  __syncthreads();
+  if (0 < w_kt) {
+    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {});
+    mask(sc[0], 0);
+    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {});
+  }
+  __syncthreads();
+  store_k_from(vreg[1], 0);
+  load_unit(1, 1);
   __syncthreads();
 
-  // iteration j computes tile j from stage j&1, stages tile j+1 (register set
-  // (j+1)&1, fetched two iterations earlier) into stage (j+1)&1, which held
-  // tile j-1, and refills that register set with tile j+3
-  auto iter = [&](auto set_tag, int j) {
-    constexpr int nset = decltype(set_tag)::value;  // (j + 1) & 1
-    const int st = j & 1;
-    if (j < w_kt) {
-      f32x16 s_cur[2];
-      __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves compete
-      qk(st, s_cur);
-      __builtin_amdgcn_s_setprio(0);
-      const int j0 = j * BC;
-      // mask (tiles that cross the diagonal or the end of the keys)
-      const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
-      if (edge) {
-        const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (acc_key<8>(mb, i, h) > lim) s_cur[mb][i] = neg_inf();
-      }
-      // row max of the tile (max3 tree, then the other lane half)
-      float t[11];
-#pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
-        t[i] = max3f(s_cur[x >> 4][x & 15], s_cur[y >> 4][y & 15], s_cur[z >> 4][z & 15]);
-      }
-      t[10] = fmaxf(s_cur[1][14], s_cur[1][15]);
-      float mx = max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
-      mx = fmaxf(mx, swap_halves(mx)) * cscale;
-      // lazy running max: move only when the tile max exceeds it by the slack
-      const bool move = mx > m_run + kRescaleSlack;
-      const float m_new = move ? mx : m_run;
-      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
-      m_run = m_new;
-      if (wave_any(move)) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-      }
-      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-      frag pf[4];
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        unsigned w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(s_cur[tt >> 1][8 * (tt & 1) + 2 * e], cscale, -m_use));
-          const float p1 = fast_exp2(__builtin_fmaf(s_cur[tt >> 1][8 * (tt & 1) + 2 * e + 1], cscale, -m_use));
-          typedef T v2 __attribute__((ext_vector_type(2)));
-          w[e] = __builtin_bit_cast(unsigned, v2{static_cast<T>(p0), static_cast<T>(p1)});
-          // the row sum uses the unrounded probabilities: the LSE must not
-          // carry the rounding of P to 16 bits
-          ls[e] += p0 + p1;
-        }
-        pf[tt] = __builtin_bit_cast(frag, u32x4{w[0], w[1], w[2], w[3]});
-      }
-      l_run = __builtin_fmaf(l_run, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
-      __builtin_amdgcn_s_setprio(1);
-      pv(st, pf);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    store_kv(nset, st ^ 1);
-    load_kv(nset, j + 3);
+  // Main loop.  Iteration t, for a wave whose rows reach tile t:
+  //   O^T += V^T P^T of tile t, with the first half of tile t+1's softmax
+  //   dealt out between its MFMAs;
+  //   S^T of tile t+2, with the second half of tile t+1's softmax.
+  // Every wave thus keeps matrix, vector and LDS work in flight together, and
+  // the two waves of a SIMD fill each other's gaps.  The wave's share of unit
+  // t rides along too: K of tile t+3 goes into the K buffer of tile t+1 and V
+  // of tile t+1 into the V buffer of tile t-1, buffers no wave reads in this
+  // iteration; then the unit's registers are refilled.  One barrier per
+  // iteration publishes the unit.
+  auto iter = [&](auto set_tag, int t) {
+    constexpr int cur = decltype(set_tag)::value;  // t & 1
+    constexpr int nxt = cur ^ 1;
+    rescale_o();
+    mask(sc[nxt], t + 1);
+    block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
+      if constexpr (decltype(I)::value == 1) store_k(cur, nxt);
+      if constexpr (decltype(I)::value == 3) store_v(cur, nxt);
+    });
+    block_qk(cur, sc[cur], sc[nxt], std::integral_constant<int, 1>{}, [&](auto I) {
+      if constexpr (decltype(I)::value == 2) load_unit(cur, t + 2);
+    });
     __syncthreads();
   };
-  for (int j = 0; j < n_kt; j += 2) {
-    iter(std::integral_constant<int, 1>{}, j);
-    if (j + 1 < n_kt) iter(std::integral_constant<int, 0>{}, j + 1);
+  // iterations past the wave's last tile (causal): staging only
+  auto iter_stage = [&](auto set_tag, int t) {
+    constexpr int cur = decltype(set_tag)::value;
+    constexpr int nxt = cur ^ 1;
+    store_k(cur, nxt);
+    store_v(cur, nxt);
+    load_unit(cur, t + 2);
+    __syncthreads();
+  };
+  // two loops with a single path each (the register sets alternate, so both
+  // are unrolled by two and the second enters at the right parity)
+  int t = 0;
+  for (; t + 1 < w_kt; t += 2) {
+    iter(std::integral_constant<int, 0>{}, t);
+    iter(std::integral_constant<int, 1>{}, t + 1);
   }
+  if (t < w_kt) {
+    iter(std::integral_constant<int, 0>{}, t);
+    ++t;
+    if (t < n_kt) {
+      iter_stage(std::integral_constant<int, 1>{}, t);
+      ++t;
+    }
+  }
+  for (; t + 1 < n_kt; t += 2) {
+    iter_stage(std::integral_constant<int, 0>{}, t);
+    iter_stage(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (t < n_kt) iter_stage(std::integral_constant<int, 0>{}, t);
 
-  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l) ----
+  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l).  The LDS is
+  // free after the loop's last barrier: each wavefront transposes its 32 x D
+  // block through its own LDS slab, so that global stores write whole rows
+  // (16 lanes x 16 bytes per row) instead of 8-byte pieces of 32 rows. ----
   const float l_tot = l_run + swap_halves(l_run);
-  if (row < a.Sq) {
+  {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T *orow = static_cast<T *>(a.o) + b * a.o_sb + hq * a.o_sh + static_cast<long long>(row) * a.o_ss;
+    T *slab = kbuf + wave * 32 * C::KROW;  // 32 rows of KROW elements
+    static_assert(C::NT / 64 * 32 * C::KROW <= 2 * (C::K_TILE + C::V_TILE), "epilogue slabs must fit the LDS");
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -627,21 +776,35 @@ void fwd_mfma16_kernel(const FwdArgs a) {
         T out[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+        *reinterpret_cast<u32x2 *>(slab + l32 * C::KROW + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
       }
-    if (a.lse != nullptr && h == 0)
-      a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+    // the slab is private to the wavefront: LDS operations of one wavefront
+    // complete in order, so its reads below see its writes above
+    constexpr int RPI = 64 / CH;  // rows per store instruction
+    T *obase = static_cast<T *>(a.o) + b * a.o_sb + hq * a.o_sh;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = k * RPI + lane / CH, c = lane % CH;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * C::KROW + c * EPC);
+      const int orow_i = wrow0 + r;
+      if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + c * EPC) = v;
+    }
   }
+  if (row < a.Sq && a.lse != nullptr && h == 0)
+    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NT>
 int launch_one(const FwdArgs &args, hipStream_t stream) {
-  using C = Cfg<T, D>;
   void (*kern)(FwdArgs);
-  if constexpr (sizeof(T) == 2) kern = fwd_mfma16_kernel<T, D, CAUSAL>;
-  else kern = fwd_mfma_kernel<T, D, CAUSAL>;
-  constexpr int threads = sizeof(T) == 2 ? Cfg16<T, D>::NT : 256;
-  constexpr int lds_bytes = sizeof(T) == 2 ? Cfg16<T, D>::LDS_BYTES : C::LDS_BYTES;
+  int lds_bytes;
+  if constexpr (sizeof(T) == 2) {
+    kern = fwd_mfma16_kernel<T, D, CAUSAL, NT>;
+    lds_bytes = Cfg16<T, D, NT>::LDS_BYTES;
+  } else {
+    kern = fwd_mfma_kernel<T, D, CAUSAL>;
+    lds_bytes = Cfg<T, D>::LDS_BYTES;
+  }
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -651,18 +814,18 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
   if (attr_err != hipSuccess)
     return fa_set_error(FA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds_bytes, stream, args);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds_bytes, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "launch: %s", hipGetErrorString(e));
   return FA_OK;
 }
 
-template <typename T, int D> int launch_causal(const FwdArgs &args, bool causal, hipStream_t s) {
-  return causal ? launch_one<T, D, true>(args, s) : launch_one<T, D, false>(args, s);
+template <typename T, int D, int NT> int launch_causal(const FwdArgs &args, bool causal, hipStream_t s) {
+  return causal ? launch_one<T, D, true, NT>(args, s) : launch_one<T, D, false, NT>(args, s);
 }
 
-template <typename T> int launch_dtype(const FwdArgs &args, int d, bool causal, hipStream_t s) {
-  return d == 64 ? launch_causal<T, 64>(args, causal, s) : launch_causal<T, 128>(args, causal, s);
+template <typename T, int NT> int launch_dtype(const FwdArgs &args, int d, bool causal, hipStream_t s) {
+  return d == 64 ? launch_causal<T, 64, NT>(args, causal, s) : launch_causal<T, 128, NT>(args, causal, s);
 }
 
 }  // namespace fa
@@ -670,12 +833,13 @@ template <typename T> int launch_dtype(const FwdArgs &args, int d, bool causal, 
 int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream) {
   using namespace fa;
   const int es = fa_dtype_size(p->in_dtype);
-  const FwdArgs args = make_fwd_args(p, es == 2 ? 256 : 128, es);  // query rows per workgroup
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (es == 4) return launch_dtype<float, 256>(make_fwd_args(p, 128, es), p->d, p->causal != 0, s);
+  constexpr int NT = 512;
+  const FwdArgs args = make_fwd_args(p, NT / 2, es);  // 32 query rows per wavefront
   switch (p->in_dtype) {
-    case FA_F32: return launch_dtype<float>(args, p->d, p->causal != 0, s);
-    case FA_BF16: return launch_dtype<__bf16>(args, p->d, p->causal != 0, s);
-    case FA_F16: return launch_dtype<_Float16>(args, p->d, p->causal != 0, s);
+    case FA_BF16: return launch_dtype<__bf16, NT>(args, p->d, p->causal != 0, s);
+    case FA_F16: return launch_dtype<_Float16, NT>(args, p->d, p->causal != 0, s);
     default: return fa_set_error(FA_ERR_UNSUPPORTED, "dtype %d has no MFMA forward kernel", p->in_dtype);
   }
 }
