@@ -105,14 +105,22 @@ __device__ __forceinline__ int exp_of(float x) {
   return x > 0.f ? e : 0;
 }
 
-// Four fp16 scales of consecutive tokens starting at token t (a multiple of 4).
-__device__ __forceinline__ u32x2 load_scales4(__amdgpu_buffer_rsrc_t r, int t, bool vec) {
-  const unsigned off = static_cast<unsigned>(t) * 2u;
-  if (vec) return buf_load8(r, off);
+// Four fp16 scales at byte offset voff.  Offsets always go in the per-lane
+// operand, which the buffer range check covers (the scalar offset operand is
+// left at zero everywhere in this library).
+template <bool VEC> __device__ __forceinline__ u32x2 load_scales4_at(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  if constexpr (VEC) return buf_load8_nt(r, voff);
   unsigned short e[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * i, 0, 0);
+  for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2u * i, 0, kNonTemporal);
   return u32x2{e[0] | (static_cast<unsigned>(e[1]) << 16), e[2] | (static_cast<unsigned>(e[3]) << 16)};
+}
+
+// Four fp16 scales of consecutive tokens starting at token t (a multiple of 4).
+// VEC (rows 16-byte aligned) is a compile-time choice: a run-time one makes
+// the compiler issue both forms and select, waiting on the loads at once.
+template <bool VEC> __device__ __forceinline__ u32x2 load_scales4(__amdgpu_buffer_rsrc_t r, int t) {
+  return load_scales4_at<VEC>(r, static_cast<unsigned>(t) * 2u);
 }
 
 struct TileRegs {
@@ -122,13 +130,15 @@ struct TileRegs {
   u32x2 vs[2];     // 4 fp16 value scales per token block
 };
 
+template <bool SCVEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: range bounds and buffer resources stay scalar
   const int n = lane & 15;   // query column (S^T, O^T) or row within a 16-row block
   const int g = lane >> 4;   // lane group: reduction slots 8g..8g+7
 
@@ -146,12 +156,6 @@ void decode_split_kernel(const DecodeArgs a) {
   const int w1 = min(w0 + quarter, c1);
   const int ntiles = w1 > w0 ? (w1 - w0 + kTile - 1) / kTile : 0;
 
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(static_cast<const char *>(a.k) + b * a.kv_sb + kvh * a.kv_sh, a.kv_ext);
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(static_cast<const char *>(a.v) + b * a.kv_sb + kvh * a.kv_sh, a.kv_ext);
-  const __amdgpu_buffer_rsrc_t rks =
-      make_rsrc(static_cast<const _Float16 *>(a.ks) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
   const __amdgpu_buffer_rsrc_t rvs =
       make_rsrc(static_cast<const _Float16 *>(a.vs) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
 
@@ -189,8 +193,8 @@ void decode_split_kernel(const DecodeArgs a) {
     float vmax = 0.f;
     // w0 is a multiple of 32 tokens, so every 16-byte load is aligned
     for (int t = w0 + 8 * lane; t < w1; t += 8 * 64) {
-      const u32x2 lo = load_scales4(rvs, t, a.sc_vec != 0);
-      const u32x2 hi = load_scales4(rvs, t + 4, a.sc_vec != 0);
+      const u32x2 lo = load_scales4<SCVEC>(rvs, t);
+      const u32x2 hi = load_scales4<SCVEC>(rvs, t + 4);
       const f16x8 sv = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -202,27 +206,43 @@ void decode_split_kernel(const DecodeArgs a) {
   }
   const float wmul = ldexpf(1.f, fw);
 
-  // ---- tile loads ----
-  const bool sreal = n < G;
+  // ---- tile loads.  Each tile gets buffer resources based at its first token
+  // and ending at the wavefront's last token, so tokens past the range read
+  // as zero without per-lane checks, and every per-lane offset is a loop
+  // constant.  The scales depend on the lane group only, so lanes of padding
+  // query columns load the same, valid, values. ----
+  const char *kslice = static_cast<const char *>(a.k) + b * a.kv_sb + kvh * a.kv_sh;
+  const char *vslice = static_cast<const char *>(a.v) + b * a.kv_sb + kvh * a.kv_sh;
+  const char *ksslice = reinterpret_cast<const char *>(static_cast<const _Float16 *>(a.ks) + b * a.sc_sb + kvh * a.sc_sh);
+  const char *vsslice = reinterpret_cast<const char *>(static_cast<const _Float16 *>(a.vs) + b * a.sc_sb + kvh * a.sc_sh);
+  const unsigned ss = a.kv_ss;
+  unsigned k_off[2], v_off[8];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) k_off[tb] = (16u * tb + n) * ss + 32u * g;  // codes 32g .. 32g+31 of token 16tb+n
+#pragma unroll
+  for (int j = 0; j < 8; ++j)  // codes 8n .. 8n+7 of token 4g + (j & 3) + 16 (j >> 2)
+    v_off[j] = (4u * g + (j & 3) + 16u * (j >> 2)) * ss + 8u * n;
+  const unsigned s_off = 8u * g;  // scales of tokens 4g .. 4g+3 (+ 16 tb)
   auto load_tile = [&](TileRegs &r, int t0) {
+    const int left = w1 - t0;  // tokens of the range from t0 on
+    const unsigned kv_rec = left > 0 ? static_cast<unsigned>(left - 1) * ss + kD : 0u;
+    const unsigned sc_rec = left > 0 ? static_cast<unsigned>(left) * 2u : 0u;
+    const unsigned shift = left > 0 ? static_cast<unsigned>(t0) * ss : 0u;
+    const __amdgpu_buffer_rsrc_t tk = make_rsrc(kslice + shift, kv_rec);
+    const __amdgpu_buffer_rsrc_t tv = make_rsrc(vslice + shift, kv_rec);
+    const __amdgpu_buffer_rsrc_t tks = make_rsrc(ksslice + (left > 0 ? 2u * t0 : 0u), sc_rec);
+    const __amdgpu_buffer_rsrc_t tvs = make_rsrc(vsslice + (left > 0 ? 2u * t0 : 0u), sc_rec);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int tok = t0 + 16 * tb + n;
-      const unsigned off = tok < w1 ? static_cast<unsigned>(tok) * a.kv_ss + 32u * g : kOOB;
-      r.k[tb][0] = buf_load16(rk, off);
-      r.k[tb][1] = buf_load16(rk, off + 16u);
+      r.k[tb][0] = buf_load16_nt(tk, k_off[tb]);
+      r.k[tb][1] = buf_load16_nt(tk, k_off[tb] + 16u);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = t0 + 4 * g + (j & 3) + 16 * (j >> 2);
-      const unsigned off = tok < w1 ? static_cast<unsigned>(tok) * a.kv_ss + 8u * n : kOOB;
-      r.v[j] = buf_load8(rv, off);
-    }
+    for (int j = 0; j < 8; ++j) r.v[j] = buf_load8_nt(tv, v_off[j]);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int t = t0 + 16 * tb + 4 * g;
-      r.ks[tb] = sreal ? load_scales4(rks, t, a.sc_vec != 0) : u32x2{0, 0};
-      r.vs[tb] = sreal ? load_scales4(rvs, t, a.sc_vec != 0) : u32x2{0, 0};
+      r.ks[tb] = load_scales4_at<SCVEC>(tks, s_off + 32u * tb);
+      r.vs[tb] = load_scales4_at<SCVEC>(tvs, s_off + 32u * tb);
     }
   };
 
@@ -309,18 +329,24 @@ void decode_split_kernel(const DecodeArgs a) {
     }
   };
 
-  // ---- stream this wavefront's range, one tile of prefetch ----
+  // ---- stream this wavefront's range, two tiles of prefetch (a ring of
+  // three register tiles; loads past the range read zeros without touching
+  // memory, so the loop body issues them unconditionally) ----
   if (ntiles > 0) {
-    TileRegs ra, rb;
-    load_tile(ra, w0);
+    TileRegs r0, r1, r2;
+    load_tile(r0, w0);
+    load_tile(r1, w0 + kTile);
     int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-      load_tile(rb, w0 + (t + 1) * kTile);
-      compute_tile(ra, w0 + t * kTile);
-      if (t + 2 < ntiles) load_tile(ra, w0 + (t + 2) * kTile);
-      compute_tile(rb, w0 + (t + 1) * kTile);
+    for (; t + 2 < ntiles; t += 3) {
+      load_tile(r2, w0 + (t + 2) * kTile);
+      compute_tile(r0, w0 + t * kTile);
+      load_tile(r0, w0 + (t + 3) * kTile);
+      compute_tile(r1, w0 + (t + 1) * kTile);
+      load_tile(r1, w0 + (t + 4) * kTile);
+      compute_tile(r2, w0 + (t + 2) * kTile);
     }
-    if (t < ntiles) compute_tile(ra, w0 + t * kTile);
+    if (t < ntiles) compute_tile(r0, w0 + t * kTile);
+    if (t + 1 < ntiles) compute_tile(r1, w0 + (t + 1) * kTile);
   }
 
   // ---- wavefront partial: O_w = O_acc / (l 2^fw), lse2_w = m + log2 l ----
@@ -446,7 +472,8 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
                                      ((rows * kD * sizeof(float) + 255) & ~size_t(255)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
+  if (a.sc_vec) hipLaunchKernelGGL(decode_split_kernel<true>, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
+  else hipLaunchKernelGGL(decode_split_kernel<false>, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode split launch: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(p->B) * p->Hq), dim3(kD), 0, s, a);

@@ -42,6 +42,16 @@ __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// Streaming loads (cache policy "nt", non-temporal) for data read exactly
+// once, such as a KV cache during decode.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ u32x2 buf_load8_nt(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
+}
+
 // Value held by lane (lane ^ 32): the other half of the wavefront.  One
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second; with x in both, the first result holds x's lower
