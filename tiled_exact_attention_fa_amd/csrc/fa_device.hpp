@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -15,6 +18,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // A byte offset that is always past the end of a buffer resource: validation
 // keeps every (batch, head) slice below 2^31 bytes, so loads at this offset
@@ -76,6 +80,17 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 // True if pred holds in any lane of the wavefront (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, fully unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Sum / max of 16 floats as a balanced tree (short dependency chains).
 __device__ __forceinline__ float tree_sum16(const float *x) {

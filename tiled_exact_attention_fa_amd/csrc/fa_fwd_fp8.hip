@@ -18,8 +18,13 @@
 //     that small probabilities stay normal numbers; the factor is removed with
 //     the row sum in the epilogue.  The row sum itself uses the unrounded fp32
 //     probabilities.
-//   * V is transposed in registers (4 keys x 8 columns per thread, byte
+//   * V is transposed in registers (4 keys x 4 columns per thread, byte
 //     permutes) on its way into a double-buffered LDS stage.
+//   * At twice the bf16 matrix rate the softmax is as long as the products, so
+//     the loop is software-pipelined like the 16-bit kernel: 8 wavefronts over
+//     256 rows; P V of tile t carries the first half of tile t+1's softmax
+//     between its MFMAs and S^T of tile t+2 the second half, with the K/V
+//     staging riding along and one barrier per tile.
 #include "fa_device.hpp"
 #include "fa_fwd_common.hpp"
 #include "fa_internal.h"
@@ -30,22 +35,24 @@ namespace fa {
 
 namespace f8 {
 
-constexpr int BR = 128;   // query rows per workgroup (4 wavefronts x 32)
+constexpr int NT = 512;   // threads per workgroup
+constexpr int BR = 256;   // query rows per workgroup (8 wavefronts x 32)
 constexpr int BC = 64;    // keys per tile: one 64-deep MFMA for P V
 constexpr int D = 128;
 constexpr int KROW = D + 16;   // bytes per K row in LDS
 constexpr int VROW = BC + 16;  // bytes per V^T row in LDS
 constexpr int K_TILE = BC * KROW;
 constexpr int V_TILE = D * VROW;
-constexpr int STAGE = K_TILE + V_TILE;
-constexpr int LDS_BYTES = 2 * STAGE;
+constexpr int ORow = D + 8;    // bf16 elements per row of the epilogue slab
+constexpr int STAGES_BYTES = 2 * (K_TILE + V_TILE);
+constexpr int SLAB_BYTES = NT / 64 * 32 * ORow * 2;
+constexpr int LDS_BYTES = STAGES_BYTES > SLAB_BYTES ? STAGES_BYTES : SLAB_BYTES;
 // P is multiplied by kPScale before rounding to e4m3 (max 448).  With the
 // lazy running max, P itself can reach 2^kSlack8, so kPScale * 2^kSlack8 = 256
 // keeps every scaled probability at or below 256, and probabilities down to
 // 2^-10 of the running max stay normal e4m3 numbers.
 constexpr float kSlack8 = 4.0f;
-constexpr float kPScale = 16.f;
-constexpr float kLog2PScale = 4.f;
+constexpr float kLog2PScale = 4.f;  // kPScale = 16
 
 // LDS row of key kr of a tile: block mb = (kr >> 4) & 1, half h = kr >> 5,
 // register i = kr & 15 of that block's accumulator, whose C row is
@@ -60,13 +67,19 @@ __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+__device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 }  // namespace f8
 
 template <bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(f8::NT, f8::NT), amdgpu_waves_per_eu(2)))
 void fwd_fp8_kernel(const FwdArgs a) {
   using namespace f8;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  unsigned char *kbuf = lds;                 // [2][BC][KROW]
+  unsigned char *vbuf = lds + 2 * K_TILE;    // [2][D][VROW]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -79,23 +92,6 @@ void fwd_fp8_kernel(const FwdArgs a) {
   const int wrow0 = i0 + 32 * wave;
   const int row = wrow0 + l32;
 
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(static_cast<const unsigned char *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
-
-  // Q: lane half h holds bytes [64h, 64h + 64) of its row; step s uses 32 of them
-  i32x8 qf[2];
-  {
-    const bool ok = row < a.Sq;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const unsigned base = ok ? row * a.q_ss + 64u * h + 32u * s : kOOB;
-      const u32x4 lo = buf_load16(rq, base);
-      const u32x4 hi = buf_load16(rq, ok ? base + 16u : kOOB);
-      qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    wait_vmem_all();
-  }
-
   const int coff = a.Sk - a.Sq;
   int n_kt = (a.Sk + BC - 1) / BC;
   int w_kt = n_kt;
@@ -106,91 +102,86 @@ void fwd_fp8_kernel(const FwdArgs a) {
     w_kt = min(n_kt, last_w < 0 ? 0 : last_w / BC + 1);
   }
 
-  // K: thread t loads rows t/8 and t/8 + 32, 16-byte chunk t%8.
-  // V: thread t loads keys 4*(t%16) .. +3 of the 8-byte column chunk t/16.
+  // ---- staging: K, thread t loads row t/8, 16-byte chunk t%8; V, thread t
+  // loads columns 4*(t/16) .. +3 of keys 4*(t%16) .. +3 (one word per key).
   // Loads go through a buffer resource placed at the tile's first row, so the
-  // lane offsets are loop constants and rows past the keys read as zero.
-  u32x4 kreg[2];
-  u32x2 vreg[4];
+  // lane offsets are loop constants and rows past the keys read as zero. ----
   const int k_c = tid & 7, k_r = tid >> 3;
   const int v_g = tid & 15, v_c = tid >> 4;
   const unsigned char *kbase = static_cast<const unsigned char *>(a.k) + b * a.k_sb + hk * a.k_sh;
   const unsigned char *vbase = static_cast<const unsigned char *>(a.v) + b * a.v_sb + hk * a.v_sh;
+  // a tile at or past n_kt gets zero records; for a live tile the first row
+  // (j * BC <= Sk - 1) starts inside the slice, so the 32-bit shift cannot
+  // overflow and the records stay positive
   auto tile_rsrc = [&](const unsigned char *base, unsigned ss, unsigned ext, int j) {
-    const unsigned long long shift = static_cast<unsigned long long>(j) * BC * ss;
-    const unsigned recs = (j < n_kt && shift < ext) ? ext - static_cast<unsigned>(shift) : 0u;
-    return make_rsrc(base + shift, recs);
+    const bool live = j < n_kt;
+    const unsigned shift = live ? static_cast<unsigned>(j * BC) * ss : 0u;
+    return make_rsrc(base + shift, live ? ext - shift : 0u);
   };
-  unsigned koff[2], voff[4];
+  const unsigned koff = k_r * a.k_ss + 16u * k_c;
+  unsigned voff[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) koff[p] = (k_r + 32 * p) * a.k_ss + 16u * k_c;
+  for (int p = 0; p < 4; ++p) voff[p] = (4 * v_g + p) * a.v_ss + 4u * v_c;
+  u32x4 kreg[2];
+  unsigned vreg[2][4];
+  auto load_k_to = [&](u32x4 &dst, int j) { dst = buf_load16(tile_rsrc(kbase, a.k_ss, a.k_ext, j), koff); };
+  auto load_v = [&](int set, int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) voff[p] = (4 * v_g + p) * a.v_ss + 8u * v_c;
-  auto load_tile = [&](int j) {
-    const __amdgpu_buffer_rsrc_t rkj = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
-    const __amdgpu_buffer_rsrc_t rvj = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) kreg[p] = buf_load16(rkj, koff[p]);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) vreg[p] = buf_load8(rvj, voff[p]);
+    for (int p = 0; p < 4; ++p) vreg[set][p] = buf_load4(r, voff[p]);
   };
-  auto store_tile = [&](int st) {
-    unsigned char *ks = lds + st * STAGE;
-    unsigned char *vt = ks + K_TILE;
+  auto store_k_from = [&](const u32x4 &src, int buf) {
+    *reinterpret_cast<u32x4 *>(kbuf + buf * K_TILE + k_lds_row(k_r) * KROW + 16 * k_c) = src;
+  };
+  // 4 keys x 4 columns -> 4 columns x 4 keys
+  auto store_v = [&](int set, int buf) {
+    const unsigned *r = vreg[set];
+    const unsigned x01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // k0c0 k1c0 k0c1 k1c1
+    const unsigned x23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const unsigned y01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // k0c2 k1c2 k0c3 k1c3
+    const unsigned y23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    unsigned col[4];
+    col[0] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+    col[1] = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+    col[2] = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
+    col[3] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
+    unsigned char *vt = vbuf + buf * V_TILE;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *reinterpret_cast<u32x4 *>(ks + k_lds_row(k_r + 32 * p) * KROW + 16 * k_c) = kreg[p];
-    // 4 keys x 8 columns -> 8 columns x 4 keys
-#pragma unroll
-    for (int hd = 0; hd < 2; ++hd) {
-      const unsigned x01 = __builtin_amdgcn_perm(vreg[1][hd], vreg[0][hd], 0x05010400u);  // k0c0 k1c0 k0c1 k1c1
-      const unsigned x23 = __builtin_amdgcn_perm(vreg[3][hd], vreg[2][hd], 0x05010400u);
-      const unsigned y01 = __builtin_amdgcn_perm(vreg[1][hd], vreg[0][hd], 0x07030602u);  // k0c2 k1c2 k0c3 k1c3
-      const unsigned y23 = __builtin_amdgcn_perm(vreg[3][hd], vreg[2][hd], 0x07030602u);
-      unsigned col[4];
-      col[0] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
-      col[1] = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
-      col[2] = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
-      col[3] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<unsigned *>(vt + (8 * v_c + 4 * hd + e) * VROW + 4 * v_g) = col[e];
-    }
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned *>(vt + (4 * v_c + e) * VROW + 4 * v_g) = col[e];
   };
 
-  float m_run = neg_inf();
-  float l_run = 0.f;
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  i32x8 qf[2];  // lane half h holds bytes [64h, 64h + 64) of its row; step s uses 32 of them
+
+  // ---- blocks: 4 MFMAs each, operands read two MFMAs (four 16-byte reads)
+  // ahead, softmax steps of the neighbouring tile dealt out over the slots ----
+  constexpr int NM = 4;
+  constexpr int RA = 2;
+  constexpr int STEPS = 16;
+  const unsigned char *k_lane = kbuf + l32 * KROW + 64 * h;
+  const unsigned char *v_lane = vbuf + l32 * VROW + 32 * h;
+  // MFMA i of S^T: key block i & 1, depth step i >> 1
+  auto kfrag = [&](int buf, int i, int half) {
+    return *reinterpret_cast<const u32x4 *>(k_lane + buf * K_TILE + (i & 1) * 32 * KROW + 32 * (i >> 1) + 16 * half);
+  };
+  // MFMA i of O^T: head-dim block i
+  auto vfrag = [&](int buf, int i, int half) {
+    return *reinterpret_cast<const u32x4 *>(v_lane + buf * V_TILE + i * 32 * VROW + 16 * half);
+  };
+
+  // ---- online softmax state ----
+  float m_run = neg_inf();
+  float l_run = 0.f;
+  float alpha_p = 1.f;
+  bool move_p = false;
+  float m_use = 0.f;  // running max minus log2 kPScale
   const float cscale = a.c;
 
-  auto compute_tile = [&](int st, int j) {
-    const unsigned char *ks = lds + st * STAGE;
-    const unsigned char *vt = ks + K_TILE;
+  // accumulator (block mb, register i, half h) is key 32h + 16mb + i
+  auto mask = [&](f32x16 s[2], int j) {
     const int j0 = j * BC;
-    f32x16 sacc[2];
-    u32x4 kr[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        kr[mb][q] = *reinterpret_cast<const u32x4 *>(ks + (32 * mb + l32) * KROW + 64 * h + 16 * q);
-    __builtin_amdgcn_s_setprio(1);  // matrix phase first when two waves compete
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 lo = kr[mb][2 * s], hi = kr[mb][2 * s + 1];
-        const i32x8 kf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sacc[mb] = mma(kf, qf[s], sacc[mb]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // accumulator (block mb, register i, half h) is key 32h + 16mb + i
     const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
     if (edge) {
       const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
@@ -198,78 +189,240 @@ void fwd_fp8_kernel(const FwdArgs a) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * h + 16 * mb + i > lim) sacc[mb][i] = neg_inf();
+          if (32 * h + 16 * mb + i > lim) s[mb][i] = neg_inf();
     }
-    // lazy running max as in the 16-bit kernel, with the smaller slack kSlack8
-    float mxv[16];
+  };
+  // first half: tile max, lazy running-max update, exponents of s[0]
+  float ta[11], ua[4], mxa;
+  auto soft_a_step = [&](auto step_tag, f32x16 s[2]) {
+    constexpr int st = decltype(step_tag)::value;
+    auto sv = [&](int x) { return s[x >> 4][x & 15]; };
+    if constexpr (st < 3) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mxv[i] = fmaxf(sacc[0][i], sacc[1][i]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 8]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mxv[i] = fmaxf(mxv[i], mxv[i + 4]);
-    float mx = fmaxf(fmaxf(mxv[0], mxv[1]), fmaxf(mxv[2], mxv[3]));
-    mx = fmaxf(mx, swap_halves(mx)) * cscale;
-    const bool move = mx > m_run + kSlack8;
-    if (wave_any(move)) {
-      const float m_new = move ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
+      if constexpr (st == 2) ta[10] = fmaxf(sv(30), sv(31));
+    } else if constexpr (st == 3) {
+      ua[0] = max3f(ta[0], ta[1], ta[2]);
+      ua[1] = max3f(ta[3], ta[4], ta[5]);
+      ua[2] = max3f(ta[6], ta[7], ta[8]);
+      ua[3] = fmaxf(ta[9], ta[10]);
+    } else if constexpr (st == 4) {
+      mxa = max3f(ua[0], ua[1], fmaxf(ua[2], ua[3]));
+      mxa = fmaxf(mxa, swap_halves(mxa));
+    } else if constexpr (st == 5) {
+      mxa *= cscale;
+      move_p = mxa > m_run + kSlack8;
+    } else if constexpr (st == 6) {
+      const float m_new = move_p ? mxa : m_run;
+      alpha_p = move_p ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
       m_run = m_new;
+      // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
+      m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale;
+    } else if constexpr (st < 15) {
+      constexpr int e = 2 * (st - 7);
+      s[0][e] = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
+      s[0][e + 1] = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
     }
-    // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
-    const float m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale;
-    int pw[8];
-    float ps[16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sacc[mb][i + e], cscale, -m_use));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ps[i + e] = mb == 0 ? p[e] : ps[i + e] + p[e];
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-        pw[4 * mb + i / 4] = w;
+  };
+  // second half: exponents of s[1]; P^T packed to e4m3, four keys per word;
+  // row sum of the unrounded probabilities as a balanced tree; l update
+  float ps[16], qa[8];
+  int pw[8];
+  auto soft_b_step = [&](auto step_tag, f32x16 s[2]) {
+    constexpr int st = decltype(step_tag)::value;
+    if constexpr (st < 8) {
+      s[1][2 * st] = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
+      s[1][2 * st + 1] = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      if constexpr (st < 4) {
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st], s[0][4 * st + 1], 0, false);
+        pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st + 2], s[0][4 * st + 3], w, true);
       }
-    l_run += tree_sum16(ps);
-    const i32x8 pf{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    u32x4 vr[4][2];
+    } else {
+      if constexpr (st < 12) {
+        constexpr int q = st - 8;
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], 0, false);
+        pw[4 + q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q + 2], s[1][4 * q + 3], w, true);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int i = 4 * q; i < 4 * q + 4; ++i) ps[i] = s[0][i] + s[1][i];
+      } else if constexpr (st < 14) {
+        constexpr int base = 4 * (st - 12);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) vr[db][q] = *reinterpret_cast<const u32x4 *>(vt + (32 * db + l32) * VROW + 32 * h + 16 * q);
-    __builtin_amdgcn_s_setprio(1);
+        for (int i = 0; i < 4; ++i) qa[base + i] = ps[base + i] + ps[base + i + 8];
+      } else if constexpr (st == 14) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const u32x4 lo = vr[db][0], hi = vr[db][1];
-      const i32x8 vf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      oacc[db] = mma(vf, pf, oacc[db]);
+        for (int i = 0; i < 4; ++i) qa[i] += qa[i + 4];
+      } else {
+        l_run = __builtin_fmaf(l_run, alpha_p, (qa[0] + qa[2]) + (qa[1] + qa[3]));
+      }
     }
-    __builtin_amdgcn_s_setprio(0);
+  };
+  auto p_pack = [&](f32x16 s[2]) {
+    s[0] = __builtin_bit_cast(f32x16, i32x16{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7],
+                                             0, 0, 0, 0, 0, 0, 0, 0});
+  };
+  auto rescale_o = [&]() {
+    if (wave_any(move_p)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha_p;
+    }
   };
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
+  // S^T of K buffer `buf` into s; softmax work on `sn` rides along: none
+  // (SOFT = 0), its second half (1) or both halves (2)
+  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra) {
+    constexpr int SOFT = decltype(soft_tag)::value;
+    u32x4 kf[RA][2];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      kf[i][0] = kfrag(buf, i, 0);
+      kf[i][1] = kfrag(buf, i, 1);
+    }
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      s[i & 1] = mma(join(kf[i % RA][0], kf[i % RA][1]), qf[i >> 1], s[i & 1]);
+      if constexpr (i + RA < NM) {
+        kf[i % RA][0] = kfrag(buf, i + RA, 0);
+        kf[i % RA][1] = kfrag(buf, i + RA, 1);
+      }
+      if constexpr (SOFT == 1)
+        static_for<STEPS / NM>([&](auto K) {
+          soft_b_step(std::integral_constant<int, i * (STEPS / NM) + decltype(K)::value>{}, sn);
+        });
+      if constexpr (SOFT == 2)
+        static_for<2 * STEPS / NM>([&](auto K) {
+          constexpr int st = i * (2 * STEPS / NM) + decltype(K)::value;
+          if constexpr (st < STEPS) soft_a_step(std::integral_constant<int, st>{}, sn);
+          else soft_b_step(std::integral_constant<int, st - STEPS>{}, sn);
+        });
+      extra(I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (SOFT != 0) p_pack(sn);
+  };
+  // O^T += V^T P^T of V buffer `buf`, P^T in the first 8 words of p; the first
+  // softmax half of `sn` rides along
+  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra) {
+    const i32x16 pi = __builtin_bit_cast(i32x16, p);
+    const i32x8 pf = __builtin_shufflevector(pi, pi, 0, 1, 2, 3, 4, 5, 6, 7);
+    u32x4 vf[RA][2];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      vf[i][0] = vfrag(buf, i, 0);
+      vf[i][1] = vfrag(buf, i, 1);
+    }
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      oacc[i] = mma(join(vf[i % RA][0], vf[i % RA][1]), pf, oacc[i]);
+      if constexpr (i + RA < NM) {
+        vf[i % RA][0] = vfrag(buf, i + RA, 0);
+        vf[i % RA][1] = vfrag(buf, i + RA, 1);
+      }
+      static_for<STEPS / NM>([&](auto K) {
+        soft_a_step(std::integral_constant<int, i * (STEPS / NM) + decltype(K)::value>{}, sn);
+      });
+      extra(I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Two score register sets: sc[j & 1] holds S^T of tile j from its QK^T
+  // until its softmax is done, then P^T (in its first 8 words) until its P V.
+  f32x16 sc[2][2];
+
+  // ---- prologue: K of tiles 0-2 and V of tile 0 staged, tile 0 through its
+  // softmax, S^T of tile 1 formed, staging units 0 and 1 in flight; the first
+  // tiles and the Q rows are fetched together ----
+  // unit u = (K of tile u+3, V of tile u+1), written to LDS in iteration u
+  auto load_unit = [&](int set, int u) {
+    load_k_to(kreg[set], u + 3);
+    load_v(set, u + 1);
+  };
+  u32x4 k0, k1, k2;
+  load_k_to(k0, 0);
+  load_k_to(k1, 1);
+  load_v(0, 0);
+  load_k_to(k2, 2);
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const unsigned char *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
+    const bool ok = row < a.Sq;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const unsigned base = ok ? row * a.q_ss + 64u * h + 32u * s : kOOB;
+      qf[s] = join(buf_load16(rq, base), buf_load16(rq, ok ? base + 16u : kOOB));
+    }
+  }
+  store_k_from(k0, 0);
+  store_k_from(k1, 1);
+  store_v(0, 0);
+  load_unit(0, 0);
+  __syncthreads();
+  if (0 < w_kt) {
+    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {});
+    mask(sc[0], 0);
+    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {});
   }
   __syncthreads();
-  for (int j = 0; j < n_kt; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-    if (j < w_kt) compute_tile(st, j);
-    if (j + 1 < n_kt) store_tile(st ^ 1);
-    __syncthreads();
-  }
+  store_k_from(k2, 0);
+  load_unit(1, 1);
+  __syncthreads();
 
+  // Main loop, as in the 16-bit kernel: iteration t runs P V of tile t with
+  // the first softmax half of tile t+1, then S^T of tile t+2 with the second
+  // half; the wave's share of unit t (K of tile t+3 into the K buffer of tile
+  // t+1, V of tile t+1 into the V buffer of tile t-1, neither read in this
+  // iteration) rides along, and one barrier per iteration publishes it.
+  auto iter = [&](auto set_tag, int t) {
+    constexpr int cur = decltype(set_tag)::value;  // t & 1
+    constexpr int nxt = cur ^ 1;
+    rescale_o();
+    mask(sc[nxt], t + 1);
+    block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
+      if constexpr (decltype(I)::value == 1) store_k_from(kreg[cur], nxt);
+      if constexpr (decltype(I)::value == 2) store_v(cur, nxt);
+    });
+    block_qk(cur, sc[cur], sc[nxt], std::integral_constant<int, 1>{}, [&](auto I) {
+      if constexpr (decltype(I)::value == 1) load_unit(cur, t + 2);
+    });
+    __syncthreads();
+  };
+  // iterations past the wave's last tile (causal): staging only
+  auto iter_stage = [&](auto set_tag, int t) {
+    constexpr int cur = decltype(set_tag)::value;
+    constexpr int nxt = cur ^ 1;
+    store_k_from(kreg[cur], nxt);
+    store_v(cur, nxt);
+    load_unit(cur, t + 2);
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < w_kt; t += 2) {
+    iter(std::integral_constant<int, 0>{}, t);
+    iter(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (t < w_kt) {
+    iter(std::integral_constant<int, 0>{}, t);
+    ++t;
+    if (t < n_kt) {
+      iter_stage(std::integral_constant<int, 1>{}, t);
+      ++t;
+    }
+  }
+  for (; t + 1 < n_kt; t += 2) {
+    iter_stage(std::integral_constant<int, 0>{}, t);
+    iter_stage(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (t < n_kt) iter_stage(std::integral_constant<int, 0>{}, t);
+
+  // ---- epilogue: O = o_mul * O_acc / l (l carries kPScale, which cancels),
+  // transposed through LDS (free after the loop's last barrier) so that each
+  // store writes whole rows ----
   const float l_tot = l_run + swap_halves(l_run);
-  if (row < a.Sq) {
-    const float inv = l_tot > 0.f ? a.o_mul / l_tot : 0.f;  // l_tot = kPScale * l: the factor cancels
-    __bf16 *orow = static_cast<__bf16 *>(a.o) + b * a.o_sb + hq * a.o_sh + static_cast<long long>(row) * a.o_ss;
+  {
+    const float inv = l_tot > 0.f ? a.o_mul / l_tot : 0.f;
+    __bf16 *slab = reinterpret_cast<__bf16 *>(lds) + wave * 32 * ORow;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -277,17 +430,25 @@ void fwd_fp8_kernel(const FwdArgs a) {
         bf16x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+        *reinterpret_cast<u32x2 *>(slab + l32 * ORow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
       }
-    if (a.lse != nullptr && h == 0)
-      a.lse[b * a.lse_sb + hq * a.lse_sh + row] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PScale) * kLn2 : neg_inf();
+    // the slab is private to the wavefront, whose LDS operations complete in order
+    __bf16 *obase = static_cast<__bf16 *>(a.o) + b * a.o_sb + hq * a.o_sh;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + lane / 16, c = lane % 16;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * ORow + 8 * c);
+      const int orow_i = wrow0 + r;
+      if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + 8 * c) = v;
+    }
   }
+  if (row < a.Sq && a.lse != nullptr && h == 0)
+    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PScale) * kLn2 : neg_inf();
 }
 
 template <bool CAUSAL> int launch_fp8(const FwdArgs &args, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
-  hipLaunchKernelGGL(fwd_fp8_kernel<CAUSAL>, dim3(grid), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL(fwd_fp8_kernel<CAUSAL>, dim3(grid), dim3(f8::NT), 0, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "fp8 launch: %s", hipGetErrorString(e));
   return FA_OK;

@@ -392,18 +392,6 @@ void fwd_mfma_kernel(const FwdArgs a) {
 #define FA16_WAVES_PER_EU 2
 #endif
 
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-
-// f(integral_constant<int, I>) for I = 0 .. N-1, fully unrolled at compile time
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <typename T, int D, bool CAUSAL, int NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
