@@ -83,6 +83,12 @@ __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ba
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// Marks x as produced at this point of the program: the empty volatile asm
+// keeps the compiler from sinking the computation of x past it (for
+// instance into a later loop iteration), so work dealt out between MFMAs
+// stays where it was placed.  No instruction is emitted.
+template <typename V> __device__ __forceinline__ void pin(V &x) { asm volatile("" : "+v"(x)); }
+
 // f(integral_constant<int, I>) for I = 0 .. N-1, fully unrolled at compile time
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {

@@ -199,16 +199,25 @@ void fwd_fp8_kernel(const FwdArgs a) {
     auto sv = [&](int x) { return s[x >> 4][x & 15]; };
     if constexpr (st < 3) {
 #pragma unroll
-      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
-      if constexpr (st == 2) ta[10] = fmaxf(sv(30), sv(31));
+      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) {
+        ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
+        pin(ta[i]);
+      }
+      if constexpr (st == 2) {
+        ta[10] = fmaxf(sv(30), sv(31));
+        pin(ta[10]);
+      }
     } else if constexpr (st == 3) {
       ua[0] = max3f(ta[0], ta[1], ta[2]);
       ua[1] = max3f(ta[3], ta[4], ta[5]);
       ua[2] = max3f(ta[6], ta[7], ta[8]);
       ua[3] = fmaxf(ta[9], ta[10]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pin(ua[i]);
     } else if constexpr (st == 4) {
       mxa = max3f(ua[0], ua[1], fmaxf(ua[2], ua[3]));
       mxa = fmaxf(mxa, swap_halves(mxa));
+      pin(mxa);
     } else if constexpr (st == 5) {
       mxa *= cscale;
       move_p = mxa > m_run + kSlack8;
@@ -218,10 +227,16 @@ void fwd_fp8_kernel(const FwdArgs a) {
       m_run = m_new;
       // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
       m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale;
+      pin(alpha_p);
+      pin(m_use);
     } else if constexpr (st < 15) {
       constexpr int e = 2 * (st - 7);
-      s[0][e] = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
-      s[0][e + 1] = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+      float p0 = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
+      float p1 = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+      pin(p0);
+      pin(p1);
+      s[0][e] = p0;
+      s[0][e + 1] = p1;
     }
   };
   // second half: exponents of s[1]; P^T packed to e4m3, four keys per word;
@@ -231,28 +246,44 @@ void fwd_fp8_kernel(const FwdArgs a) {
   auto soft_b_step = [&](auto step_tag, f32x16 s[2]) {
     constexpr int st = decltype(step_tag)::value;
     if constexpr (st < 8) {
-      s[1][2 * st] = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
-      s[1][2 * st + 1] = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      float p0 = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
+      float p1 = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      pin(p0);
+      pin(p1);
+      s[1][2 * st] = p0;
+      s[1][2 * st + 1] = p1;
       if constexpr (st < 4) {
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st], s[0][4 * st + 1], 0, false);
         pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st + 2], s[0][4 * st + 3], w, true);
+        pin(pw[st]);
       }
     } else {
       if constexpr (st < 12) {
         constexpr int q = st - 8;
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], 0, false);
         pw[4 + q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q + 2], s[1][4 * q + 3], w, true);
+        pin(pw[4 + q]);
 #pragma unroll
-        for (int i = 4 * q; i < 4 * q + 4; ++i) ps[i] = s[0][i] + s[1][i];
+        for (int i = 4 * q; i < 4 * q + 4; ++i) {
+          ps[i] = s[0][i] + s[1][i];
+          pin(ps[i]);
+        }
       } else if constexpr (st < 14) {
         constexpr int base = 4 * (st - 12);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qa[base + i] = ps[base + i] + ps[base + i + 8];
+        for (int i = 0; i < 4; ++i) {
+          qa[base + i] = ps[base + i] + ps[base + i + 8];
+          pin(qa[base + i]);
+        }
       } else if constexpr (st == 14) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qa[i] += qa[i + 4];
+        for (int i = 0; i < 4; ++i) {
+          qa[i] += qa[i + 4];
+          pin(qa[i]);
+        }
       } else {
         l_run = __builtin_fmaf(l_run, alpha_p, (qa[0] + qa[2]) + (qa[1] + qa[3]));
+        pin(l_run);
       }
     }
   };
@@ -300,6 +331,10 @@ void fwd_fp8_kernel(const FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (SOFT != 0) p_pack(sn);
+    // the scores are first read in the next iteration: keep their MFMAs here,
+    // between this block's softmax steps, rather than after the barrier
+    pin(s[0]);
+    pin(s[1]);
   };
   // O^T += V^T P^T of V buffer `buf`, P^T in the first 8 words of p; the first
   // softmax half of `sn` rides along

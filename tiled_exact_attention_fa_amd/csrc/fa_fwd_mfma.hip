@@ -531,16 +531,25 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     auto sv = [&](int x) { return s[x >> 4][x & 15]; };
     if constexpr (st < 3) {
 #pragma unroll
-      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
-      if constexpr (st == 2) ta[10] = fmaxf(sv(30), sv(31));
+      for (int i = 4 * st; i < (st == 2 ? 10 : 4 * st + 4); ++i) {
+        ta[i] = max3f(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
+        pin(ta[i]);
+      }
+      if constexpr (st == 2) {
+        ta[10] = fmaxf(sv(30), sv(31));
+        pin(ta[10]);
+      }
     } else if constexpr (st == 3) {
       ua[0] = max3f(ta[0], ta[1], ta[2]);
       ua[1] = max3f(ta[3], ta[4], ta[5]);
       ua[2] = max3f(ta[6], ta[7], ta[8]);
       ua[3] = fmaxf(ta[9], ta[10]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pin(ua[i]);
     } else if constexpr (st == 4) {
       mxa = max3f(ua[0], ua[1], fmaxf(ua[2], ua[3]));
       mxa = fmaxf(mxa, swap_halves(mxa));
+      pin(mxa);
     } else if constexpr (st == 5) {
       mxa *= cscale;
       // lazy running max: move only when the tile max exceeds it by the slack
@@ -550,10 +559,16 @@ void fwd_mfma16_kernel(const FwdArgs a) {
       alpha_p = move_p ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
       m_run = m_new;
       m_use = (m_run == neg_inf()) ? 0.f : m_run;
+      pin(alpha_p);
+      pin(m_use);
     } else if constexpr (st < 15) {
       constexpr int e = 2 * (st - 7);
-      s[0][e] = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
-      s[0][e + 1] = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+      float p0 = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
+      float p1 = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+      pin(p0);
+      pin(p1);
+      s[0][e] = p0;
+      s[0][e + 1] = p1;
     }
   };
   // Second half, in 16 steps: exponents of s[1]; P^T rounded to 16 bits, two
@@ -568,24 +583,40 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   auto soft_b_step = [&](auto step_tag, f32x16 s[2]) {
     constexpr int st = decltype(step_tag)::value;
     if constexpr (st < 8) {
-      s[1][2 * st] = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
-      s[1][2 * st + 1] = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      float p0 = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
+      float p1 = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      pin(p0);
+      pin(p1);
+      s[1][2 * st] = p0;
+      s[1][2 * st + 1] = p1;
       pw[st] = pack2(s[0][2 * st], s[0][2 * st + 1]);
+      pin(pw[st]);
     } else {
       pw[st] = pack2(s[1][2 * (st - 8)], s[1][2 * (st - 8) + 1]);
+      pin(pw[st]);
       if constexpr (st < 12) {
         constexpr int mb = (st - 8) >> 1, base = 4 * ((st - 8) & 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ps[8 * mb + base + i] = s[mb][2 * (base + i)] + s[mb][2 * (base + i) + 1];
+        for (int i = 0; i < 4; ++i) {
+          ps[8 * mb + base + i] = s[mb][2 * (base + i)] + s[mb][2 * (base + i) + 1];
+          pin(ps[8 * mb + base + i]);
+        }
       } else if constexpr (st < 14) {
         constexpr int base = 4 * (st - 12);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qa[base + i] = ps[base + i] + ps[base + i + 8];
+        for (int i = 0; i < 4; ++i) {
+          qa[base + i] = ps[base + i] + ps[base + i + 8];
+          pin(qa[base + i]);
+        }
       } else if constexpr (st == 14) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qa[i] += qa[i + 4];
+        for (int i = 0; i < 4; ++i) {
+          qa[i] += qa[i + 4];
+          pin(qa[i]);
+        }
       } else {
         l_run = __builtin_fmaf(l_run, alpha_p, (qa[0] + qa[2]) + (qa[1] + qa[3]));
+        pin(l_run);
       }
     }
   };
@@ -628,6 +659,10 @@ void fwd_mfma16_kernel(const FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (SOFT != 0) p_pack(sn);
+    // the scores are first read in the next iteration: keep their MFMAs here,
+    // between this block's softmax steps, rather than after the barrier
+    pin(s[0]);
+    pin(s[1]);
   };
   // O^T += V^T P^T of V buffer `buf`, P^T in p[0]; the first softmax half of
   // `sn` rides along
