@@ -298,16 +298,26 @@ void fwd_fp8_kernel(const FwdArgs a) {
     }
   };
 
-  // S^T of K buffer `buf` into s; softmax work on `sn` rides along: none
-  // (SOFT = 0), its second half (1) or both halves (2)
-  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra) {
-    constexpr int SOFT = decltype(soft_tag)::value;
-    u32x4 kf[RA][2];
+  // first RA operand fragments of a block, read ahead by the caller
+  auto k_init = [&](int buf, u32x4 (&kf)[RA][2]) {
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       kf[i][0] = kfrag(buf, i, 0);
       kf[i][1] = kfrag(buf, i, 1);
     }
+  };
+  auto v_init = [&](int buf, u32x4 (&vf)[RA][2]) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      vf[i][0] = vfrag(buf, i, 0);
+      vf[i][1] = vfrag(buf, i, 1);
+    }
+  };
+  // S^T of K buffer `buf` into s, starting from the fragments kf; softmax
+  // work on `sn` rides along: none (SOFT = 0), its second half (1) or both
+  // halves (2)
+  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra, u32x4 (&kf)[RA][2]) {
+    constexpr int SOFT = decltype(soft_tag)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
     static_for<NM>([&](auto I) {
@@ -336,23 +346,23 @@ void fwd_fp8_kernel(const FwdArgs a) {
     pin(s[0]);
     pin(s[1]);
   };
-  // O^T += V^T P^T of V buffer `buf`, P^T in the first 8 words of p; the first
-  // softmax half of `sn` rides along
-  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra) {
+  // O^T += V^T P^T of V buffer `buf`, P^T in the first 8 words of p,
+  // starting from the fragments vf; the first softmax half of `sn` rides
+  // along, and the slots past the last V read fetch the first fragments kn
+  // of the next S^T block (K buffer kbn)
+  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra, u32x4 (&vf)[RA][2], int kbn,
+                      u32x4 (&kn)[RA][2]) {
     const i32x16 pi = __builtin_bit_cast(i32x16, p);
     const i32x8 pf = __builtin_shufflevector(pi, pi, 0, 1, 2, 3, 4, 5, 6, 7);
-    u32x4 vf[RA][2];
-#pragma unroll
-    for (int i = 0; i < RA; ++i) {
-      vf[i][0] = vfrag(buf, i, 0);
-      vf[i][1] = vfrag(buf, i, 1);
-    }
     static_for<NM>([&](auto I) {
       constexpr int i = decltype(I)::value;
       oacc[i] = mma(join(vf[i % RA][0], vf[i % RA][1]), pf, oacc[i]);
       if constexpr (i + RA < NM) {
         vf[i % RA][0] = vfrag(buf, i + RA, 0);
         vf[i % RA][1] = vfrag(buf, i + RA, 1);
+      } else {
+        kn[i + RA - NM][0] = kfrag(kbn, i + RA - NM, 0);
+        kn[i + RA - NM][1] = kfrag(kbn, i + RA - NM, 1);
       }
       static_for<STEPS / NM>([&](auto K) {
         soft_a_step(std::integral_constant<int, i * (STEPS / NM) + decltype(K)::value>{}, sn);
@@ -395,9 +405,12 @@ void fwd_fp8_kernel(const FwdArgs a) {
   load_unit(0, 0);
   __syncthreads();
   if (0 < w_kt) {
-    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {});
+    u32x4 kf[RA][2];
+    k_init(0, kf);
+    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {}, kf);
     mask(sc[0], 0);
-    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {});
+    k_init(1, kf);
+    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {}, kf);
   }
   __syncthreads();
   store_k_from(k2, 0);
@@ -412,15 +425,18 @@ void fwd_fp8_kernel(const FwdArgs a) {
   auto iter = [&](auto set_tag, int t) {
     constexpr int cur = decltype(set_tag)::value;  // t & 1
     constexpr int nxt = cur ^ 1;
+    // V of tile t and K of tile t+2 both sit in buffer cur
+    u32x4 vf[RA][2], kf[RA][2];
+    v_init(cur, vf);  // first, so the reads overlap the rescale and mask
     rescale_o();
     mask(sc[nxt], t + 1);
     block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
       if constexpr (decltype(I)::value == 1) store_k_from(kreg[cur], nxt);
       if constexpr (decltype(I)::value == 2) store_v(cur, nxt);
-    });
+    }, vf, cur, kf);
     block_qk(cur, sc[cur], sc[nxt], std::integral_constant<int, 1>{}, [&](auto I) {
       if constexpr (decltype(I)::value == 1) load_unit(cur, t + 2);
-    });
+    }, kf);
     __syncthreads();
   };
   // iterations past the wave's last tile (causal): staging only

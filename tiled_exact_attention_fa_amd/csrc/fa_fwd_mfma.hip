@@ -632,13 +632,20 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     }
   };
 
-  // S^T of K buffer `buf` into s; softmax work on `sn` rides along: none
-  // (SOFT = 0), its second half (1) or both halves (2)
-  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra) {
-    constexpr int SOFT = decltype(soft_tag)::value;
-    u32x4 kf[RA];
+  // first RA operand fragments of a block, read ahead by the caller
+  auto k_init = [&](int buf, u32x4 (&kf)[RA]) {
 #pragma unroll
     for (int i = 0; i < RA; ++i) kf[i] = kfrag(buf, i);
+  };
+  auto v_init = [&](int buf, u32x4 (&vf)[RA]) {
+#pragma unroll
+    for (int i = 0; i < RA; ++i) vf[i] = vfrag(buf, i);
+  };
+  // S^T of K buffer `buf` into s, starting from the fragments kf; softmax
+  // work on `sn` rides along: none (SOFT = 0), its second half (1) or both
+  // halves (2)
+  auto block_qk = [&](int buf, f32x16 s[2], f32x16 sn[2], auto soft_tag, auto &&extra, u32x4 (&kf)[RA]) {
+    constexpr int SOFT = decltype(soft_tag)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
     static_for<NQK>([&](auto I) {
@@ -664,21 +671,22 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     pin(s[0]);
     pin(s[1]);
   };
-  // O^T += V^T P^T of V buffer `buf`, P^T in p[0]; the first softmax half of
-  // `sn` rides along
-  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra) {
+  // O^T += V^T P^T of V buffer `buf`, P^T in p[0], starting from the
+  // fragments vf; the first softmax half of `sn` rides along, and the slots
+  // past the last V read fetch the first fragments kn of the next S^T block
+  // (K buffer kbn), so that block starts without waiting on LDS
+  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra, u32x4 (&vf)[RA], int kbn,
+                      u32x4 (&kn)[RA]) {
     frag pf[4];
     pf[0] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 0, 1, 2, 3));
     pf[1] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 4, 5, 6, 7));
     pf[2] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 8, 9, 10, 11));
     pf[3] = __builtin_bit_cast(frag, __builtin_shufflevector(p, p, 12, 13, 14, 15));
-    u32x4 vf[RA];
-#pragma unroll
-    for (int i = 0; i < RA; ++i) vf[i] = vfrag(buf, i);
     static_for<NPV>([&](auto I) {
       constexpr int i = decltype(I)::value;
       oacc[i >> 2] = M::mma(__builtin_bit_cast(frag, vf[i % RA]), pf[i & 3], oacc[i >> 2]);
       if constexpr (i + RA < NPV) vf[i % RA] = vfrag(buf, i + RA);
+      else kn[i + RA - NPV] = kfrag(kbn, i + RA - NPV);
       static_for<STEPS / NPV>([&](auto K) {
         soft_a_step(std::integral_constant<int, i * (STEPS / NPV) + decltype(K)::value>{}, sn);
       });
@@ -720,9 +728,12 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   load_unit(0, 0);
   __syncthreads();
   if (0 < w_kt) {
-    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {});
+    u32x4 kf[RA];
+    k_init(0, kf);
+    block_qk(0, sc[0], sc[1], std::integral_constant<int, 0>{}, [](auto) {}, kf);
     mask(sc[0], 0);
-    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {});
+    k_init(1, kf);
+    block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {}, kf);
   }
   __syncthreads();
   store_k_from(vreg[1], 0);
@@ -742,15 +753,18 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   auto iter = [&](auto set_tag, int t) {
     constexpr int cur = decltype(set_tag)::value;  // t & 1
     constexpr int nxt = cur ^ 1;
+    // V of tile t and K of tile t+2 both sit in buffer cur
+    u32x4 vf[RA], kf[RA];
+    v_init(cur, vf);  // first, so the reads overlap the rescale and mask
     rescale_o();
     mask(sc[nxt], t + 1);
     block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
       if constexpr (decltype(I)::value == 1) store_k(cur, nxt);
       if constexpr (decltype(I)::value == 3) store_v(cur, nxt);
-    });
+    }, vf, cur, kf);
     block_qk(cur, sc[cur], sc[nxt], std::integral_constant<int, 1>{}, [&](auto I) {
       if constexpr (decltype(I)::value == 2) load_unit(cur, t + 2);
-    });
+    }, kf);
     __syncthreads();
   };
   // iterations past the wave's last tile (causal): staging only
