@@ -17,16 +17,20 @@ Modules
              split-and-merge evaluation used only to pin invariants.
   brute      pure-Python scalar loops (math.exp / math.fsum) for tiny shapes.
   e4m3       OCP E4M3FN byte decoder written from the format's definition.
+  quant      the KV-cache write side: per-token-per-head int8 and E4M3FN
+             quantisers (and the E4M3FN encoder), and the append of quantised
+             rows into a cache.
 
-Every function has a pin in tests/test_oracle.py (brute force, closed forms,
-invariants, library special cases, a hand-derived golden example); none of them
-is "parity unpinned".
+Every function has a pin in tests/test_oracle.py or tests/test_oracle_kv.py
+(brute force, closed forms, invariants, library special cases, a hand-derived
+golden example); none of them is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
     attention_fp64,
     attention_probs_fp64,
     decode_fp64,
+    dequant_fp8_fp64,
     dequant_int8_fp64,
     online_softmax_fp64,
     split_merge_fp64,
@@ -34,3 +38,4 @@ from .attention import (  # noqa: F401
 )
 from .brute import attention_brute  # noqa: F401
 from .e4m3 import e4m3_decode  # noqa: F401
+from .quant import e4m3_encode, kv_append_ref, quantize_kv_tokhead  # noqa: F401

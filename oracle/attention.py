@@ -13,7 +13,10 @@ Definitions follow the pages:
   ``online_softmax_fp64``, the pages' recurrence, to pin the exactness claim.
 * Decode over a quantised cache (KV-cache quantisation overview, section 1 "decode
   step" and section 3 "read path"): one new query attends to every cached key;
-  the cache is dequantised into the compute domain (int8 code x per-token scale).
+  the cache is dequantised into the compute domain (int8 or E4M3FN code x
+  per-token scale).  The optional residual window (same section, "residual
+  window" box: the most recent tokens stay in high precision) adds bf16 keys and
+  values that are attended next to the dequantised ones.
 
 Readings where the pages are silent (each is listed in the design notes):
   scale tau = 1/sqrt(d) unless given; causal mask is bottom-right aligned (key j
@@ -262,22 +265,47 @@ def dequant_int8_fp64(codes, scales) -> np.ndarray:
     return _f64(codes) * _f64(scales)[..., None]
 
 
-def decode_fp64(q, k_codes, k_scales, v_codes, v_scales, seq_lens=None,
-                scale: float | None = None, heads=None, threads: int | None = None):
-    """One-token decode over an int8 cache with per-token-per-head fp16 scales.
+def dequant_fp8_fp64(codes, scales) -> np.ndarray:
+    """E4M3FN code (decoded by the oracle's own decoder) times its per-token
+    fp16 scale, in float64 (exact: a 4-bit by 11-bit significand product).
+    codes [..., T, d] as bytes, scales [..., T]."""
+    from .e4m3 import e4m3_decode
 
-    q [B,Hq,d]; k_codes/v_codes [B,Hkv,L,d] int8; k_scales/v_scales [B,Hkv,L].
-    seq_lens [B] or None (all L).  Each query row sees keys 0..seq_len-1
-    (KV-cache quantisation overview, section 1: the decode step's new token
-    queries every cached key).  Returns (O [B,Hq,d], LSE [B,Hq]) in float64.
-    Only the (b, kv-head) slices that the requested heads need are dequantised.
+    return e4m3_decode(codes) * _f64(scales)[..., None]
+
+
+def _as_list(lens, B, default):
+    if lens is None:
+        return [default] * B
+    return [int(x) for x in (lens.tolist() if hasattr(lens, "tolist") else lens)]
+
+
+def decode_fp64(q, k_codes, k_scales, v_codes, v_scales, seq_lens=None,
+                scale: float | None = None, heads=None, threads: int | None = None,
+                kv_format: str = "int8", k_recent=None, v_recent=None, recent_lens=None):
+    """One-token decode over a quantised cache with per-token-per-head fp16 scales.
+
+    q [B,Hq,d]; k_codes/v_codes [B,Hkv,L,d] (int8 codes, or E4M3FN bytes when
+    kv_format is "fp8"); k_scales/v_scales [B,Hkv,L].  seq_lens [B] or None
+    (all L): each query row sees cache tokens 0..seq_len-1 (KV-cache
+    quantisation overview, section 1: the decode step's new token queries every
+    cached key).  With a residual window, k_recent/v_recent [B,Hkv,W,d] hold the
+    most recent tokens unquantised and recent_lens [B] (None = all W) of them are
+    attended as well; the window's keys join the same softmax.  Returns
+    (O [B,Hq,d], LSE [B,Hq]) in float64.  Only the (b, kv-head) slices that the
+    requested heads need are dequantised.
     """
+    if kv_format not in ("int8", "fp8"):
+        raise ValueError(kv_format)
+    deq = dequant_int8_fp64 if kv_format == "int8" else dequant_fp8_fp64
     qf = _f64(q)
     B, Hq, d = qf.shape
     Hkv, L = k_codes.shape[1], k_codes.shape[2]
     G = Hq // Hkv
     tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
-    lens = [L] * B if seq_lens is None else [int(x) for x in (seq_lens.tolist() if hasattr(seq_lens, "tolist") else seq_lens)]
+    lens = _as_list(seq_lens, B, L)
+    W = 0 if k_recent is None else k_recent.shape[2]
+    rlens = _as_list(recent_lens, B, W)
     work = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     o = np.zeros((B, Hq, d))
     lse = np.full((B, Hq), -np.inf)
@@ -288,10 +316,14 @@ def decode_fp64(q, k_codes, k_scales, v_codes, v_scales, seq_lens=None,
     def one(item):
         (b, kvh), hs = item
         n = lens[b]
-        kk = dequant_int8_fp64(k_codes[b, kvh, :n], k_scales[b, kvh, :n])
-        vv = dequant_int8_fp64(v_codes[b, kvh, :n], v_scales[b, kvh, :n])
+        kk = deq(k_codes[b, kvh, :n], k_scales[b, kvh, :n])
+        vv = deq(v_codes[b, kvh, :n], v_scales[b, kvh, :n])
+        if W:
+            r = rlens[b]
+            kk = np.concatenate([kk, _f64(k_recent[b, kvh, :r])])
+            vv = np.concatenate([vv, _f64(v_recent[b, kvh, :r])])
         qq = qf[b, hs][:, None, :]  # [g, 1, d]
-        nv = np.array([n])
+        nv = np.array([kk.shape[0]])
         for j, h in enumerate(hs):
             oo, ll = _two_pass_rows(qq[j], kk, vv, tau, nv, 1)
             o[b, h], lse[b, h] = oo[0], ll[0]

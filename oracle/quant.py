@@ -1,0 +1,110 @@
+"""KV-cache write-side quantisers — TEST INFRASTRUCTURE ONLY (see package doc).
+
+KV-cache quantisation overview, section 3 ("where quantisation can sit"): before
+a key or value row enters the cache it is turned from FP16/BF16 into a low-bit
+code plus the metadata needed to read it back (a scale); FP8 and INT8 are two of
+the storage forms the section lists, and the read side maps code x scale back
+into the compute domain.  The overview does not fix the granularity or the
+rounding; the readings taken here are:
+
+* symmetric codes, no zero point; one fp16 scale per (batch, cache head, token);
+* sc = fp16(fp32(absmax / QMAX)) with QMAX = 127 (int8) or 448 (E4M3FN, the
+  largest finite value of the format), the fp32 quotient clamped to 65504 first
+  so that the scale never becomes infinite; round to nearest even at each step;
+* sc == 0 (an all-zero row, or a row so small that its scale underflows fp16)
+  stores code 0 everywhere;
+* otherwise y = fp32(x) / fp32(sc), one correctly rounded fp32 division — the
+  precision in which the integer code is decided, on both sides of a parity test;
+* int8: code = clamp(rint(y), -127, 127), rint rounding half to even;
+* fp8:  code = the E4M3FN byte nearest to clamp(y, -448, 448), ties to the even
+  mantissa; the sign of y is kept, so a negative y that rounds to zero gives 0x80.
+
+The E4M3FN encoder is written from the format's definition (1 sign bit, 4
+exponent bits with bias 7, 3 mantissa bits, subnormals m/8 x 2^-6, largest
+finite 448, no infinities); it shares nothing with the GPU path.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+INT8_QMAX = 127.0
+E4M3_QMAX = 448.0
+F16_MAX = 65504.0
+
+
+def _f32(x) -> np.ndarray:
+    if isinstance(x, np.ndarray):
+        return x.astype(np.float32)
+    import torch
+
+    return x.detach().to("cpu", torch.float32).numpy()
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3FN byte to each float64 value, ties to even mantissa,
+    saturating at +-448.  Returns uint8 codes of the same shape."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_QMAX)
+    # binade exponent, held inside the normal range; below 2^-6 the spacing is
+    # that of the subnormals, 2^-9
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    spacing = np.exp2(e - 3)
+    val = np.rint(a / spacing) * spacing  # a / spacing is exact (power of two)
+    val = np.minimum(val, E4M3_QMAX)
+    normal = val >= 2.0 ** -6
+    with np.errstate(divide="ignore"):
+        en = np.floor(np.log2(np.where(normal, val, 1.0)))
+    efield = np.where(normal, en + 7, 0)
+    mfield = np.where(normal, val / np.exp2(en) * 8 - 8, val / 2.0 ** -9)
+    code = (neg.astype(np.int64) << 7) | (efield.astype(np.int64) << 3) | mfield.astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def quantize_kv_tokhead(x, fmt: str):
+    """Rows x [..., T, d] (bf16/fp16 values, numpy or torch) -> (codes, scales).
+
+    fmt "int8": codes int8; fmt "fp8": codes uint8 E4M3FN bytes.  scales are
+    float16 [..., T].  Every step follows the readings in the module doc."""
+    if fmt not in ("int8", "fp8"):
+        raise ValueError(fmt)
+    xf = _f32(x)
+    qmax = np.float32(INT8_QMAX if fmt == "int8" else E4M3_QMAX)
+    amax = np.max(np.abs(xf), axis=-1) if xf.shape[-1] else np.zeros(xf.shape[:-1], np.float32)
+    sc32 = np.minimum(amax.astype(np.float32) / qmax, np.float32(F16_MAX))
+    sc = sc32.astype(np.float16)
+    scf = sc.astype(np.float32)
+    live = scf > 0
+    y = xf / np.where(live, scf, np.float32(1.0))[..., None]  # float32 / float32
+    if fmt == "int8":
+        codes = np.clip(np.rint(y), -INT8_QMAX, INT8_QMAX)
+        codes = np.where(live[..., None], codes, 0).astype(np.int8)
+    else:
+        codes = e4m3_encode(np.clip(y.astype(np.float64), -E4M3_QMAX, E4M3_QMAX))
+        codes = np.where(live[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, sc
+
+
+def kv_append_ref(cache_codes, cache_scales, rows, positions, fmt: str):
+    """Writes quantised rows into copies of a cache.
+
+    cache_codes [B, H, L, d], cache_scales [B, H, L]; rows [B, H, T, d];
+    positions [B] (first cache slot written for batch b; None = 0).  Row t of
+    batch b goes to slot positions[b] + t; rows whose slot falls outside
+    [0, L) are dropped.  Returns the new (codes, scales)."""
+    codes = np.array(cache_codes, copy=True)
+    scales = np.array(cache_scales, copy=True)
+    qc, qs = quantize_kv_tokhead(rows, fmt)
+    B, H, T = qc.shape[:3]
+    L = codes.shape[2]
+    pos = [0] * B if positions is None else [int(p) for p in np.asarray(positions).tolist()]
+    for b in range(B):
+        for t in range(T):
+            s = pos[b] + t
+            if 0 <= s < L:
+                codes[b, :, s] = qc[b, :, t]
+                scales[b, :, s] = qs[b, :, t]
+    return codes, scales
