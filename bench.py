@@ -8,8 +8,11 @@ resident in HBM.  The headline workload is causal bf16 prefill, B=4, H=16,
 S=2048, d=128 with LSE output; its TFLOP/s counts 4*d flops per visible
 (query, key) pair (S*(S+1)/2 pairs per head under the causal mask).  The other
 workloads are timed the same way and reported under "workloads": long-context
-GQA prefill and fp8 prefill in TFLOP/s, int8-KV split decode in GB/s of the
-bytes the method must move (K/V codes + scales + query + output + LSE).
+GQA prefill and fp8 prefill in TFLOP/s; int8-KV and fp8-KV split decode, the
+decode with a bf16 residual window, and the quantise-on-append of a 4096-token
+chunk in GB/s of the bytes the method must move (codes + scales + window +
+query + output + LSE for decode; rows read and codes + scales written for the
+append).
 
 Timing uses HIP events on the stream the kernels are launched on (torch's
 current stream), bracketed by device synchronisations, after at least W
@@ -71,14 +74,35 @@ def fwd_hbm_bytes(cfg) -> int:
 
 def decode_bytes(cfg) -> int:
     """KV bytes = 2 * layers * batch * tokens * kv_heads * head_dim * bytes_per_elem
-    with one layer and 1-byte codes, plus the per-token fp16 scales of K and V,
+    with one layer and 1-byte codes (int8 or fp8), plus the per-token fp16 scales
+    of K and V, the bf16 residual window's keys and values when there is one,
     the bf16 query, the bf16 output and the float32 LSE."""
     kv = 2 * 1 * cfg.B * cfg.L * cfg.Hkv * cfg.d * 1
     scales = 2 * cfg.B * cfg.Hkv * cfg.L * 2
+    window = 2 * cfg.B * cfg.Hkv * cfg.W * cfg.d * 2
     q = cfg.B * cfg.Hq * cfg.d * 2
     o = cfg.B * cfg.Hq * cfg.d * 2
     lse = cfg.B * cfg.Hq * 4
-    return kv + scales + q + o + lse
+    return kv + scales + window + q + o + lse
+
+
+def append_bytes(cfg) -> int:
+    """Quantise-on-append: the bf16 key and value rows read once, their 1-byte
+    codes and fp16 per-row scales written once."""
+    rows = cfg.B * cfg.H * cfg.T
+    return 2 * rows * cfg.d * 2 + 2 * (rows * cfg.d + rows * 2)
+
+
+def algorithmic_bytes(cfg) -> int:
+    if isinstance(cfg, fa_inputs.DecodeConfig):
+        return decode_bytes(cfg)
+    if isinstance(cfg, fa_inputs.AppendConfig):
+        return append_bytes(cfg)
+    return fwd_hbm_bytes(cfg)
+
+
+def workload(name):
+    return fa_inputs.CONFIGS[name] if name in fa_inputs.CONFIGS else fa_inputs.KV_CONFIGS[name]
 
 
 # ---- GPU timing ---------------------------------------------------------------
@@ -139,12 +163,27 @@ def _decode_runner(cfg, seed=0):
     x = fa_inputs.make_decode_inputs(cfg, seed=seed, device="cuda")
     o = torch.empty(cfg.B, cfg.Hq, cfg.d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(cfg.B, cfg.Hq, dtype=torch.float32, device="cuda")
-    ws = fa.decode_workspace(cfg.B, cfg.Hq, cfg.d, cfg.num_splits)
+    ws = fa.decode_workspace(cfg.B, cfg.Hq, cfg.d, cfg.num_splits, window=cfg.W > 0)
+    win = {}
+    if cfg.W > 0:
+        win = {"k_recent": x["k_recent"], "v_recent": x["v_recent"], "recent_lens": x["recent_lens"]}
 
     def run():
         fa.fa_decode_kvq(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], o, lse,
                          seq_lens=x["seq_lens"], num_splits=cfg.num_splits,
-                         softmax_scale=cfg.scale, workspace=ws)
+                         softmax_scale=cfg.scale, workspace=ws, kv_format=cfg.kv_format, **win)
+
+    return run
+
+
+def _append_runner(cfg, seed=0):
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_append_inputs(cfg, seed=seed, device="cuda")
+
+    def run():  # every call writes the same chunk to the same slots
+        fa.fa_kv_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"],
+                        positions=x["positions"], kv_format=cfg.kv_format)
 
     return run
 
@@ -175,13 +214,13 @@ def stored_traffic(workload: str):
 
 
 def measure(name, steps, warmup):
-    cfg = fa_inputs.CONFIGS[name]
+    cfg = workload(name)
     import torch
 
-    if isinstance(cfg, fa_inputs.DecodeConfig):
-        run = _decode_runner(cfg)
+    if isinstance(cfg, (fa_inputs.DecodeConfig, fa_inputs.AppendConfig)):
+        run = _decode_runner(cfg) if isinstance(cfg, fa_inputs.DecodeConfig) else _append_runner(cfg)
         ms, wall = _time_region(run, steps, warmup)
-        work = decode_bytes(cfg)
+        work = algorithmic_bytes(cfg)
         gbs = work / (ms * 1e-3) / 1e9
         res = {"unit": "GB/s", "value": gbs, "ms_per_call": ms, "bytes_per_call": work,
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -279,8 +318,8 @@ def summarize_pmc(a):
     ww, nw = _pmc_per_dispatch(a.pmc_write, "WRITE_SIZE", a.kernel)
     fetch = wf * 1024.0 * f_scale
     write = ww * 1024.0 * w_scale
-    cfg = fa_inputs.CONFIGS[a.workload]
-    algo = decode_bytes(cfg) if isinstance(cfg, fa_inputs.DecodeConfig) else fwd_hbm_bytes(cfg)
+    cfg = workload(a.workload)
+    algo = algorithmic_bytes(cfg)
     path = os.path.join(PROFILES, "hbm_traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[a.workload] = {"kernel": a.kernel, "bytes_per_launch": fetch + write, "fetch_bytes": fetch,
@@ -332,10 +371,10 @@ def main():
     fa.load()
     torch.cuda.set_device(0)
     head = measure(a.workload, a.steps, a.warmup)
-    cfg = fa_inputs.CONFIGS[a.workload]
+    cfg = workload(a.workload)
 
     extras = {}
-    names = [n for n in fa_inputs.CONFIGS if n != a.workload]
+    names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.KV_CONFIGS) if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":

@@ -21,6 +21,13 @@ runs, so CPU and GPU draws differ but each is deterministic for a given seed):
   code = clamp(rint(x / float(sc)), -127, 127), 0 where sc == 0.  The decode cache
   is drawn one batch entry at a time (seed (seed << 20) + b, K then V) so that no
   full-size float32 temporary is needed; the query uses seed (seed << 20) + B.
+* fp8 KV cache: the same draws, with sc = fp16(absmax_over_d / 448) and
+  code = E4M3FN(clamp(x / float(sc), +-448)), round to nearest even;
+* residual window: bf16 N(0,1) keys then values [B, Hkv, W, d] drawn with seed
+  (seed << 20) + B + 1, every sequence attending all W of them unless the config
+  lists window lengths;
+* append: new key rows then value rows [B, H, T, d] bf16 N(0,1) from seed
+  (seed << 20) + 7, written at each sequence's position pos0.
 """
 
 from __future__ import annotations
@@ -63,10 +70,25 @@ class DecodeConfig:
     d: int
     num_splits: int
     seq_lens: tuple = field(default=())
+    kv_format: str = "int8"  # "int8" | "fp8"
+    W: int = 0  # residual window capacity (0: none)
+    recent_lens: tuple = field(default=())
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
+
+
+@dataclass(frozen=True)
+class AppendConfig:
+    name: str
+    B: int
+    H: int
+    T: int
+    L: int
+    d: int
+    kv_format: str  # "int8" | "fp8"
+    pos0: int = 0
 
 
 # The five workloads: a tiny fp32 case, causal bf16 prefill, long-context GQA
@@ -78,6 +100,19 @@ CONFIGS = {
         "bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
     "fp8_b8_h16_s4096": FwdConfig("fp8_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128, False, out_dtype="bf16"),
     "decode_int8_b64_gqa32x8_L32768": DecodeConfig("decode_int8_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16),
+}
+
+# The cache's other formats and its write side, at the decode workload's sizes:
+# the same decode over an fp8 cache, the int8 decode with a 128-token bf16
+# residual window, and the quantise-on-append of a 4096-token chunk for all 64
+# sequences (positions 28672 .. 32767 of the 32768-slot cache).
+KV_CONFIGS = {
+    "decode_fp8_b64_gqa32x8_L32768": DecodeConfig("decode_fp8_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16,
+                                                  kv_format="fp8"),
+    "decode_int8_window128_b64_gqa32x8_L32768": DecodeConfig(
+        "decode_int8_window128_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16, W=128),
+    "append_int8_b64_h8_t4096": AppendConfig("append_int8_b64_h8_t4096", 64, 8, 4096, 32768, 128, "int8", 28672),
+    "append_fp8_b64_h8_t4096": AppendConfig("append_fp8_b64_h8_t4096", 64, 8, 4096, 32768, 128, "fp8", 28672),
 }
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -116,6 +151,22 @@ def quantize_int8_tokhead(x: torch.Tensor):
     return qv.to(torch.int8), sc
 
 
+def quantize_fp8_tokhead(x: torch.Tensor):
+    """float tensor [..., T, d] -> (E4M3FN codes [..., T, d] as uint8, fp16 scales [..., T]).
+
+    Symmetric per-token scale sc = fp16(absmax_d / 448); code = E4M3FN(x / sc)
+    after clamping to +-448, round to nearest even."""
+    xf = x.float()
+    amax = xf.abs().amax(dim=-1)
+    sc = (amax / E4M3_MAX).to(torch.float16)
+    scf = sc.float()
+    safe = torch.where(scf > 0, scf, torch.ones_like(scf))
+    y = (xf / safe[..., None]).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = torch.where(scf[..., None] > 0, codes, torch.zeros_like(codes))
+    return codes, sc
+
+
 def make_fwd_inputs(cfg: FwdConfig, seed: int = 0, device="cpu"):
     """Returns a dict with q, k, v (in the config's input dtype) and, for fp8,
     the float32 per-tensor scales q_scale, k_scale, v_scale."""
@@ -139,20 +190,24 @@ def make_fwd_inputs(cfg: FwdConfig, seed: int = 0, device="cpu"):
 
 
 def make_decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):
-    """Returns q [B,Hq,d] bf16, k/v codes [B,Hkv,L,d] int8, k/v scales [B,Hkv,L]
-    fp16 and seq_lens [B] int32 (all L unless the config lists lengths)."""
+    """Returns q [B,Hq,d] bf16, k/v codes [B,Hkv,L,d] (int8, or uint8 E4M3FN
+    bytes for the fp8 format), k/v scales [B,Hkv,L] fp16 and seq_lens [B] int32
+    (all L unless the config lists lengths); with a window also k_recent /
+    v_recent [B,Hkv,W,d] bf16 and recent_lens [B] int32."""
     B, Hkv, L, d = cfg.B, cfg.Hkv, cfg.L, cfg.d
-    kc = torch.empty(B, Hkv, L, d, dtype=torch.int8, device=device)
-    vc = torch.empty(B, Hkv, L, d, dtype=torch.int8, device=device)
+    quant = quantize_int8_tokhead if cfg.kv_format == "int8" else quantize_fp8_tokhead
+    cdt = torch.int8 if cfg.kv_format == "int8" else torch.uint8
+    kc = torch.empty(B, Hkv, L, d, dtype=cdt, device=device)
+    vc = torch.empty(B, Hkv, L, d, dtype=cdt, device=device)
     ks = torch.empty(B, Hkv, L, dtype=torch.float16, device=device)
     vs = torch.empty(B, Hkv, L, dtype=torch.float16, device=device)
     for b in range(B):
         g = _gen(device, (seed << 20) + b)
         kf = torch.randn(Hkv, L, d, generator=g, device=device, dtype=torch.float32)
-        kc[b], ks[b] = quantize_int8_tokhead(kf)
+        kc[b], ks[b] = quant(kf)
         del kf
         vf = torch.randn(Hkv, L, d, generator=g, device=device, dtype=torch.float32)
-        vc[b], vs[b] = quantize_int8_tokhead(vf)
+        vc[b], vs[b] = quant(vf)
         del vf
     g = _gen(device, (seed << 20) + B)
     q = torch.randn(B, cfg.Hq, d, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
@@ -160,4 +215,29 @@ def make_decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):
         lens = torch.tensor(cfg.seq_lens, dtype=torch.int32, device=device)
     else:
         lens = torch.full((B,), L, dtype=torch.int32, device=device)
-    return {"q": q, "k": kc, "v": vc, "k_scale": ks, "v_scale": vs, "seq_lens": lens}
+    out = {"q": q, "k": kc, "v": vc, "k_scale": ks, "v_scale": vs, "seq_lens": lens}
+    if cfg.W > 0:
+        g = _gen(device, (seed << 20) + B + 1)
+        out["k_recent"] = torch.randn(B, Hkv, cfg.W, d, generator=g, device=device).to(torch.bfloat16)
+        out["v_recent"] = torch.randn(B, Hkv, cfg.W, d, generator=g, device=device).to(torch.bfloat16)
+        rl = cfg.recent_lens if cfg.recent_lens else (cfg.W,) * B
+        out["recent_lens"] = torch.tensor(rl, dtype=torch.int32, device=device)
+    return out
+
+
+def make_append_inputs(cfg: AppendConfig, seed: int = 0, device="cpu"):
+    """Returns new rows k_new / v_new [B,H,T,d] bf16, empty caches [B,H,L,d]
+    (int8, or uint8 E4M3FN bytes) with fp16 scales [B,H,L], and positions [B]
+    int32 (all pos0)."""
+    g = _gen(device, (seed << 20) + 7)
+    shape = (cfg.B, cfg.H, cfg.T, cfg.d)
+    kn = torch.randn(*shape, generator=g, device=device).to(torch.bfloat16)
+    vn = torch.randn(*shape, generator=g, device=device).to(torch.bfloat16)
+    cdt = torch.int8 if cfg.kv_format == "int8" else torch.uint8
+    kc = torch.zeros(cfg.B, cfg.H, cfg.L, cfg.d, dtype=cdt, device=device)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(cfg.B, cfg.H, cfg.L, dtype=torch.float16, device=device)
+    vs = torch.zeros_like(ks)
+    pos = torch.full((cfg.B,), cfg.pos0, dtype=torch.int32, device=device)
+    return {"k_new": kn, "v_new": vn, "k_cache": kc, "v_cache": vc, "k_scale": ks, "v_scale": vs,
+            "positions": pos}

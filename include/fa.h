@@ -11,16 +11,23 @@
  * forward also returns the per-row statistic LSE_i = ln sum_j exp(s_ij) that a
  * recomputing backward needs (panel 3, Q3).
  *
- * Two entry points do work:
+ * Three entry points do work:
  *   fa_fwd         prefill (KV-cache quantisation overview, section 1, "prefill"):
  *                  every query row of a sequence against its keys, optional
  *                  causal mask, grouped-query heads, optional LSE output;
  *                  fp32, bf16, fp16 or fp8-e4m3 inputs.
  *   fa_decode_kvq  one decode step (same page, section 1, "decode step"): one new
  *                  query token per sequence against the whole cache, read from an
- *                  int8 cache with per-token-per-head scales and dequantised inside
- *                  the kernel (section 3, "read path"); the cache is split into
- *                  chunks processed in parallel and merged by their log-sum-exps.
+ *                  int8 or fp8-e4m3 cache with per-token-per-head scales and
+ *                  dequantised inside the kernel (section 3, "read path"); the
+ *                  cache is split into chunks processed in parallel and merged by
+ *                  their log-sum-exps.  An optional residual window of recent
+ *                  tokens kept in bf16 (section 3, "residual window") joins the
+ *                  same softmax.
+ *   fa_kv_append   the cache's write side (section 3, "before writing the cache"):
+ *                  new bf16/fp16 key and value rows are quantised to int8 or
+ *                  fp8-e4m3 codes with one fp16 scale per token and head, and
+ *                  stored at each sequence's next cache positions.
  *
  * Conventions shared by every call.
  *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
@@ -105,25 +112,42 @@ typedef struct {
 int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
 
 /*
+ * Cache formats.  Both store one code byte per element and one fp16 scale per
+ * (batch, head, token); the value of an element is code * scale (symmetric, no
+ * zero point).  The KV-cache quantisation overview lists FP8 and INT8 among the
+ * storage forms (section 3, "storage form").
+ *   FA_KV_INT8_TOKHEAD_F16SCALE      signed int8 codes in [-127, 127]
+ *   FA_KV_FP8_E4M3_TOKHEAD_F16SCALE  OCP FP8 E4M3FN bytes (max 448); the NaN
+ *                                    codes 0x7F / 0xFF must not occur
+ */
+typedef enum { FA_KV_INT8_TOKHEAD_F16SCALE = 0, FA_KV_FP8_E4M3_TOKHEAD_F16SCALE = 1 } fa_kv_format;
+
+/*
  * One-token decode over a quantised cache.
  *   q [B, Hq, d] bf16                         o [B, Hq, d] bf16
- *   k_cache, v_cache [B, Hkv, L, d] int8      lse [B, Hq] float32 (may be NULL)
+ *   k_cache, v_cache [B, Hkv, L, d] codes     lse [B, Hq] float32 (may be NULL)
  *   k_scale, v_scale [B, Hkv, L] fp16 (token stride 1; 2-byte alignment is
- *                    enough, 16-byte aligned scale rows take the faster loads)
+ *                    enough; 16-byte aligned scale rows with L a multiple of 4 take the
+ *                    faster loads)
  *   seq_lens [B] int32 on the device, or NULL meaning every sequence has L tokens
- * The dequantised key/value of token t is code * scale (symmetric, no zero
- * point).  Query head h reads cache head h / (Hq / Hkv).  d must be 128 and
- * Hq / Hkv at most 16.  Each sequence's first seq_lens[b] tokens are attended
- * (0 <= seq_lens[b] <= L; a value outside that range is clamped into it;
- * zero tokens give O = 0 and LSE = -inf).
+ * kv_format says how the codes are read (fa_kv_format).  Query head h reads
+ * cache head h / (Hq / Hkv).  d must be 128 and Hq / Hkv at most 16.  Each
+ * sequence's first seq_lens[b] tokens are attended (0 <= seq_lens[b] <= L; a
+ * value outside that range is clamped into it).
+ * Residual window (optional, W > 0): k_recent, v_recent [B, Hkv, W, d] bf16
+ * (strides recent_strides, shared by both) hold recent tokens unquantised, and
+ * recent_lens [B] int32 on the device (NULL = W; clamped into [0, W]) says how
+ * many of them each sequence attends; they join the same softmax as the cache
+ * tokens.  With W == 0 the window pointers are ignored.  A sequence that attends
+ * no token at all gets O = 0 and LSE = -inf.
  * The L positions are cut into num_splits chunks of ceil(L / num_splits)
  * tokens rounded up to a multiple of 32 (1 <= num_splits <= 64; trailing chunks
- * may be empty); every chunk yields a normalised partial output and its
- * log-sum-exp, and a second kernel merges them.  The partials live in
- * the caller's workspace, of at least fa_decode_workspace_size(...) bytes
+ * may be empty); every chunk, and the window, yields a normalised partial
+ * output and its log-sum-exp, and a second kernel merges them.  The partials
+ * live in the caller's workspace, of at least
+ * fa_decode_workspace_size(B, Hq, d, num_splits + (W > 0 ? 1 : 0)) bytes
  * (16-byte aligned); its contents on entry do not matter.
  */
-typedef enum { FA_KV_INT8_TOKHEAD_F16SCALE = 0 } fa_kv_format;
 
 typedef struct {
   const void *q;
@@ -142,17 +166,59 @@ typedef struct {
   float softmax_scale;
   void *workspace;
   size_t workspace_bytes;
+  /* residual window; W == 0 disables it */
+  const void *k_recent, *v_recent;
+  const int32_t *recent_lens;
+  int32_t W;
+  int64_t recent_strides[3]; /* batch, head, token — shared by k_recent and v_recent */
 } fa_decode_params;
 
-/* Bytes of workspace fa_decode_kvq needs for these sizes (0 on invalid sizes). */
+/* Bytes of workspace fa_decode_kvq needs for these sizes (0 on invalid sizes);
+ * num_splits counts the window as one more partial when it is used. */
 size_t fa_decode_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t num_splits);
 
 int fa_decode_kvq(const fa_decode_params *p, fa_stream_t stream);
 
-/* Host-only validation used by the two calls above; makes no HIP call, so it
+/*
+ * Quantise-on-append: the write side of the cache (KV-cache quantisation
+ * overview, section 3, "before writing the cache": K/V go from FP16/BF16 to a
+ * low-bit form that needs a scale).
+ *   k_new, v_new [B, H, T, d] in_dtype (FA_BF16 or FA_F16), strides new_strides
+ *   k_cache, v_cache [B, H, L, d] code bytes, strides kv_strides (shared)
+ *   k_scale, v_scale [B, H, L] fp16, strides scale_strides (token stride 1)
+ *   positions [B] int32 on the device, or NULL meaning 0 for every sequence
+ * Row t of sequence b is written to cache slot positions[b] + t; rows whose slot
+ * falls outside [0, L) are skipped, and no other slot is touched.  d must be 128.
+ * Per row (one token of one head), with QMAX = 127 for int8 and 448 for E4M3FN:
+ *   sc   = fp16(min(fp32(absmax / QMAX), 65504)), round to nearest even
+ *   code = 0 everywhere if sc == 0, else with y = fp32(x) / fp32(sc) (one
+ *          correctly rounded fp32 division):
+ *          int8:   clamp(rint(y), -127, 127), ties to even
+ *          E4M3FN: the nearest E4M3FN value to clamp(y, -448, 448), ties to even
+ * so that dequantising (code * sc) gives back x to within half a code step.
+ * The inputs must be finite.  A call writes only the cache slots it addresses;
+ * concurrent calls that address the same slot race.
+ */
+typedef struct {
+  const void *k_new, *v_new;
+  void *k_cache, *v_cache;
+  void *k_scale, *v_scale;
+  const int32_t *positions;
+  int32_t in_dtype;             /* fa_dtype: FA_BF16 or FA_F16 */
+  int32_t kv_format;            /* fa_kv_format */
+  int32_t B, H, T, L, d;
+  int64_t new_strides[3];       /* batch, head, token — shared by k_new and v_new */
+  int64_t kv_strides[3];        /* batch, head, token — shared by k_cache and v_cache */
+  int64_t scale_strides[2];     /* batch, head — shared by k_scale and v_scale */
+} fa_kv_append_params;
+
+int fa_kv_append(const fa_kv_append_params *p, fa_stream_t stream);
+
+/* Host-only validation used by the calls above; makes no HIP call, so it
  * can run on a machine without a GPU.  Returns FA_OK or a negative fa_status. */
 int fa_check_fwd_params(const fa_fwd_params *p);
 int fa_check_decode_params(const fa_decode_params *p);
+int fa_check_kv_append_params(const fa_kv_append_params *p);
 
 /* Static description of a status code. */
 const char *fa_status_string(int status);

@@ -31,10 +31,31 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
-def test_struct_layout_matches_header():
-    # sizes follow from the field lists of include/fa.h on LP64
-    assert ctypes.sizeof(fa.FaFwdParams) == 5 * 8 + 8 * 4 + 4 * 24 + 16 + 4 * 5 + 4
-    assert ctypes.sizeof(fa.FaDecodeParams) == 8 * 8 + 6 * 4 + 16 + 24 + 16 + 16 + 16 + 8 + 8 + 8
+STRUCTS = [("fa_fwd_params", fa.FaFwdParams), ("fa_decode_params", fa.FaDecodeParams),
+           ("fa_kv_append_params", fa.FaKvAppendParams)]
+
+
+def test_struct_layout_matches_header(tmp_path):
+    # the C compiler's own sizeof / offsetof of every field of include/fa.h
+    # against the ctypes mirrors
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', "int main(void) {"]
+    for cname, py in STRUCTS:
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out if ln.strip()}
+    for cname, py in STRUCTS:
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
 
 
 def good_fwd():
@@ -137,11 +158,87 @@ def test_decode_validator(lib):
     (lambda p: setattr(p, "v_scale", 0x20001), fa.FA_ERR_ALIGNMENT),
     (lambda p: setattr(p, "scale_strides", fa.I64x2(8 * 1000, -1)), fa.FA_ERR_INVALID_ARG),
     (lambda p: setattr(p, "softmax_scale", -1.0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "W", -1), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "W", 64), fa.FA_ERR_INVALID_ARG),  # window on, window pointers NULL
 ])
 def test_decode_validator_errors(lib, mutate, status):
     p = good_decode()
     mutate(p)
     assert fa.fa_check_decode_params(p) == status
+
+
+def good_window(p):
+    p.k_recent = p.v_recent = 0x60000
+    p.W = 64
+    p.recent_strides = fa.I64x3(8 * 64 * 128, 64 * 128, 128)
+    p.workspace_bytes = fa.fa_decode_workspace_size(4, 32, 128, 17)
+    return p
+
+
+def test_decode_fp8_format_and_window_accepted(lib):
+    p = good_decode()
+    p.kv_format = fa.FA_KV_FP8_E4M3_TOKHEAD_F16SCALE
+    assert fa.fa_check_decode_params(p) == fa.FA_OK
+    assert fa.fa_check_decode_params(good_window(good_decode())) == fa.FA_OK
+
+
+@pytest.mark.parametrize("mutate,status", [
+    # the window takes one more partial slot: the split-only size is too small
+    (lambda p: setattr(p, "workspace_bytes", fa.fa_decode_workspace_size(4, 32, 128, 16)), fa.FA_ERR_WORKSPACE),
+    (lambda p: setattr(p, "v_recent", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "k_recent", 0x60008), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "recent_strides", fa.I64x3(8 * 64 * 128, 64 * 128, 120)), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "recent_strides", fa.I64x3(8 * 64 * 128, 64 * 128, 132)), fa.FA_ERR_ALIGNMENT),
+])
+def test_decode_window_validator_errors(lib, mutate, status):
+    p = good_window(good_decode())
+    mutate(p)
+    assert fa.fa_check_decode_params(p) == status
+
+
+def good_append():
+    p = fa.FaKvAppendParams()
+    p.k_new = p.v_new = 0x10000
+    p.k_cache = p.v_cache = 0x20000
+    p.k_scale = p.v_scale = 0x30000
+    p.in_dtype = fa.FA_BF16
+    p.kv_format = fa.FA_KV_INT8_TOKHEAD_F16SCALE
+    p.B, p.H, p.T, p.L, p.d = 4, 8, 16, 1000, 128
+    p.new_strides = fa.I64x3(8 * 16 * 128, 16 * 128, 128)
+    p.kv_strides = fa.I64x3(8 * 1000 * 128, 1000 * 128, 128)
+    p.scale_strides = fa.I64x2(8 * 1000, 1000)
+    return p
+
+
+def test_append_validator(lib):
+    assert fa.fa_check_kv_append_params(good_append()) == fa.FA_OK
+    p = good_append()
+    p.kv_format, p.in_dtype = fa.FA_KV_FP8_E4M3_TOKHEAD_F16SCALE, fa.FA_F16
+    assert fa.fa_check_kv_append_params(p) == fa.FA_OK
+    p = good_append()
+    p.T = 0
+    p.k_new = 0  # nothing to write: no tensor is looked at
+    assert fa.fa_check_kv_append_params(p) == fa.FA_OK
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "kv_format", 5), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "in_dtype", fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "d", 64), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "H", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "T", -1), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "v_new", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "k_cache", 0x20008), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "k_scale", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "v_scale", 0x30001), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "new_strides", fa.I64x3(8 * 16 * 128, 16 * 128, 120)), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "scale_strides", fa.I64x2(-1, 1000)), fa.FA_ERR_INVALID_ARG),
+    (lambda p: (setattr(p, "B", 1 << 20), setattr(p, "H", 1 << 8), setattr(p, "T", 1 << 4)), fa.FA_ERR_UNSUPPORTED),
+])
+def test_append_validator_errors(lib, mutate, status):
+    p = good_append()
+    mutate(p)
+    assert fa.fa_check_kv_append_params(p) == status
 
 
 def test_status_strings(lib):

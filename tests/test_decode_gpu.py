@@ -1,5 +1,6 @@
-"""GPU parity of fa_decode_kvq (int8 KV cache, split-KV + LSE combine) against
-the float64 oracle fed the same quantised cache."""
+"""GPU parity of fa_decode_kvq (int8 KV cache, split-KV + LSE combine; the
+ragged-tail check also over an fp8 cache) against the float64 oracle fed the
+same quantised cache."""
 
 import dataclasses
 
@@ -29,8 +30,9 @@ def run_decode(fa, x, num_splits, lse_wanted=True):
 
 
 def compare(o, lse, xc, heads=None):
+    fmt = "int8" if xc["k"].dtype == torch.int8 else "fp8"
     ro, rl = oracle.decode_fp64(xc["q"], xc["k"].numpy(), xc["k_scale"].numpy(), xc["v"].numpy(),
-                                xc["v_scale"].numpy(), xc["seq_lens"].numpy(), heads=heads)
+                                xc["v_scale"].numpy(), xc["seq_lens"].numpy(), heads=heads, kv_format=fmt)
     og = o.double().cpu().numpy()
     sel = heads if heads is not None else [(b, h) for b in range(og.shape[0]) for h in range(og.shape[1])]
     bi = [b for b, _ in sel]
@@ -117,3 +119,32 @@ def test_decode_full_size_sampled(gpu):
             "seq_lens": x["seq_lens"][b:b + 1].cpu(),
         }
         compare(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], sub)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("vec_scales", [True, False])
+def test_decode_ragged_tail_tokens(gpu, fmt, vec_scales):
+    """Every sequence length 1..40 and a few longer odd ones, with each query
+    pointing at its sequence's LAST token so that this token dominates the
+    softmax: a tail token lost, or read with a wrong scale, moves O and LSE far
+    beyond the tolerance.  Both scale-load forms: 16-byte aligned scale rows
+    (8-byte loads) and rows offset by one element (2-byte loads)."""
+    lens = list(range(1, 41)) + [97, 255, 1001]
+    B, Hq, Hkv, L = len(lens), 4, 1, 1024
+    cfg = fa_inputs.DecodeConfig("t", B, Hq, Hkv, L, 128, 7, tuple(lens), fmt)
+    xc = fa_inputs.make_decode_inputs(cfg, seed=17)
+    deq = oracle.dequant_int8_fp64 if fmt == "int8" else oracle.dequant_fp8_fp64
+    q = torch.empty(B, Hq, 128, dtype=torch.float64)
+    for b, n in enumerate(lens):
+        last = deq(xc["k"][b, 0, n - 1:n].numpy(), xc["k_scale"][b, 0, n - 1:n].numpy())[0]
+        for h in range(Hq):
+            q[b, h] = torch.from_numpy(last * (3.0 + h) / max(1e-9, float(np.abs(last).max())))
+    xc["q"] = q.to(torch.bfloat16)
+    x = {k: v.cuda() for k, v in xc.items()}
+    if not vec_scales:  # the same scales one element into a larger buffer: 2-byte aligned rows
+        for key in ("k_scale", "v_scale"):
+            big = torch.zeros(B, Hkv, L + 1, dtype=torch.float16, device="cuda")
+            big[..., 1:] = x[key]
+            x[key] = big[..., 1:]
+    o, lse = run_decode(gpu, x, 7)
+    compare(o, lse, xc)

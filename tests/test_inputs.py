@@ -78,3 +78,29 @@ def test_config_table_matches_workloads():
     assert (x.B, x.Hq, x.Sq, x.causal, x.dtype) == (8, 16, 4096, False, "fp8")
     x = c["decode_int8_b64_gqa32x8_L32768"]
     assert (x.B, x.Hq, x.Hkv, x.L, x.num_splits) == (64, 32, 8, 32768, 16)
+
+
+def test_kv_generators_fp8_window_and_append():
+    dc = fa_inputs.DecodeConfig("t", 2, 8, 2, 40, 128, 4, (40, 7), "fp8", 16, (16, 3))
+    x = fa_inputs.make_decode_inputs(dc, seed=2)
+    assert x["k"].dtype == torch.uint8 and x["k"].shape == (2, 2, 40, 128)
+    assert x["k_recent"].dtype == torch.bfloat16 and x["k_recent"].shape == (2, 2, 16, 128)
+    assert x["recent_lens"].tolist() == [16, 3] and x["seq_lens"].tolist() == [40, 7]
+    # no NaN codes; each row's absmax maps to +-448
+    assert not ((x["k"] & 0x7F) == 0x7F).any()
+    assert bool((((x["v"] & 0x7F) == 0x7E).sum(dim=-1) >= 1).all())
+    ac = fa_inputs.AppendConfig("a", 2, 3, 5, 16, 128, "int8", 4)
+    y = fa_inputs.make_append_inputs(ac, seed=0)
+    assert y["k_new"].shape == (2, 3, 5, 128) and y["k_cache"].dtype == torch.int8
+    assert y["positions"].tolist() == [4, 4] and int(y["k_cache"].abs().max()) == 0
+
+
+def test_kv_config_table():
+    k = fa_inputs.KV_CONFIGS
+    x = k["decode_fp8_b64_gqa32x8_L32768"]
+    assert (x.B, x.Hq, x.Hkv, x.L, x.num_splits, x.kv_format, x.W) == (64, 32, 8, 32768, 16, "fp8", 0)
+    x = k["decode_int8_window128_b64_gqa32x8_L32768"]
+    assert (x.kv_format, x.W) == ("int8", 128)
+    for f in ("int8", "fp8"):
+        x = k[f"append_{f}_b64_h8_t4096"]
+        assert (x.B, x.H, x.T, x.L, x.pos0, x.kv_format) == (64, 8, 4096, 32768, 28672, f)

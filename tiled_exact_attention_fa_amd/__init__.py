@@ -10,7 +10,9 @@ been built, load() raises.
     fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None, ...)
     fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, ...)
     fa_decode_workspace_size(B, Hq, d, num_splits)
-    fa_check_fwd_params(params) / fa_check_decode_params(params)
+    fa_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=None, ...)
+    fa_check_fwd_params(params) / fa_check_decode_params(params) /
+    fa_check_kv_append_params(params)
     fa_status_string(status) / fa_last_error()
 
 Build with ``python -m tiled_exact_attention_fa_amd.build``.
@@ -27,7 +29,7 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3, FA_INT8 = 0, 1, 2, 3, 4
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGNMENT, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4, -5
-FA_KV_INT8_TOKHEAD_F16SCALE = 0
+FA_KV_INT8_TOKHEAD_F16SCALE, FA_KV_FP8_E4M3_TOKHEAD_F16SCALE = 0, 1
 
 I64x3 = ctypes.c_int64 * 3
 I64x2 = ctypes.c_int64 * 2
@@ -62,11 +64,28 @@ class FaDecodeParams(ctypes.Structure):
         ("o_strides", I64x2), ("lse_strides", I64x2),
         ("kv_format", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p), ("recent_lens", ctypes.c_void_p),
+        ("W", ctypes.c_int32), ("recent_strides", I64x3),
     ]
 
 
-EXPORTS = ["fa_fwd", "fa_decode_kvq", "fa_decode_workspace_size", "fa_check_fwd_params",
-           "fa_check_decode_params", "fa_status_string", "fa_last_error"]
+class FaKvAppendParams(ctypes.Structure):
+    """Mirror of fa_kv_append_params."""
+
+    _fields_ = [
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p),
+        ("in_dtype", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("new_strides", I64x3), ("kv_strides", I64x3), ("scale_strides", I64x2),
+    ]
+
+
+EXPORTS = ["fa_fwd", "fa_decode_kvq", "fa_decode_workspace_size", "fa_kv_append", "fa_check_fwd_params",
+           "fa_check_decode_params", "fa_check_kv_append_params", "fa_status_string", "fa_last_error"]
 
 
 class FaError(RuntimeError):
@@ -97,6 +116,10 @@ def load(path: str | None = None):
     lib.fa_check_fwd_params.restype = ctypes.c_int
     lib.fa_check_decode_params.argtypes = [ctypes.POINTER(FaDecodeParams)]
     lib.fa_check_decode_params.restype = ctypes.c_int
+    lib.fa_kv_append.argtypes = [ctypes.POINTER(FaKvAppendParams), ctypes.c_void_p]
+    lib.fa_kv_append.restype = ctypes.c_int
+    lib.fa_check_kv_append_params.argtypes = [ctypes.POINTER(FaKvAppendParams)]
+    lib.fa_check_kv_append_params.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -119,6 +142,10 @@ def fa_check_fwd_params(params: FaFwdParams) -> int:
 
 def fa_check_decode_params(params: FaDecodeParams) -> int:
     return load().fa_check_decode_params(ctypes.byref(params))
+
+
+def fa_check_kv_append_params(params: FaKvAppendParams) -> int:
+    return load().fa_check_kv_append_params(ctypes.byref(params))
 
 
 def fa_decode_workspace_size(B: int, Hq: int, d: int, num_splits: int) -> int:
@@ -186,15 +213,36 @@ def fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None,
         raise FaError(st, "fa_fwd", fa_last_error())
 
 
+def _kv_format(cache, kv_format):
+    """fa_kv_format from an explicit name/code, else from the cache dtype:
+    int8 -> int8 codes; float8_e4m3fn or uint8 -> E4M3FN bytes."""
+    import torch
+
+    if kv_format is not None:
+        return {"int8": FA_KV_INT8_TOKHEAD_F16SCALE, "fp8": FA_KV_FP8_E4M3_TOKHEAD_F16SCALE}.get(kv_format, kv_format)
+    if cache.dtype == torch.int8:
+        return FA_KV_INT8_TOKHEAD_F16SCALE
+    if cache.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FA_KV_FP8_E4M3_TOKHEAD_F16SCALE
+    raise TypeError(f"cannot infer the cache format from dtype {cache.dtype}")
+
+
 def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,
-                  num_splits=16, softmax_scale=None, workspace=None) -> FaDecodeParams:
+                  num_splits=16, softmax_scale=None, workspace=None, kv_format=None,
+                  k_recent=None, v_recent=None, recent_lens=None) -> FaDecodeParams:
     """fa_decode_params for q [B,Hq,d], caches [B,Hkv,L,d], scales [B,Hkv,L],
-    o [B,Hq,d], lse [B,Hq]; k and v caches (and their scales) must share strides."""
+    o [B,Hq,d], lse [B,Hq], and an optional bf16 window k_recent/v_recent
+    [B,Hkv,W,d]; k and v caches (and their scales, and the two window tensors)
+    must share strides."""
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o),
-                 ("k_scale", k_scale), ("v_scale", v_scale)):
+                 ("k_scale", k_scale), ("v_scale", v_scale), ("k_recent", k_recent), ("v_recent", v_recent)):
         _require_dense_d(n, t)
     if k_cache.stride() != v_cache.stride() or k_scale.stride() != v_scale.stride():
         raise ValueError("k and v caches (and their scales) must have identical strides")
+    if (k_recent is None) != (v_recent is None):
+        raise ValueError("k_recent and v_recent go together")
+    if k_recent is not None and k_recent.stride() != v_recent.stride():
+        raise ValueError("k_recent and v_recent must have identical strides")
     B, Hq, d = q.shape
     Hkv, L = k_cache.shape[1], k_cache.shape[2]
     p = FaDecodeParams()
@@ -207,27 +255,70 @@ def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=N
     p.scale_strides = I64x2(*k_scale.stride()[:2])
     p.o_strides = I64x2(*o.stride()[:2])
     p.lse_strides = I64x2(*(lse.stride()[:2] if lse is not None else (0, 0)))
-    p.kv_format = FA_KV_INT8_TOKHEAD_F16SCALE
+    p.kv_format = _kv_format(k_cache, kv_format)
     p.softmax_scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if k_recent is not None:
+        p.k_recent, p.v_recent, p.recent_lens = _ptr(k_recent), _ptr(v_recent), _ptr(recent_lens)
+        p.W = k_recent.shape[2]
+        p.recent_strides = I64x3(*k_recent.stride()[:3])
     return p
 
 
-def decode_workspace(B, Hq, d, num_splits, device="cuda"):
-    """A torch byte tensor big enough for fa_decode_kvq's partial results."""
+def decode_workspace(B, Hq, d, num_splits, device="cuda", window=False):
+    """A torch byte tensor big enough for fa_decode_kvq's partial results
+    (one more partial slot when a residual window is used)."""
     import torch
 
-    return torch.empty(fa_decode_workspace_size(B, Hq, d, num_splits), dtype=torch.uint8, device=device)
+    n = fa_decode_workspace_size(B, Hq, d, num_splits + (1 if window else 0))
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,
-                  num_splits=16, softmax_scale=None, workspace=None, stream=None) -> None:
-    """Enqueue one decode step over the int8 cache on torch's current stream."""
+                  num_splits=16, softmax_scale=None, workspace=None, stream=None, kv_format=None,
+                  k_recent=None, v_recent=None, recent_lens=None) -> None:
+    """Enqueue one decode step over the quantised cache (and the optional bf16
+    residual window) on torch's current stream."""
     if workspace is None:
-        workspace = decode_workspace(q.shape[0], q.shape[1], q.shape[2], num_splits, q.device)
+        workspace = decode_workspace(q.shape[0], q.shape[1], q.shape[2], num_splits, q.device,
+                                     window=k_recent is not None and k_recent.shape[2] > 0)
     p = decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse, seq_lens, num_splits,
-                      softmax_scale, workspace)
+                      softmax_scale, workspace, kv_format, k_recent, v_recent, recent_lens)
     st = load().fa_decode_kvq(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_decode_kvq", fa_last_error())
+
+
+def kv_append_params(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=None,
+                     kv_format=None) -> FaKvAppendParams:
+    """fa_kv_append_params for new rows k_new/v_new [B,H,T,d] (bf16 or fp16),
+    caches [B,H,L,d] and scales [B,H,L]; positions [B] int32 or None."""
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("k_scale", k_scale), ("v_scale", v_scale)):
+        _require_dense_d(n, t)
+    if k_new.stride() != v_new.stride() or k_cache.stride() != v_cache.stride() \
+            or k_scale.stride() != v_scale.stride():
+        raise ValueError("k and v tensors of each kind must have identical strides")
+    B, H, T, d = k_new.shape
+    p = FaKvAppendParams()
+    p.k_new, p.v_new = _ptr(k_new), _ptr(v_new)
+    p.k_cache, p.v_cache = _ptr(k_cache), _ptr(v_cache)
+    p.k_scale, p.v_scale = _ptr(k_scale), _ptr(v_scale)
+    p.positions = _ptr(positions)
+    p.in_dtype = _dtype_code(k_new)
+    p.kv_format = _kv_format(k_cache, kv_format)
+    p.B, p.H, p.T, p.L, p.d = B, H, T, k_cache.shape[2], d
+    p.new_strides = I64x3(*k_new.stride()[:3])
+    p.kv_strides = I64x3(*k_cache.stride()[:3])
+    p.scale_strides = I64x2(*k_scale.stride()[:2])
+    return p
+
+
+def fa_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=None,
+                 kv_format=None, stream=None) -> None:
+    """Enqueue the quantise-on-append of new key/value rows into the cache."""
+    p = kv_append_params(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions, kv_format)
+    st = load().fa_kv_append(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_kv_append", fa_last_error())

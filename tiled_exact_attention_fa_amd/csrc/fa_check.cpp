@@ -127,7 +127,7 @@ extern "C" size_t fa_decode_workspace_size(int32_t B, int32_t Hq, int32_t d, int
 extern "C" int fa_check_decode_params(const fa_decode_params *p) {
   fa_clear_error();
   if (p == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "params is NULL");
-  if (p->kv_format != FA_KV_INT8_TOKHEAD_F16SCALE)
+  if (p->kv_format != FA_KV_INT8_TOKHEAD_F16SCALE && p->kv_format != FA_KV_FP8_E4M3_TOKHEAD_F16SCALE)
     return fa_set_error(FA_ERR_UNSUPPORTED, "kv_format %d not supported", p->kv_format);
   if (p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->L < 0 || p->d <= 0)
     return fa_set_error(FA_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d L=%d d=%d", p->B, p->Hq, p->Hkv,
@@ -163,9 +163,43 @@ extern "C" int fa_check_decode_params(const fa_decode_params *p) {
   }
   if (p->lse != nullptr && (p->lse_strides[0] < 0 || p->lse_strides[1] < 0))
     return fa_set_error(FA_ERR_INVALID_ARG, "lse strides must be >= 0");
-  const size_t need = fa_decode_workspace_size(p->B, p->Hq, p->d, p->num_splits);
+  if (p->W < 0) return fa_set_error(FA_ERR_INVALID_ARG, "window length W=%d is negative", p->W);
+  if (p->W > 0) {
+    if ((st = check_tensor("k_recent", p->k_recent, p->recent_strides, 3, p->W, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("v_recent", p->v_recent, p->recent_strides, 3, p->W, p->d, 2)) != FA_OK) return st;
+  }
+  // the window's partial takes one more slot of the workspace
+  const size_t need = fa_decode_workspace_size(p->B, p->Hq, p->d, p->num_splits + (p->W > 0 ? 1 : 0));
   if (p->workspace == nullptr || p->workspace_bytes < need)
     return fa_set_error(FA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", p->workspace_bytes, need);
   if (!aligned16(p->workspace)) return fa_set_error(FA_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  return FA_OK;
+}
+
+extern "C" int fa_check_kv_append_params(const fa_kv_append_params *p) {
+  fa_clear_error();
+  if (p == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "params is NULL");
+  if (p->kv_format != FA_KV_INT8_TOKHEAD_F16SCALE && p->kv_format != FA_KV_FP8_E4M3_TOKHEAD_F16SCALE)
+    return fa_set_error(FA_ERR_UNSUPPORTED, "kv_format %d not supported", p->kv_format);
+  if (p->in_dtype != FA_BF16 && p->in_dtype != FA_F16)
+    return fa_set_error(FA_ERR_UNSUPPORTED, "append input dtype %d not supported (bf16 or fp16)", p->in_dtype);
+  if (p->B < 0 || p->H <= 0 || p->T < 0 || p->L < 0 || p->d <= 0)
+    return fa_set_error(FA_ERR_INVALID_ARG, "bad sizes B=%d H=%d T=%d L=%d d=%d", p->B, p->H, p->T, p->L, p->d);
+  if (p->d != 128) return fa_set_error(FA_ERR_UNSUPPORTED, "append head dim %d not supported (128)", p->d);
+  if (static_cast<int64_t>(p->B) * p->H * p->T >= (int64_t(1) << 31))
+    return fa_set_error(FA_ERR_UNSUPPORTED, "B*H*T rows exceed 2^31");
+  if (p->B == 0 || p->T == 0 || p->L == 0) return FA_OK;  // nothing can be written
+  int st;
+  if ((st = check_tensor("k_new", p->k_new, p->new_strides, 3, p->T, p->d, 2)) != FA_OK) return st;
+  if ((st = check_tensor("v_new", p->v_new, p->new_strides, 3, p->T, p->d, 2)) != FA_OK) return st;
+  if ((st = check_tensor("k_cache", p->k_cache, p->kv_strides, 3, p->L, p->d, 1)) != FA_OK) return st;
+  if ((st = check_tensor("v_cache", p->v_cache, p->kv_strides, 3, p->L, p->d, 1)) != FA_OK) return st;
+  for (const void *sp : {static_cast<const void *>(p->k_scale), static_cast<const void *>(p->v_scale)}) {
+    if (sp == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "k_scale/v_scale is NULL");
+    if ((reinterpret_cast<uintptr_t>(sp) & 1u) != 0)
+      return fa_set_error(FA_ERR_ALIGNMENT, "k_scale/v_scale not 2-byte aligned");
+  }
+  for (int i = 0; i < 2; ++i)
+    if (p->scale_strides[i] < 0) return fa_set_error(FA_ERR_INVALID_ARG, "scale stride %d is negative", i);
   return FA_OK;
 }

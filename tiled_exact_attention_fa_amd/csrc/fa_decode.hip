@@ -1,12 +1,14 @@
-// One-token decode over an int8 KV cache with per-token-per-head fp16 scales,
-// split over the cache length and merged by log-sum-exp.
+// One-token decode over an int8 or fp8-e4m3 KV cache with per-token-per-head
+// fp16 scales, split over the cache length and merged by log-sum-exp, with an
+// optional residual window of recent bf16 tokens.
 //
 // What is computed (KV-cache quantisation overview, section 1 "decode step" and
-// section 3 "read path"; FlashAttention interview canvas, panel 1 "online
-// softmax key state"): for each sequence b and query head h, the new query
-// attends to the first seq_len[b] cached tokens of cache head h / G, whose keys
-// and values are code * scale.  Decode reads every cached byte once per step
-// and so is bound by HBM bandwidth (same overview, section 2).
+// section 3 "read path" and "residual window"; FlashAttention interview canvas,
+// panel 1 "online softmax key state"): for each sequence b and query head h,
+// the new query attends to the first seq_len[b] cached tokens of cache head
+// h / G, whose keys and values are code * scale, together with the first
+// recent_len[b] tokens of the bf16 window.  Decode reads every cached byte once
+// per step and so is bound by HBM bandwidth (same overview, section 2).
 //
 // MI355X design.
 //   * Kernel 1 (decode_split_kernel): one workgroup per (batch, cache head,
@@ -17,9 +19,10 @@
 //     no barrier, and the four partial states are merged through LDS at the end.
 //   * The dequantisation is fused into the tile load and folded into the math:
 //     int8 codes become exact fp16 values with two byte permutes and a packed
-//     subtract (1024 + u in fp16 is 0x6400 | u), the key scale multiplies the
-//     score, and the value scale multiplies the probability before it is
-//     rounded, so no dequantised tile is ever stored.
+//     subtract (1024 + u in fp16 is 0x6400 | u); E4M3FN codes (every one of
+//     them exact in fp16) go through the packed fp8 -> fp16 conversion.  The
+//     key scale multiplies the score, and the value scale multiplies the
+//     probability before it is rounded, so no dequantised tile is ever stored.
 //   * S^T = K Q^T and O^T = V^T P^T run on 16x16x32 fp16 MFMA.  The value
 //     operand needs 8 tokens of one head-dim column per lane; lanes load 8
 //     bytes of each token row and the byte permutes of the fp16 conversion
@@ -32,6 +35,14 @@
 //     range, so they neither overflow nor lose range in fp16 (probabilities
 //     reach 2^8 under the lazy running max, see kRescaleSlack).  Both factors are
 //     undone in fp32.
+//   * The residual window rides in the same launch: when it is used, the
+//     first B * Hkv workgroups of the grid (dispatched first, so they overlap
+//     the cache stream rather than trail it) each take the window of one
+//     (batch, cache head).  Its tokens are few and unquantised, so this path
+//     is plain fp32 arithmetic: a lane scores one token against all G query
+//     rows, and the probabilities are broadcast lane by lane into the P V
+//     update, each lane owning two head-dim columns.  Its partial goes to one
+//     more workspace slot.
 //   * Kernel 2 (decode_combine_kernel) merges the splits of one (batch, head):
 //     with M = max_s lse_s and w_s = 2^(lse_s - M), LSE = M + log2 sum_s w_s and
 //     O = sum_s w_s O_s / sum_s w_s, in the log2 domain; it writes bf16 O and
@@ -58,6 +69,13 @@ struct DecodeArgs {
   float *lse;
   float *ws_o;  // [split][B][Hq][d] normalised partial outputs
   float *ws_l;  // [split][B][Hq]   partial log2-sum-exp (log2 units)
+  const void *kr;        // residual window keys [B][Hkv][W][d] bf16, or null
+  const void *vr;        // residual window values
+  const int *rlens;      // [B] window tokens attended, or null for W
+  int W;                 // window capacity (0 = no window)
+  int win_blocks;        // B * Hkv when the window is used, else 0
+  int nslots;            // partial slots: nsplit, plus one for the window
+  long long r_sb, r_sh, r_st;
   int B, Hq, Hkv, G, L, nsplit, chunk;
   long long q_sb, q_sh, kv_sb, kv_sh, sc_sb, sc_sh, o_sb, o_sh, lse_sb, lse_sh;
   unsigned kv_ss;   // token stride in bytes
@@ -98,6 +116,20 @@ __device__ __forceinline__ void i8_pair_transpose(unsigned a, unsigned b, unsign
   out[3] = unbias(perm(kMagic, m23, 0x04030402u));
 }
 
+// Four E4M3FN codes -> two dwords of exact fp16 pairs (d0,d1) and (d2,d3).
+__device__ __forceinline__ void f8x4_to_f16(unsigned w, unsigned &lo, unsigned &hi) {
+  lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// E4M3FN counterpart of i8_pair_transpose.
+__device__ __forceinline__ void f8_pair_transpose(unsigned a, unsigned b, unsigned out[4]) {
+  const unsigned m01 = perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const unsigned m23 = perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  f8x4_to_f16(m01, out[0], out[1]);
+  f8x4_to_f16(m23, out[2], out[3]);
+}
+
 // Exponent E with x = m * 2^E, m in [0.5, 1); 0 for x == 0.
 __device__ __forceinline__ int exp_of(float x) {
   int e;
@@ -130,11 +162,153 @@ struct TileRegs {
   u32x2 vs[2];     // 4 fp16 value scales per token block
 };
 
-template <bool SCVEC>
+// Merges the four wavefront partials in s_o / s_l into partial slot `slot`
+// of the workspace: with M the largest wavefront lse2, lse2 = M + log2 sum 2^(lse2_w - M)
+// and O = sum 2^(lse2_w - lse2) O_w.  Called by the whole workgroup after a barrier.
+__device__ __forceinline__ void merge_waves_to_slot(const DecodeArgs &a, const float (*s_o)[FA_DECODE_MAX_GROUP][kD],
+                                                    const float (*s_l)[FA_DECODE_MAX_GROUP], int slot, int b, int kvh) {
+  const int G = a.G;
+  for (int idx = threadIdx.x; idx < G * kD; idx += kDecodeThreads) {
+    const int qn = idx / kD, d = idx % kD;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_l[w][qn]);
+    float lse2 = neg_inf(), o = 0.f;
+    if (M != neg_inf()) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) tot += fast_exp2(s_l[w][qn] - M);
+      lse2 = M + __log2f(tot);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o += fast_exp2(s_l[w][qn] - lse2) * s_o[w][qn][d];
+    }
+    const long long row = (static_cast<long long>(slot) * a.B + b) * a.Hq + kvh * G + qn;
+    a.ws_o[row * kD + d] = o;
+    if (d == 0) a.ws_l[row] = lse2;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// The residual window of one (batch, cache head): up to W bf16 tokens, cut
+// into four contiguous quarters, one per wavefront, walked 64 tokens at a time.
+// Lane l scores token t0 + l against every query row (fp32 dot products, the
+// query rows read from LDS as broadcasts); the per-row running max and sum are
+// wave-uniform; lane l accumulates head-dim columns 2l and 2l + 1.
+__device__ void decode_window(const DecodeArgs &a, int b, int kvh, float (*s_o)[FA_DECODE_MAX_GROUP][kD],
+                              float (*s_l)[FA_DECODE_MAX_GROUP]) {
+  __shared__ float s_q[FA_DECODE_MAX_GROUP][kD];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.G;
+  for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
+    const int qn = idx / kD, d = idx % kD;
+    s_q[qn][d] = static_cast<float>(static_cast<const __bf16 *>(a.q)[b * a.q_sb + (kvh * G + qn) * a.q_sh + d]);
+  }
+  __syncthreads();
+  int r = a.rlens != nullptr ? a.rlens[b] : a.W;
+  r = min(max(r, 0), a.W);
+  const int quarter = ((r + 3) / 4 + 63) / 64 * 64;
+  const int w0 = min(wave * quarter, r);
+  const int w1 = min(w0 + quarter, r);
+  const __bf16 *kbase = static_cast<const __bf16 *>(a.kr) + b * a.r_sb + kvh * a.r_sh;
+  const __bf16 *vbase = static_cast<const __bf16 *>(a.vr) + b * a.r_sb + kvh * a.r_sh;
+
+  float m[FA_DECODE_MAX_GROUP], l[FA_DECODE_MAX_GROUP], o0[FA_DECODE_MAX_GROUP], o1[FA_DECODE_MAX_GROUP];
+#pragma unroll
+  for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
+    m[n] = neg_inf();
+    l[n] = 0.f;
+    o0[n] = 0.f;
+    o1[n] = 0.f;
+  }
+  for (int t0 = w0; t0 < w1; t0 += 64) {
+    const int t = t0 + lane;
+    const bool ok = t < w1;
+    float sc[FA_DECODE_MAX_GROUP];
+#pragma unroll
+    for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) sc[n] = 0.f;
+    const __bf16 *krow = kbase + static_cast<long long>(ok ? t : w0) * a.r_st;
+#pragma unroll 2
+    for (int c8 = 0; c8 < kD / 8; ++c8) {
+      const u32x4 raw = ok ? *reinterpret_cast<const u32x4 *>(krow + 8 * c8) : u32x4{0u, 0u, 0u, 0u};
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, raw);
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = static_cast<float>(kv[e]);
+#pragma unroll
+      for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
+        if (n < G) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[n] = fmaf(s_q[n][8 * c8 + e], kf[e], sc[n]);
+        }
+      }
+    }
+    const int nt = min(64, w1 - t0);
+    float p[FA_DECODE_MAX_GROUP];
+#pragma unroll
+    for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
+      p[n] = 0.f;
+      if (n < G) {
+        const float s2 = ok ? sc[n] * a.c : neg_inf();  // log2 units
+        const float m_new = fmaxf(m[n], wave_max(s2));  // finite: lane 0 holds a token
+        const float alpha = fast_exp2(m[n] - m_new);     // 0 while m is -inf
+        p[n] = fast_exp2(s2 - m_new);                    // 0 for lanes past the range
+        l[n] = l[n] * alpha + wave_sum(p[n]);
+        o0[n] *= alpha;
+        o1[n] *= alpha;
+        m[n] = m_new;
+      }
+    }
+    for (int j = 0; j < nt; ++j) {
+      const unsigned vv = *reinterpret_cast<const unsigned *>(vbase + static_cast<long long>(t0 + j) * a.r_st + 2 * lane);
+      const float v0 = __builtin_bit_cast(float, vv << 16);
+      const float v1 = __builtin_bit_cast(float, vv & 0xFFFF0000u);
+#pragma unroll
+      for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
+        if (n < G) {
+          const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[n]), j));
+          o0[n] = fmaf(pj, v0, o0[n]);
+          o1[n] = fmaf(pj, v1, o1[n]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
+    if (n < G) {
+      const float inv = l[n] > 0.f ? 1.f / l[n] : 0.f;
+      s_o[wave][n][2 * lane] = o0[n] * inv;
+      s_o[wave][n][2 * lane + 1] = o1[n] * inv;
+      if (lane == 0) s_l[wave][n] = l[n] > 0.f ? m[n] + __log2f(l[n]) : neg_inf();
+    }
+  }
+  __syncthreads();
+  merge_waves_to_slot(a, s_o, s_l, a.nsplit, b, kvh);
+}
+
+template <bool SCVEC, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
+
+  if (static_cast<int>(blockIdx.x) < a.win_blocks) {  // workgroup-uniform
+    decode_window(a, blockIdx.x / a.Hkv, blockIdx.x % a.Hkv, s_o, s_l);
+    return;
+  }
+  const int bid = blockIdx.x - a.win_blocks;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,9 +316,9 @@ void decode_split_kernel(const DecodeArgs a) {
   const int n = lane & 15;   // query column (S^T, O^T) or row within a 16-row block
   const int g = lane >> 4;   // lane group: reduction slots 8g..8g+7
 
-  const int split = blockIdx.x % a.nsplit;
-  const int kvh = (blockIdx.x / a.nsplit) % a.Hkv;
-  const int b = blockIdx.x / (a.nsplit * a.Hkv);
+  const int split = bid % a.nsplit;
+  const int kvh = (bid / a.nsplit) % a.Hkv;
+  const int b = bid / (a.nsplit * a.Hkv);
   const int G = a.G;
 
   int len = a.seq_lens != nullptr ? a.seq_lens[b] : a.L;
@@ -226,7 +400,14 @@ void decode_split_kernel(const DecodeArgs a) {
   auto load_tile = [&](TileRegs &r, int t0) {
     const int left = w1 - t0;  // tokens of the range from t0 on
     const unsigned kv_rec = left > 0 ? static_cast<unsigned>(left - 1) * ss + kD : 0u;
-    const unsigned sc_rec = left > 0 ? static_cast<unsigned>(left) * 2u : 0u;
+    // The range check of a buffer load is made per dword: a dword that
+    // straddles the end of the range reads as zero in full.  The 8-byte scale
+    // loads therefore get a range rounded up to whole groups of four tokens
+    // (never past the cache slice: L is a multiple of 4 on this path); the
+    // scores of the extra tokens are masked below.  The 2-byte loads take the
+    // exact range.
+    const int sc_tok = SCVEC ? min((left + 3) & ~3, a.L - t0) : left;
+    const unsigned sc_rec = left > 0 ? static_cast<unsigned>(sc_tok) * 2u : 0u;
     const unsigned shift = left > 0 ? static_cast<unsigned>(t0) * ss : 0u;
     const __amdgpu_buffer_rsrc_t tk = make_rsrc(kslice + shift, kv_rec);
     const __amdgpu_buffer_rsrc_t tv = make_rsrc(vslice + shift, kv_rec);
@@ -262,8 +443,13 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int s = 0; s < 4; ++s) {
         const u32x4 raw = r.k[tb][s >> 1];
         unsigned w[4];
-        i8x4_to_f16(raw[2 * (s & 1)], w[0], w[1]);
-        i8x4_to_f16(raw[2 * (s & 1) + 1], w[2], w[3]);
+        if constexpr (FP8) {
+          f8x4_to_f16(raw[2 * (s & 1)], w[0], w[1]);
+          f8x4_to_f16(raw[2 * (s & 1) + 1], w[2], w[3]);
+        } else {
+          i8x4_to_f16(raw[2 * (s & 1)], w[0], w[1]);
+          i8x4_to_f16(raw[2 * (s & 1) + 1], w[2], w[3]);
+        }
         const f16x8 kf = __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
         sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], sacc[tb], 0, 0, 0);
       }
@@ -313,7 +499,8 @@ void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd) {
         unsigned out[4];
-        i8_pair_transpose(r.v[2 * p][hd], r.v[2 * p + 1][hd], out);
+        if constexpr (FP8) f8_pair_transpose(r.v[2 * p][hd], r.v[2 * p + 1][hd], out);
+        else i8_pair_transpose(r.v[2 * p][hd], r.v[2 * p + 1][hd], out);
 #pragma unroll
         for (int k = 0; k < 4; ++k) vt[4 * hd + k][p] = out[k];
       }
@@ -364,51 +551,35 @@ void decode_split_kernel(const DecodeArgs a) {
   __syncthreads();
 
   // ---- merge the four wavefronts into this split's partial ----
-  for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
-    const int qn = idx / kD, d = idx % kD;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_l[w][qn]);
-    float lse2 = neg_inf(), o = 0.f;
-    if (M != neg_inf()) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) tot += fast_exp2(s_l[w][qn] - M);
-      lse2 = M + __log2f(tot);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) o += fast_exp2(s_l[w][qn] - lse2) * s_o[w][qn][d];
-    }
-    const long long row = (static_cast<long long>(split) * a.B + b) * a.Hq + kvh * G + qn;
-    a.ws_o[row * kD + d] = o;
-    if (d == 0) a.ws_l[row] = lse2;
-  }
+  merge_waves_to_slot(a, s_o, s_l, split, b, kvh);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
 void decode_combine_kernel(const DecodeArgs a) {
   // one workgroup per (batch, query head); thread d owns output column d.
-  // Splits are taken 16 at a time with all loads of a group in flight.
+  // Partial slots (the splits, then the window's) are taken 16 at a time with
+  // all loads of a group in flight.
   const int d = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const long long stride = static_cast<long long>(a.B) * a.Hq;
   constexpr int kGroup = 16;
   float M = neg_inf();
-  for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+  for (int s0 = 0; s0 < a.nslots; s0 += kGroup) {
     float l[kGroup];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) l[i] = s0 + i < a.nsplit ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
+    for (int i = 0; i < kGroup; ++i) l[i] = s0 + i < a.nslots ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) M = fmaxf(M, l[i]);
   }
   float lse2 = neg_inf(), o = 0.f;
   if (M != neg_inf()) {
     float tot = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+    for (int s0 = 0; s0 < a.nslots; s0 += kGroup) {
       float l[kGroup], v[kGroup];
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        const bool ok = s0 + i < a.nsplit;
+        const bool ok = s0 + i < a.nslots;
         l[i] = ok ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
         v[i] = ok ? a.ws_o[((s0 + i) * stride + bh) * kD + d] : 0.f;
       }
@@ -462,18 +633,34 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   a.kv_ss = p->L > 1 ? static_cast<unsigned>(p->kv_strides[2]) : 0u;
   a.kv_ext = p->L > 0 ? static_cast<unsigned>((static_cast<long long>(p->L - 1) * p->kv_strides[2] + p->d)) : 0u;
   a.sc_ext = static_cast<unsigned>(p->L) * 2u;
+  // 8-byte scale loads need 16-byte aligned scale rows and a slice of whole
+  // 4-token groups, so that no load straddles the end of the slice
   a.sc_vec = (reinterpret_cast<uintptr_t>(p->k_scale) % 16 == 0 && reinterpret_cast<uintptr_t>(p->v_scale) % 16 == 0 &&
-              (p->scale_strides[0] * 2) % 16 == 0 && (p->scale_strides[1] * 2) % 16 == 0)
+              (p->scale_strides[0] * 2) % 16 == 0 && (p->scale_strides[1] * 2) % 16 == 0 && p->L % 4 == 0)
                  ? 1 : 0;
   a.c = p->softmax_scale * 1.4426950408889634f;
-  const size_t rows = static_cast<size_t>(p->num_splits) * p->B * p->Hq;
+  const bool window = p->W > 0;
+  a.kr = window ? p->k_recent : nullptr;
+  a.vr = window ? p->v_recent : nullptr;
+  a.rlens = window ? p->recent_lens : nullptr;
+  a.W = window ? p->W : 0;
+  a.r_sb = p->recent_strides[0];
+  a.r_sh = p->recent_strides[1];
+  a.r_st = p->recent_strides[2];
+  a.win_blocks = window ? p->B * p->Hkv : 0;
+  a.nslots = p->num_splits + (window ? 1 : 0);
+  const size_t rows = static_cast<size_t>(a.nslots) * p->B * p->Hq;
   a.ws_o = static_cast<float *>(p->workspace);
   a.ws_l = reinterpret_cast<float *>(static_cast<char *>(p->workspace) +
                                      ((rows * kD * sizeof(float) + 255) & ~size_t(255)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
-  if (a.sc_vec) hipLaunchKernelGGL(decode_split_kernel<true>, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
-  else hipLaunchKernelGGL(decode_split_kernel<false>, dim3(grid1), dim3(kDecodeThreads), 0, s, a);
+  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B + static_cast<unsigned>(a.win_blocks);
+  const dim3 g1(grid1), b1(kDecodeThreads);
+  const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
+  if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);
+  else if (a.sc_vec) hipLaunchKernelGGL((decode_split_kernel<true, false>), g1, b1, 0, s, a);
+  else if (fp8) hipLaunchKernelGGL((decode_split_kernel<false, true>), g1, b1, 0, s, a);
+  else hipLaunchKernelGGL((decode_split_kernel<false, false>), g1, b1, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode split launch: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(p->B) * p->Hq), dim3(kD), 0, s, a);
