@@ -35,14 +35,14 @@
 //     range, so they neither overflow nor lose range in fp16 (probabilities
 //     reach 2^8 under the lazy running max, see kRescaleSlack).  Both factors are
 //     undone in fp32.
-//   * The residual window rides in the same launch: when it is used, the
-//     first B * Hkv workgroups of the grid (dispatched first, so they overlap
-//     the cache stream rather than trail it) each take the window of one
+//   * The residual window (decode_window_kernel, launched before the split
+//     kernel when it is used) gives one workgroup to the window of each
 //     (batch, cache head).  Its tokens are few and unquantised, so this path
 //     is plain fp32 arithmetic: a lane scores one token against all G query
 //     rows, and the probabilities are broadcast lane by lane into the P V
 //     update, each lane owning two head-dim columns.  Its partial goes to one
-//     more workspace slot.
+//     more workspace slot.  A kernel of its own keeps the split kernel's
+//     register allocation untouched.
 //   * Kernel 2 (decode_combine_kernel) merges the splits of one (batch, head):
 //     with M = max_s lse_s and w_s = 2^(lse_s - M), LSE = M + log2 sum_s w_s and
 //     O = sum_s w_s O_s / sum_s w_s, in the log2 domain; it writes bf16 O and
@@ -73,7 +73,6 @@ struct DecodeArgs {
   const void *vr;        // residual window values
   const int *rlens;      // [B] window tokens attended, or null for W
   int W;                 // window capacity (0 = no window)
-  int win_blocks;        // B * Hkv when the window is used, else 0
   int nslots;            // partial slots: nsplit, plus one for the window
   long long r_sb, r_sh, r_st;
   int B, Hq, Hkv, G, L, nsplit, chunk;
@@ -188,111 +187,124 @@ __device__ __forceinline__ void merge_waves_to_slot(const DecodeArgs &a, const f
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 // The residual window of one (batch, cache head): up to W bf16 tokens, cut
-// into four contiguous quarters, one per wavefront, walked 64 tokens at a time.
-// Lane l scores token t0 + l against every query row (fp32 dot products, the
-// query rows read from LDS as broadcasts); the per-row running max and sum are
-// wave-uniform; lane l accumulates head-dim columns 2l and 2l + 1.
-__device__ void decode_window(const DecodeArgs &a, int b, int kvh, float (*s_o)[FA_DECODE_MAX_GROUP][kD],
-                              float (*s_l)[FA_DECODE_MAX_GROUP]) {
-  __shared__ float s_q[FA_DECODE_MAX_GROUP][kD];
+// into four contiguous quarters, one per wavefront, walked in 32-token tiles
+// with the split kernel's matrix-core layout on bf16 operands: S^T = K Q^T as
+// 16x16x32 bf16 MFMAs (lane (n, g) holds key and query elements 32g + 8s + j,
+// so both operands are plain 16-byte row loads), the probabilities rounded to
+// bf16 straight from the S^T accumulator into the B operand of O^T = V^T P^T,
+// and V^T built from 16-byte row loads with 16-bit permutes (block j of the
+// output holds head-dim column 8m + j in row m).  The running max is exact
+// (no lazy slack), so probabilities stay <= 1.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void decode_window_kernel(const DecodeArgs a) {
+  __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
+  __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
+  const int b = blockIdx.x / a.Hkv;
+  const int kvh = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
   const int G = a.G;
-  for (int idx = tid; idx < G * kD; idx += kDecodeThreads) {
-    const int qn = idx / kD, d = idx % kD;
-    s_q[qn][d] = static_cast<float>(static_cast<const __bf16 *>(a.q)[b * a.q_sb + (kvh * G + qn) * a.q_sh + d]);
-  }
-  __syncthreads();
+
   int r = a.rlens != nullptr ? a.rlens[b] : a.W;
   r = min(max(r, 0), a.W);
-  const int quarter = ((r + 3) / 4 + 63) / 64 * 64;
+  const int quarter = ((r + 3) / 4 + kTile - 1) / kTile * kTile;
   const int w0 = min(wave * quarter, r);
   const int w1 = min(w0 + quarter, r);
-  const __bf16 *kbase = static_cast<const __bf16 *>(a.kr) + b * a.r_sb + kvh * a.r_sh;
-  const __bf16 *vbase = static_cast<const __bf16 *>(a.vr) + b * a.r_sb + kvh * a.r_sh;
 
-  float m[FA_DECODE_MAX_GROUP], l[FA_DECODE_MAX_GROUP], o0[FA_DECODE_MAX_GROUP], o1[FA_DECODE_MAX_GROUP];
+  // query column n (zero past G): elements 32g + 8s .. 32g + 8s + 7
+  bf16x8 qf[4];
+  {
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + b * a.q_sb + (kvh * G + (n < G ? n : 0)) * a.q_sh;
 #pragma unroll
-  for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
-    m[n] = neg_inf();
-    l[n] = 0.f;
-    o0[n] = 0.f;
-    o1[n] = 0.f;
-  }
-  for (int t0 = w0; t0 < w1; t0 += 64) {
-    const int t = t0 + lane;
-    const bool ok = t < w1;
-    float sc[FA_DECODE_MAX_GROUP];
-#pragma unroll
-    for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) sc[n] = 0.f;
-    const __bf16 *krow = kbase + static_cast<long long>(ok ? t : w0) * a.r_st;
-#pragma unroll 2
-    for (int c8 = 0; c8 < kD / 8; ++c8) {
-      const u32x4 raw = ok ? *reinterpret_cast<const u32x4 *>(krow + 8 * c8) : u32x4{0u, 0u, 0u, 0u};
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, raw);
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = static_cast<float>(kv[e]);
-#pragma unroll
-      for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
-        if (n < G) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[n] = fmaf(s_q[n][8 * c8 + e], kf[e], sc[n]);
-        }
-      }
-    }
-    const int nt = min(64, w1 - t0);
-    float p[FA_DECODE_MAX_GROUP];
-#pragma unroll
-    for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
-      p[n] = 0.f;
-      if (n < G) {
-        const float s2 = ok ? sc[n] * a.c : neg_inf();  // log2 units
-        const float m_new = fmaxf(m[n], wave_max(s2));  // finite: lane 0 holds a token
-        const float alpha = fast_exp2(m[n] - m_new);     // 0 while m is -inf
-        p[n] = fast_exp2(s2 - m_new);                    // 0 for lanes past the range
-        l[n] = l[n] * alpha + wave_sum(p[n]);
-        o0[n] *= alpha;
-        o1[n] *= alpha;
-        m[n] = m_new;
-      }
-    }
-    for (int j = 0; j < nt; ++j) {
-      const unsigned vv = *reinterpret_cast<const unsigned *>(vbase + static_cast<long long>(t0 + j) * a.r_st + 2 * lane);
-      const float v0 = __builtin_bit_cast(float, vv << 16);
-      const float v1 = __builtin_bit_cast(float, vv & 0xFFFF0000u);
-#pragma unroll
-      for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
-        if (n < G) {
-          const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[n]), j));
-          o0[n] = fmaf(pj, v0, o0[n]);
-          o1[n] = fmaf(pj, v1, o1[n]);
-        }
-      }
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const u32x4 raw = n < G ? *reinterpret_cast<const u32x4 *>(qrow + 32 * g + 8 * s4) : u32x4{0u, 0u, 0u, 0u};
+      qf[s4] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  const char *kbase = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.kr) + b * a.r_sb + kvh * a.r_sh);
+  const char *vbase = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.vr) + b * a.r_sb + kvh * a.r_sh);
+  const unsigned rs = static_cast<unsigned>(a.r_st) * 2u;  // row stride, bytes
+
+  float m_run = neg_inf();
+  float l_run = 0.f;
+  f32x4 oacc[8];
 #pragma unroll
-  for (int n = 0; n < FA_DECODE_MAX_GROUP; ++n) {
-    if (n < G) {
-      const float inv = l[n] > 0.f ? 1.f / l[n] : 0.f;
-      s_o[wave][n][2 * lane] = o0[n] * inv;
-      s_o[wave][n][2 * lane + 1] = o1[n] * inv;
-      if (lane == 0) s_l[wave][n] = l[n] > 0.f ? m[n] + __log2f(l[n]) : neg_inf();
+  for (int j = 0; j < 8; ++j) oacc[j] = f32x4{};
+
+  for (int t0 = w0; t0 < w1; t0 += kTile) {
+    // rows past the range read as zero through a buffer range that ends at
+    // the wavefront's last token
+    const int left = w1 - t0;
+    const __amdgpu_buffer_rsrc_t tk = make_rsrc(kbase + static_cast<size_t>(t0) * rs, (left - 1) * rs + 2u * kD);
+    const __amdgpu_buffer_rsrc_t tv = make_rsrc(vbase + static_cast<size_t>(t0) * rs, (left - 1) * rs + 2u * kD);
+    u32x4 kf[2][4], vrow[8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) kf[tb][s4] = buf_load16(tk, (16u * tb + n) * rs + 2u * (32 * g + 8 * s4));
+#pragma unroll
+    for (int e = 0; e < 8; ++e)  // token 4g + (e & 3) + 16 (e >> 2), columns 8n .. 8n + 7
+      vrow[e] = buf_load16(tv, (4u * g + (e & 3) + 16u * (e >> 2)) * rs + 16u * n);
+
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sacc[tb] = f32x4{};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[tb][s4]), qf[s4], sacc[tb], 0, 0, 0);
     }
+    float sc[8];
+    float mx = neg_inf();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * tb + 4 * g + i;
+        const float s2 = tok < w1 ? sacc[tb][i] * a.c : neg_inf();
+        sc[4 * tb + i] = s2;
+        mx = fmaxf(mx, s2);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);      // finite: the tile holds a token
+    const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
+    float lsum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(sc[e] - m_new);
+      lsum += pe;
+      pf[e] = static_cast<__bf16>(pe);
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // column 8n + j of the 8 tokens: 16-bit half (j & 1) of dword j / 2
+      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 w;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) w[p2] = perm(vrow[2 * p2 + 1][j >> 1], vrow[2 * p2][j >> 1], sel);
+      oacc[j] = oacc[j] * alpha;
+      oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pf, oacc[j], 0, 0, 0);
+    }
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (n < G) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[wave][n][32 * g + 8 * i + j] = oacc[j][i] * inv;
+    if (g == 0) s_l[wave][n] = l_tot > 0.f ? m_run + __log2f(l_tot) : neg_inf();
   }
   __syncthreads();
   merge_waves_to_slot(a, s_o, s_l, a.nsplit, b, kvh);
@@ -304,11 +316,7 @@ void decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
 
-  if (static_cast<int>(blockIdx.x) < a.win_blocks) {  // workgroup-uniform
-    decode_window(a, blockIdx.x / a.Hkv, blockIdx.x % a.Hkv, s_o, s_l);
-    return;
-  }
-  const int bid = blockIdx.x - a.win_blocks;
+  const int bid = blockIdx.x;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -647,14 +655,18 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   a.r_sb = p->recent_strides[0];
   a.r_sh = p->recent_strides[1];
   a.r_st = p->recent_strides[2];
-  a.win_blocks = window ? p->B * p->Hkv : 0;
   a.nslots = p->num_splits + (window ? 1 : 0);
   const size_t rows = static_cast<size_t>(a.nslots) * p->B * p->Hq;
   a.ws_o = static_cast<float *>(p->workspace);
   a.ws_l = reinterpret_cast<float *>(static_cast<char *>(p->workspace) +
                                      ((rows * kD * sizeof(float) + 255) & ~size_t(255)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B + static_cast<unsigned>(a.win_blocks);
+  if (window) {
+    hipLaunchKernelGGL(decode_window_kernel, dim3(static_cast<unsigned>(p->B) * p->Hkv), dim3(kDecodeThreads), 0, s, a);
+    const hipError_t ew = hipGetLastError();
+    if (ew != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode window launch: %s", hipGetErrorString(ew));
+  }
+  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
   const dim3 g1(grid1), b1(kDecodeThreads);
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
   if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);

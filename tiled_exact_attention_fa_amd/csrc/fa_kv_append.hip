@@ -12,11 +12,13 @@
 // positions[b] + t; slots outside [0, L) are skipped.
 //
 // MI355X design.  The work is a pure stream (256 bytes read, 130 written per
-// row, no reuse), so it is shaped for HBM: a row is one 16-lane group, each
-// lane moving one 16-byte chunk in and one 8-byte chunk out, so a wavefront
-// reads four whole rows with fully coalesced 128-bit loads.  The same group
-// handles the key row and the value row of its (batch, head, token), which
-// keeps two independent loads in flight per lane.  The absmax is reduced over
+// row, no reuse), so it is shaped for HBM: a row is handled by one 16-lane
+// group, each lane moving one 16-byte chunk in and one 8-byte chunk out, so a
+// wavefront covers whole rows with fully coalesced 128-bit loads.  A group
+// takes four consecutive rows, and with them the key row and the value row of
+// each (batch, head, token): eight independent 16-byte loads are in flight per
+// lane before the first is used, and the grid has a quarter as many
+// workgroups as rows / 16.  The absmax is reduced over
 // the group with lane exchanges only (no LDS, no barrier).  fp8 codes come from
 // the hardware's packed E4M3FN conversion (round to nearest even), int8 codes
 // from rint; the division stays a true IEEE division because the code is an
@@ -42,7 +44,9 @@ struct AppendArgs {
 };
 
 constexpr int kAppendThreads = 256;
-constexpr int kRowsPerBlock = kAppendThreads / 16;
+constexpr int kGroupsPerBlock = kAppendThreads / 16;
+constexpr int kRowsPerGroup = 4;
+constexpr int kRowsPerBlock = kGroupsPerBlock * kRowsPerGroup;
 
 // Eight input values of one 16-byte chunk, widened exactly to fp32.
 template <bool BF16> __device__ __forceinline__ void widen8(const u32x4 w, float x[8]) {
@@ -105,37 +109,51 @@ template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(const AppendArgs a) {
   const int tid = threadIdx.x;
   const int c = tid & 15;  // 8-element chunk of the row
-  // rows < 2^31 (checked on the host), so 32-bit unsigned index math is exact
-  const unsigned r = blockIdx.x * static_cast<unsigned>(kRowsPerBlock) + static_cast<unsigned>(tid >> 4);
+  // rows < 2^31 (checked on the host), so 32-bit unsigned index math is exact;
+  // the group takes kRowsPerGroup consecutive rows (consecutive tokens, so a
+  // contiguous stretch of the input and of the cache)
+  const unsigned r0 = (blockIdx.x * static_cast<unsigned>(kGroupsPerBlock) + static_cast<unsigned>(tid >> 4)) *
+                      static_cast<unsigned>(kRowsPerGroup);
   // every lane stays live through the group exchange; only loads and stores
   // are predicated
-  bool write = false;
-  long long in_off = 0, c_off = 0, s_off = 0;
-  if (r < a.rows) {
-    const int t = static_cast<int>(r % static_cast<unsigned>(a.T));
-    const unsigned bh = r / static_cast<unsigned>(a.T);
-    const int h = static_cast<int>(bh % static_cast<unsigned>(a.H));
-    const long long b = bh / static_cast<unsigned>(a.H);
-    const long long slot = static_cast<long long>(a.positions != nullptr ? a.positions[b] : 0) + t;
-    write = slot >= 0 && slot < a.L;
-    in_off = b * a.n_sb + h * a.n_sh + t * a.n_st + 8 * c;
-    c_off = b * a.c_sb + h * a.c_sh + slot * a.c_st + 8 * c;
-    s_off = b * a.s_sb + h * a.s_sh + slot;
+  bool write[kRowsPerGroup];
+  long long c_off[kRowsPerGroup], s_off[kRowsPerGroup];
+  u32x4 kx[kRowsPerGroup], vx[kRowsPerGroup];
+#pragma unroll
+  for (int i = 0; i < kRowsPerGroup; ++i) {
+    const unsigned r = r0 + i;
+    write[i] = false;
+    c_off[i] = s_off[i] = 0;
+    long long in_off = 0;
+    if (r < a.rows) {
+      const int t = static_cast<int>(r % static_cast<unsigned>(a.T));
+      const unsigned bh = r / static_cast<unsigned>(a.T);
+      const int h = static_cast<int>(bh % static_cast<unsigned>(a.H));
+      const long long b = bh / static_cast<unsigned>(a.H);
+      const long long slot = static_cast<long long>(a.positions != nullptr ? a.positions[b] : 0) + t;
+      write[i] = slot >= 0 && slot < a.L;
+      in_off = b * a.n_sb + h * a.n_sh + t * a.n_st + 8 * c;
+      c_off[i] = b * a.c_sb + h * a.c_sh + slot * a.c_st + 8 * c;
+      s_off[i] = b * a.s_sb + h * a.s_sh + slot;
+    }
+    kx[i] = vx[i] = u32x4{0u, 0u, 0u, 0u};
+    if (write[i]) {  // all loads of the group issued before any is used
+      kx[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const unsigned short *>(a.k_new) + in_off));
+      vx[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const unsigned short *>(a.v_new) + in_off));
+    }
   }
-  u32x4 kx{0u, 0u, 0u, 0u}, vx{0u, 0u, 0u, 0u};
-  if (write) {
-    kx = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const unsigned short *>(a.k_new) + in_off));
-    vx = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const unsigned short *>(a.v_new) + in_off));
-  }
-  _Float16 ks, vs;
-  const u32x2 kq = quantise8<BF16, FP8>(kx, ks);
-  const u32x2 vq = quantise8<BF16, FP8>(vx, vs);
-  if (write) {
-    *reinterpret_cast<u32x2 *>(a.k_cache + c_off) = kq;
-    *reinterpret_cast<u32x2 *>(a.v_cache + c_off) = vq;
-    if (c == 0) {
-      a.k_scale[s_off] = ks;
-      a.v_scale[s_off] = vs;
+#pragma unroll
+  for (int i = 0; i < kRowsPerGroup; ++i) {
+    _Float16 ks, vs;
+    const u32x2 kq = quantise8<BF16, FP8>(kx[i], ks);
+    const u32x2 vq = quantise8<BF16, FP8>(vx[i], vs);
+    if (write[i]) {
+      *reinterpret_cast<u32x2 *>(a.k_cache + c_off[i]) = kq;
+      *reinterpret_cast<u32x2 *>(a.v_cache + c_off[i]) = vq;
+      if (c == 0) {
+        a.k_scale[s_off[i]] = ks;
+        a.v_scale[s_off[i]] = vs;
+      }
     }
   }
 }
