@@ -105,6 +105,7 @@ def workload(name):
     return fa_inputs.CONFIGS[name] if name in fa_inputs.CONFIGS else fa_inputs.KV_CONFIGS[name]
 
 
+
 # ---- GPU timing ---------------------------------------------------------------
 
 WARMUP_SECONDS = 0.3
@@ -188,27 +189,45 @@ def _append_runner(cfg, seed=0):
     return run
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources, to tie stored counter readings to a build."""
+# the files that hold each kernel family's device code
+KERNEL_SOURCES = {
+    "fwd16": ["fa_fwd_mfma.hip", "fa_fwd_common.hpp", "fa_device.hpp"],
+    "fwd8": ["fa_fwd_fp8.hip", "fa_fwd_common.hpp", "fa_device.hpp"],
+    "decode": ["fa_decode.hip", "fa_device.hpp"],
+    "append": ["fa_kv_append.hip", "fa_device.hpp"],
+}
+
+
+def kernel_family(cfg) -> str:
+    if isinstance(cfg, fa_inputs.DecodeConfig):
+        return "decode"
+    if isinstance(cfg, fa_inputs.AppendConfig):
+        return "append"
+    return "fwd8" if cfg.dtype == "fp8" else "fwd16"
+
+
+def source_digest(family: str) -> str:
+    """Hash of one kernel family's sources, to tie stored counter readings to
+    the code they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_exact_attention_fa_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in KERNEL_SOURCES[family]:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(name: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+    taken on the current sources of the workload's kernels; else None."""
     path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(workload)
-    if not ent or ent.get("source_digest") != source_digest():
+    ent = data.get(name)
+    if not ent or ent.get("source_digest") != source_digest(kernel_family(workload(name))):
         return None
     return ent.get("bytes_per_launch")
 
@@ -324,7 +343,7 @@ def summarize_pmc(a):
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[a.workload] = {"kernel": a.kernel, "bytes_per_launch": fetch + write, "fetch_bytes": fetch,
                         "write_bytes": write, "algorithmic_bytes": algo, "fetch_scale": f_scale,
-                        "write_scale": w_scale, "source_digest": source_digest()}
+                        "write_scale": w_scale, "source_digest": source_digest(kernel_family(cfg))}
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
     print(f"| {a.workload} | {a.kernel} | {nf} | {wf:.0f} | {ww:.0f} | {f_scale:.4f} | {w_scale:.4f} | "

@@ -37,3 +37,23 @@ def test_gpus_above_one_is_refused():
 
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_kv_workload_bytes():
+    k = fa_inputs.KV_CONFIGS
+    base = bench.decode_bytes(C["decode_int8_b64_gqa32x8_L32768"])
+    assert bench.decode_bytes(k["decode_fp8_b64_gqa32x8_L32768"]) == base  # 1-byte codes either way
+    # the window adds its bf16 keys and values: 2 * B * Hkv * W * d * 2 bytes
+    assert bench.decode_bytes(k["decode_int8_window128_b64_gqa32x8_L32768"]) == base + 2 * 64 * 8 * 128 * 128 * 2
+    a = k["append_int8_b64_h8_t4096"]
+    rows = 64 * 8 * 4096
+    # bf16 rows read (K and V), one code byte per element and a 2-byte scale per row written
+    assert bench.append_bytes(a) == 2 * rows * 256 + 2 * (rows * 128 + rows * 2) == 1619001344
+
+
+def test_counter_digest_follows_each_kernel_family():
+    fams = {n: bench.kernel_family(bench.workload(n)) for n in list(C) + list(fa_inputs.KV_CONFIGS)}
+    assert fams["bf16_b4_h16_s2048_causal"] == "fwd16" and fams["fp8_b8_h16_s4096"] == "fwd8"
+    assert fams["decode_fp8_b64_gqa32x8_L32768"] == "decode" and fams["append_fp8_b64_h8_t4096"] == "append"
+    digests = {f: bench.source_digest(f) for f in bench.KERNEL_SOURCES}
+    assert len(set(digests.values())) == len(digests)
