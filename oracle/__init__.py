@@ -15,13 +15,16 @@ Modules
   attention  numpy float64 two-pass oracle (prefill, decode over a quantised
              cache), plus the pages' own online-softmax recurrence and a
              split-and-merge evaluation used only to pin invariants.
+  backward   float64 gradients of attention (dQ, dK, dV given dO) from the
+             softmax Jacobian, for the recomputing backward.
   brute      pure-Python scalar loops (math.exp / math.fsum) for tiny shapes.
   e4m3       OCP E4M3FN byte decoder written from the format's definition.
   quant      the KV-cache write side: per-token-per-head int8 and E4M3FN
              quantisers (and the E4M3FN encoder), and the append of quantised
              rows into a cache.
 
-Every function has a pin in tests/test_oracle.py or tests/test_oracle_kv.py
+Every function has a pin in tests/test_oracle.py, tests/test_oracle_kv.py or
+tests/test_oracle_bwd.py
 (brute force, closed forms, invariants, library special cases, a hand-derived
 golden example); none of them is "parity unpinned".
 """
@@ -36,6 +39,7 @@ from .attention import (  # noqa: F401
     split_merge_fp64,
     visible_keys,
 )
+from .backward import attention_bwd_fp64  # noqa: F401
 from .brute import attention_brute  # noqa: F401
 from .e4m3 import e4m3_decode  # noqa: F401
 from .quant import e4m3_encode, kv_append_ref, quantize_kv_tokhead  # noqa: F401
