@@ -8,7 +8,8 @@ resident in HBM.  The headline workload is causal bf16 prefill, B=4, H=16,
 S=2048, d=128 with LSE output; its TFLOP/s counts 4*d flops per visible
 (query, key) pair (S*(S+1)/2 pairs per head under the causal mask).  The other
 workloads are timed the same way and reported under "workloads": long-context
-GQA prefill and fp8 prefill in TFLOP/s; int8-KV and fp8-KV split decode, the
+GQA prefill, fp8 prefill and the backward of the two causal bf16 workloads in
+TFLOP/s (10 d flops per visible pair for the backward); int8-KV and fp8-KV split decode, the
 decode with a bf16 residual window, and the quantise-on-append of a 4096-token
 chunk in GB/s of the bytes the method must move (codes + scales + window +
 query + output + LSE for decode; rows read and codes + scales written for the
@@ -86,6 +87,14 @@ def decode_bytes(cfg) -> int:
     return kv + scales + window + q + o + lse
 
 
+def bwd_flops(cfg) -> int:
+    """The backward's five products per visible pair: S recomputed (2d), dP = dO V^T
+    (2d), dV = P^T dO (2d), dQ = dS K (2d), dK = dS^T Q (2d): 10 d flops, 2.5x the
+    forward.  Recomputations beyond these (S and dP are formed in both the dK/dV
+    and the dQ pass here) are not counted."""
+    return 10 * cfg.d * visible_pairs(cfg.Sq, cfg.Sk, cfg.causal) * cfg.B * cfg.Hq
+
+
 def append_bytes(cfg) -> int:
     """Quantise-on-append: the bf16 key and value rows read once, their 1-byte
     codes and fp16 per-row scales written once."""
@@ -93,7 +102,17 @@ def append_bytes(cfg) -> int:
     return 2 * rows * cfg.d * 2 + 2 * (rows * cfg.d + rows * 2)
 
 
+def bwd_hbm_bytes(cfg) -> int:
+    """Compulsory HBM bytes of one backward: Q, K, V, O, dO and LSE read once,
+    dQ, dK, dV written once."""
+    q = cfg.B * cfg.Hq * cfg.Sq * cfg.d * 2
+    kv = cfg.B * cfg.Hkv * cfg.Sk * cfg.d * 2
+    return 3 * q + 2 * kv + cfg.B * cfg.Hq * cfg.Sq * 4 + q + 2 * kv
+
+
 def algorithmic_bytes(cfg) -> int:
+    if isinstance(cfg, fa_inputs.BwdConfig):
+        return bwd_hbm_bytes(cfg)
     if isinstance(cfg, fa_inputs.DecodeConfig):
         return decode_bytes(cfg)
     if isinstance(cfg, fa_inputs.AppendConfig):
@@ -102,7 +121,10 @@ def algorithmic_bytes(cfg) -> int:
 
 
 def workload(name):
-    return fa_inputs.CONFIGS[name] if name in fa_inputs.CONFIGS else fa_inputs.KV_CONFIGS[name]
+    for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 
@@ -177,6 +199,25 @@ def _decode_runner(cfg, seed=0):
     return run
 
 
+def _bwd_runner(cfg, seed=0):
+    import torch
+
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_bwd_inputs(cfg, seed=seed, device="cuda")
+    q, k, v, dout = x["q"], x["k"], x["v"], x["dout"]
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(cfg.B, cfg.Hq, cfg.Sq), dtype=torch.uint8, device="cuda")
+
+    def run():
+        fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=cfg.causal, softmax_scale=cfg.scale, workspace=ws)
+
+    return run
+
+
 def _append_runner(cfg, seed=0):
     import tiled_exact_attention_fa_amd as fa
 
@@ -195,6 +236,7 @@ KERNEL_SOURCES = {
     "fwd8": ["fa_fwd_fp8.hip", "fa_fwd_common.hpp", "fa_device.hpp"],
     "decode": ["fa_decode.hip", "fa_device.hpp"],
     "append": ["fa_kv_append.hip", "fa_device.hpp"],
+    "bwd": ["fa_bwd.hip", "fa_device.hpp"],
 }
 
 
@@ -203,6 +245,8 @@ def kernel_family(cfg) -> str:
         return "decode"
     if isinstance(cfg, fa_inputs.AppendConfig):
         return "append"
+    if isinstance(cfg, fa_inputs.BwdConfig):
+        return "bwd"
     return "fwd8" if cfg.dtype == "fp8" else "fwd16"
 
 
@@ -245,9 +289,10 @@ def measure(name, steps, warmup):
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic(name)}}
     else:
-        run = _fwd_runner(cfg)
+        bwd = isinstance(cfg, fa_inputs.BwdConfig)
+        run = _bwd_runner(cfg) if bwd else _fwd_runner(cfg)
         ms, wall = _time_region(run, steps, warmup)
-        work = fwd_flops(cfg)
+        work = bwd_flops(cfg) if bwd else fwd_flops(cfg)
         tf = work / (ms * 1e-3) / 1e12
         # a contraction is priced against the dense MFMA peak of its own input type
         peak = {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
@@ -393,7 +438,8 @@ def main():
     cfg = workload(a.workload)
 
     extras = {}
-    names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.KV_CONFIGS) if n != a.workload]
+    names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.BWD_CONFIGS) + list(fa_inputs.KV_CONFIGS)
+             if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":

@@ -27,7 +27,9 @@ runs, so CPU and GPU draws differ but each is deterministic for a given seed):
   (seed << 20) + B + 1, every sequence attending all W of them unless the config
   lists window lengths;
 * append: new key rows then value rows [B, H, T, d] bf16 N(0,1) from seed
-  (seed << 20) + 7, written at each sequence's position pos0.
+  (seed << 20) + 7, written at each sequence's position pos0;
+* backward: the forward's inputs, then dO [B, Hq, Sq, d] N(0,1) from seed
+  (seed << 20) + 5, cast like the inputs.
 """
 
 from __future__ import annotations
@@ -80,6 +82,11 @@ class DecodeConfig:
 
 
 @dataclass(frozen=True)
+class BwdConfig(FwdConfig):
+    """A backward workload: the forward's inputs plus a dO drawn after them."""
+
+
+@dataclass(frozen=True)
 class AppendConfig:
     name: str
     B: int
@@ -100,6 +107,14 @@ CONFIGS = {
         "bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
     "fp8_b8_h16_s4096": FwdConfig("fp8_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128, False, out_dtype="bf16"),
     "decode_int8_b64_gqa32x8_L32768": DecodeConfig("decode_int8_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16),
+}
+
+# The backward of the two causal bf16 prefill workloads (same inputs, plus a
+# N(0,1) gradient dO of the output).
+BWD_CONFIGS = {
+    "bwd_bf16_b4_h16_s2048_causal": BwdConfig("bwd_bf16_b4_h16_s2048_causal", "bf16", 4, 16, 16, 2048, 2048, 128, True),
+    "bwd_bf16_gqa32x8_s16384_causal_outlier": BwdConfig(
+        "bwd_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
 }
 
 # The cache's other formats and its write side, at the decode workload's sizes:
@@ -187,6 +202,16 @@ def make_fwd_inputs(cfg: FwdConfig, seed: int = 0, device="cpu"):
         return {"q": q8, "k": k8, "v": v8, "q_scale": qs, "k_scale": ks, "v_scale": vs}
     dt = _TORCH_DT[cfg.dtype]
     return {"q": qf.to(dt), "k": kf.to(dt), "v": vf.to(dt)}
+
+
+def make_bwd_inputs(cfg: BwdConfig, seed: int = 0, device="cpu"):
+    """The forward inputs of the same seed plus dout [B,Hq,Sq,d] in the input
+    dtype, drawn N(0,1) from seed (seed << 20) + 5."""
+    x = make_fwd_inputs(cfg, seed=seed, device=device)
+    g = _gen(device, (seed << 20) + 5)
+    dout = torch.randn(cfg.B, cfg.Hq, cfg.Sq, cfg.d, generator=g, device=device, dtype=torch.float32)
+    x["dout"] = dout.to(_TORCH_DT[cfg.dtype])
+    return x
 
 
 def make_decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):

@@ -11,7 +11,7 @@
  * forward also returns the per-row statistic LSE_i = ln sum_j exp(s_ij) that a
  * recomputing backward needs (panel 3, Q3).
  *
- * Three entry points do work:
+ * Four entry points do work:
  *   fa_fwd         prefill (KV-cache quantisation overview, section 1, "prefill"):
  *                  every query row of a sequence against its keys, optional
  *                  causal mask, grouped-query heads, optional LSE output;
@@ -24,6 +24,10 @@
  *                  their log-sum-exps.  An optional residual window of recent
  *                  tokens kept in bf16 (section 3, "residual window") joins the
  *                  same softmax.
+ *   fa_bwd         the backward of fa_fwd (interview canvas, panel 1 v1 card and
+ *                  panel 3, Q3: the backward keeps no score matrix and recomputes
+ *                  the local scores and probabilities from O and the per-row
+ *                  LSE): dQ, dK, dV for bf16 / fp16.
  *   fa_kv_append   the cache's write side (section 3, "before writing the cache"):
  *                  new bf16/fp16 key and value rows are quantised to int8 or
  *                  fp8-e4m3 codes with one fp16 scale per token and head, and
@@ -110,6 +114,43 @@ typedef struct {
 } fa_fwd_params;
 
 int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
+
+/*
+ * Backward of fa_fwd by recomputation.  Given the forward's inputs, its output
+ * o and natural-log lse (as fa_fwd writes them), and the gradient dout of a
+ * loss with respect to o, writes
+ *   dq [B, Hq, Sq, d], dk, dv [B, Hkv, Sk, d]
+ * the gradients of o = softmax(softmax_scale * q k^T) v (same causal rule, same
+ * grouped-query mapping; dk and dv of a key/value head sum the contributions of
+ * all the query heads that read it).  The gradient reaches o only: lse is an
+ * input, not differentiated.  A query row that sees no key contributes
+ * nothing (its lse is -inf).
+ * dtype is FA_BF16 or FA_F16 for every tensor but lse (float32); d must be 128.
+ * The probabilities and dS are rounded to dtype as matrix-core operands and
+ * accumulate in float32.  The caller's workspace (16-byte aligned, at least
+ * fa_bwd_workspace_size(B, Hq, Sq) bytes, contents on entry irrelevant) holds
+ * the per-row term rowsum(dout * o) in float32.  No atomics: results are
+ * bitwise reproducible.  dq, dk, dv must not overlap any input.
+ */
+typedef struct {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  int32_t dtype; /* fa_dtype: FA_BF16 or FA_F16 */
+  int32_t B, Hq, Hkv, Sq, Sk, d;
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3], do_strides[3];
+  int64_t dq_strides[3], dk_strides[3], dv_strides[3];
+  int64_t lse_strides[2];
+  float softmax_scale;
+  int32_t causal;
+  void *workspace;
+  size_t workspace_bytes;
+} fa_bwd_params;
+
+/* Bytes of workspace fa_bwd needs (0 on invalid sizes). */
+size_t fa_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq);
+
+int fa_bwd(const fa_bwd_params *p, fa_stream_t stream);
 
 /*
  * Cache formats.  Both store one code byte per element and one fp16 scale per
@@ -219,6 +260,7 @@ int fa_kv_append(const fa_kv_append_params *p, fa_stream_t stream);
 int fa_check_fwd_params(const fa_fwd_params *p);
 int fa_check_decode_params(const fa_decode_params *p);
 int fa_check_kv_append_params(const fa_kv_append_params *p);
+int fa_check_bwd_params(const fa_bwd_params *p);
 
 /* Static description of a status code. */
 const char *fa_status_string(int status);

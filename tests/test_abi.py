@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 STRUCTS = [("fa_fwd_params", fa.FaFwdParams), ("fa_decode_params", fa.FaDecodeParams),
-           ("fa_kv_append_params", fa.FaKvAppendParams)]
+           ("fa_kv_append_params", fa.FaKvAppendParams), ("fa_bwd_params", fa.FaBwdParams)]
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -247,3 +247,45 @@ def test_status_strings(lib):
     assert fa.fa_status_string(-99) == "FA_ERR_UNKNOWN"
     fa.fa_check_fwd_params(good_fwd())
     assert fa.fa_last_error() == ""
+
+
+def good_bwd():
+    p = fa.FaBwdParams()
+    p.q = p.k = p.v = p.o = p.dout = p.dq = p.dk = p.dv = 0x10000
+    p.lse = 0x20000
+    p.dtype = fa.FA_BF16
+    p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d = 2, 8, 2, 100, 120, 128
+    for name in ("q", "o", "do", "dq"):
+        setattr(p, f"{name}_strides", fa.I64x3(8 * 100 * 128, 100 * 128, 128))
+    for name in ("k", "v", "dk", "dv"):
+        setattr(p, f"{name}_strides", fa.I64x3(2 * 120 * 128, 120 * 128, 128))
+    p.lse_strides = fa.I64x2(8 * 100, 100)
+    p.softmax_scale = 128 ** -0.5
+    p.workspace = 0x40000
+    p.workspace_bytes = fa.fa_bwd_workspace_size(2, 8, 100)
+    return p
+
+
+def test_bwd_validator(lib):
+    assert fa.fa_check_bwd_params(good_bwd()) == fa.FA_OK
+    assert fa.fa_bwd_workspace_size(2, 8, 100) >= 2 * 8 * 100 * 4
+    assert fa.fa_bwd_workspace_size(1, 0, 10) == 0
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "dtype", fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "d", 64), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "Hkv", 3), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "dout", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "lse", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "lse", 0x20002), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "dk", 0x10008), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "workspace_bytes", 16), fa.FA_ERR_WORKSPACE),
+    (lambda p: setattr(p, "workspace", 0x40004), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "softmax_scale", 0.0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "dq_strides", fa.I64x3(8 * 100 * 128, 100 * 128, 120)), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_validator_errors(lib, mutate, status):
+    p = good_bwd()
+    mutate(p)
+    assert fa.fa_check_bwd_params(p) == status

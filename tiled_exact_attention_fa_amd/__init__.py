@@ -10,9 +10,11 @@ been built, load() raises.
     fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None, ...)
     fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, ...)
     fa_decode_workspace_size(B, Hq, d, num_splits)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=False, ...)
+    fa_bwd_workspace_size(B, Hq, Sq)
     fa_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=None, ...)
-    fa_check_fwd_params(params) / fa_check_decode_params(params) /
-    fa_check_kv_append_params(params)
+    fa_check_fwd_params(params) / fa_check_bwd_params(params) /
+    fa_check_decode_params(params) / fa_check_kv_append_params(params)
     fa_status_string(status) / fa_last_error()
 
 Build with ``python -m tiled_exact_attention_fa_amd.build``.
@@ -69,6 +71,24 @@ class FaDecodeParams(ctypes.Structure):
     ]
 
 
+class FaBwdParams(ctypes.Structure):
+    """Mirror of fa_bwd_params."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("q_strides", I64x3), ("k_strides", I64x3), ("v_strides", I64x3), ("o_strides", I64x3),
+        ("do_strides", I64x3), ("dq_strides", I64x3), ("dk_strides", I64x3), ("dv_strides", I64x3),
+        ("lse_strides", I64x2),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class FaKvAppendParams(ctypes.Structure):
     """Mirror of fa_kv_append_params."""
 
@@ -84,8 +104,9 @@ class FaKvAppendParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ["fa_fwd", "fa_decode_kvq", "fa_decode_workspace_size", "fa_kv_append", "fa_check_fwd_params",
-           "fa_check_decode_params", "fa_check_kv_append_params", "fa_status_string", "fa_last_error"]
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_kvq", "fa_decode_workspace_size",
+           "fa_kv_append", "fa_check_fwd_params", "fa_check_bwd_params", "fa_check_decode_params",
+           "fa_check_kv_append_params", "fa_status_string", "fa_last_error"]
 
 
 class FaError(RuntimeError):
@@ -116,6 +137,12 @@ def load(path: str | None = None):
     lib.fa_check_fwd_params.restype = ctypes.c_int
     lib.fa_check_decode_params.argtypes = [ctypes.POINTER(FaDecodeParams)]
     lib.fa_check_decode_params.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [ctypes.POINTER(FaBwdParams), ctypes.c_void_p]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_check_bwd_params.argtypes = [ctypes.POINTER(FaBwdParams)]
+    lib.fa_check_bwd_params.restype = ctypes.c_int
+    lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int32] * 3
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_kv_append.argtypes = [ctypes.POINTER(FaKvAppendParams), ctypes.c_void_p]
     lib.fa_kv_append.restype = ctypes.c_int
     lib.fa_check_kv_append_params.argtypes = [ctypes.POINTER(FaKvAppendParams)]
@@ -142,6 +169,14 @@ def fa_check_fwd_params(params: FaFwdParams) -> int:
 
 def fa_check_decode_params(params: FaDecodeParams) -> int:
     return load().fa_check_decode_params(ctypes.byref(params))
+
+
+def fa_check_bwd_params(params: FaBwdParams) -> int:
+    return load().fa_check_bwd_params(ctypes.byref(params))
+
+
+def fa_bwd_workspace_size(B: int, Hq: int, Sq: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, Hq, Sq))
 
 
 def fa_check_kv_append_params(params: FaKvAppendParams) -> int:
@@ -225,6 +260,43 @@ def _kv_format(cache, kv_format):
     if cache.dtype in (torch.float8_e4m3fn, torch.uint8):
         return FA_KV_FP8_E4M3_TOKHEAD_F16SCALE
     raise TypeError(f"cannot infer the cache format from dtype {cache.dtype}")
+
+
+def bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=None,
+               workspace=None) -> FaBwdParams:
+    """fa_bwd_params for q/o/dout/dq [B,Hq,Sq,d], k/v/dk/dv [B,Hkv,Sk,d] and
+    lse [B,Hq,Sq] float32 (any strides with a unit head-dim stride)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _require_dense_d(n, t)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    p = FaBwdParams()
+    p.q, p.k, p.v, p.o, p.dout, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse)
+    p.dq, p.dk, p.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    p.dtype = _dtype_code(q)
+    p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.d = B, Hq, Hkv, Sq, Sk, d
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(p, f"{name}_strides", I64x3(*t.stride()[:3]))
+    p.lse_strides = I64x2(*lse.stride()[:2])
+    p.softmax_scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    p.causal = 1 if causal else 0
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=None, workspace=None,
+           stream=None) -> None:
+    """Enqueue the backward (dq, dk, dv from dout, o and the forward's lse)."""
+    import torch
+
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(q.shape[0], q.shape[1], q.shape[2]),
+                                dtype=torch.uint8, device=q.device)
+    p = bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal, softmax_scale, workspace)
+    st = load().fa_bwd(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd", fa_last_error())
 
 
 def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,

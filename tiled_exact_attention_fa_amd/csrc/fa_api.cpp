@@ -22,3 +22,10 @@ extern "C" int fa_kv_append(const fa_kv_append_params *p, fa_stream_t stream) {
   if (p->B == 0 || p->T == 0 || p->L == 0) return FA_OK;
   return fa_launch_kv_append(p, stream);
 }
+
+extern "C" int fa_bwd(const fa_bwd_params *p, fa_stream_t stream) {
+  const int st = fa_check_bwd_params(p);
+  if (st != FA_OK) return st;
+  if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return FA_OK;
+  return fa_launch_bwd(p, stream);
+}

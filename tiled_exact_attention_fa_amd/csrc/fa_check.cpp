@@ -203,3 +203,48 @@ extern "C" int fa_check_kv_append_params(const fa_kv_append_params *p) {
     if (p->scale_strides[i] < 0) return fa_set_error(FA_ERR_INVALID_ARG, "scale stride %d is negative", i);
   return FA_OK;
 }
+
+extern "C" size_t fa_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq) {
+  if (B < 0 || Hq <= 0 || Sq < 0) return 0;
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(Hq) * static_cast<size_t>(Sq);
+  return ((rows * sizeof(float) + 255) & ~size_t(255)) + 256;
+}
+
+extern "C" int fa_check_bwd_params(const fa_bwd_params *p) {
+  fa_clear_error();
+  if (p == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Sq < 0 || p->Sk < 0 || p->d <= 0)
+    return fa_set_error(FA_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d", p->B, p->Hq,
+                        p->Hkv, p->Sq, p->Sk, p->d);
+  if (p->Hq % p->Hkv != 0)
+    return fa_set_error(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->d != 128) return fa_set_error(FA_ERR_UNSUPPORTED, "backward head dim %d not supported (128)", p->d);
+  if (p->dtype != FA_BF16 && p->dtype != FA_F16)
+    return fa_set_error(FA_ERR_UNSUPPORTED, "backward dtype %d not supported (bf16 or fp16)", p->dtype);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
+    return fa_set_error(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return FA_OK;
+  int st;
+  if (p->Sq > 0) {
+    if ((st = check_tensor("q", p->q, p->q_strides, 3, p->Sq, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("o", p->o, p->o_strides, 3, p->Sq, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("dout", p->dout, p->do_strides, 3, p->Sq, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("dq", p->dq, p->dq_strides, 3, p->Sq, p->d, 2)) != FA_OK) return st;
+    if (p->lse == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "lse is NULL");
+    if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0)
+      return fa_set_error(FA_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    if (p->lse_strides[0] < 0 || p->lse_strides[1] < 0)
+      return fa_set_error(FA_ERR_INVALID_ARG, "lse strides must be >= 0");
+  }
+  if (p->Sk > 0) {
+    if ((st = check_tensor("k", p->k, p->k_strides, 3, p->Sk, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("v", p->v, p->v_strides, 3, p->Sk, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("dk", p->dk, p->dk_strides, 3, p->Sk, p->d, 2)) != FA_OK) return st;
+    if ((st = check_tensor("dv", p->dv, p->dv_strides, 3, p->Sk, p->d, 2)) != FA_OK) return st;
+  }
+  const size_t need = fa_bwd_workspace_size(p->B, p->Hq, p->Sq);
+  if (p->workspace == nullptr || p->workspace_bytes < need)
+    return fa_set_error(FA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", p->workspace_bytes, need);
+  if (!aligned16(p->workspace)) return fa_set_error(FA_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  return FA_OK;
+}

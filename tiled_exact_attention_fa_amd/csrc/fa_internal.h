@@ -17,3 +17,4 @@ int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream);
 int fa_launch_fwd_fp8(const fa_fwd_params *p, void *stream);
 int fa_launch_decode(const fa_decode_params *p, void *stream);
 int fa_launch_kv_append(const fa_kv_append_params *p, void *stream);
+int fa_launch_bwd(const fa_bwd_params *p, void *stream);
