@@ -12,20 +12,22 @@
 //
 // MI355X design.  Three kernels, no atomics, so every result is deterministic:
 //   * bwd_rowdot_kernel: Dr per query row, one 16-lane group per row.
-//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, kv head), a
-//     wavefront 32 of them; it walks every query head of the group and every
+//   * bwd_dkdv_kernel: a workgroup owns 256 keys of one (batch, kv head), a
+//     wavefront 32 of them (8 wavefronts, two per SIMD); it walks every query head of the group and every
 //     query tile that can see its keys, and keeps dK^T and dV^T of its keys in
 //     registers until the end.  Per tile: S = Q K^T and dP = dO V^T with the
-//     keys' K and V rows held in registers as the B operand, then
+//     keys' K rows in registers and V rows in LDS as the B operands, then
 //     dV^T += dO^T P and dK^T += Q^T dS with the probabilities fed from the
 //     S accumulators straight into the B operand (the query tile is written
 //     to LDS with bits 2 and 3 of the row index swapped, which puts the
 //     accumulator registers in the operand's order).  The query tile is staged
 //     twice, row-major for the first products and transposed for the second.
 //   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch, head), a
-//     wavefront 32; per key tile S^T = K Q^T and dP^T = V dO^T with the rows'
+//     wavefront 32 (two wavefronts per SIMD); per 32-key tile S^T = K Q^T and dP^T = V dO^T with the rows'
 //     Q and dO in registers, then dQ^T += K^T dS^T, K staged both row-major
 //     (permuted rows) and transposed.
+//   * Both tile loops stage through two LDS buffers with register prefetch two
+//     tiles ahead: one barrier per tile.
 // All products are 32x32x16 MFMAs on the input type with fp32 accumulation; P
 // and dS are rounded to the input type only as MFMA operands.  Scores stay in
 // the log2 domain (tau * log2 e folded into one multiply, hardware exp2).
@@ -73,12 +75,12 @@ constexpr int kRow = kBD + kEPC;  // row-major tile row in LDS, +16 bytes
 __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 __device__ __forceinline__ int acc_row(int mb, int i, int h) { return 32 * mb + 16 * (i >> 3) + 8 * h + (i & 7); }
 
-// A tile of R rows x 128 elements, loaded by 256 threads: thread (g, c) holds
+// A tile of R rows x 128 elements, loaded by NT threads: thread (g, c) holds
 // rows g * RPT .. g * RPT + RPT - 1 of chunk c, which it can write both
 // row-major (one 16-byte store per row) and transposed (RPT elements of each of
 // its 8 columns).
-template <typename T, int R> struct Tile {
-  static constexpr int RPT = R * kCH / 256;  // rows per thread
+template <typename T, int R, int NT = 256> struct Tile {
+  static constexpr int RPT = R * kCH / NT;   // rows per thread
   static constexpr int NG = R / RPT;         // row groups
   static constexpr int TROW = R + kEPC;      // transposed row in LDS (+16 bytes)
   u32x4 r[RPT];
@@ -111,9 +113,11 @@ template <typename T, int R> struct Tile {
       if constexpr (RPT == 4) {
         *reinterpret_cast<u32x2 *>(d) = u32x2{col[0] | (static_cast<unsigned>(col[1]) << 16),
                                               col[2] | (static_cast<unsigned>(col[3]) << 16)};
-      } else {
-        static_assert(RPT == 2, "tile rows per thread");
+      } else if constexpr (RPT == 2) {
         *reinterpret_cast<unsigned *>(d) = col[0] | (static_cast<unsigned>(col[1]) << 16);
+      } else {
+        static_assert(RPT == 1, "tile rows per thread");
+        *d = col[0];
       }
     }
   }
@@ -162,42 +166,57 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse == neg_inf() ? __builtin_inff() : lse * kLog2e;
 }
 
-// ---- dK, dV: a workgroup owns 128 keys, a wavefront 32 ----
+// ---- dK, dV: a workgroup of 8 wavefronts owns 256 keys, a wavefront 32 ----
+// (two wavefronts per SIMD).  The keys' K rows stay in registers as the B
+// operand of S = Q K^T; their V rows are staged once in LDS (the register file
+// holds K, dK^T and dV^T for two wavefronts per SIMD, not V as well) and read
+// as the B operand of dP = dO V^T.  Query tiles are staged by all 512 threads,
+// one 16-byte chunk each, double-buffered.
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvKeys = 32 * kDkdvWaves;
+
 template <typename T, bool CAUSAL, int BR>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   using M = BwdMfma<T>;
   typedef typename M::frag frag;
-  using Tl = Tile<T, BR>;
+  using Tl = Tile<T, BR, 512>;
   constexpr int MB = BR / 32;
-  __shared__ __attribute__((aligned(16))) T sQ[BR * kRow];
-  __shared__ __attribute__((aligned(16))) T sDO[BR * kRow];
-  __shared__ __attribute__((aligned(16))) T sQt[kBD * Tl::TROW];
-  __shared__ __attribute__((aligned(16))) T sDOt[kBD * Tl::TROW];
-  __shared__ __attribute__((aligned(16))) float sL[BR];
-  __shared__ __attribute__((aligned(16))) float sD[BR];
+  // two LDS stages: tile w is read from stage w & 1 while tile w + 1 is
+  // written to the other one, so one barrier per tile suffices
+  __shared__ __attribute__((aligned(16))) T sQ[2][BR * kRow];
+  __shared__ __attribute__((aligned(16))) T sDO[2][BR * kRow];
+  __shared__ __attribute__((aligned(16))) T sQt[2][kBD * Tl::TROW];
+  __shared__ __attribute__((aligned(16))) T sDOt[2][kBD * Tl::TROW];
+  __shared__ __attribute__((aligned(16))) float sL[2][BR];
+  __shared__ __attribute__((aligned(16))) float sD[2][BR];
+  __shared__ __attribute__((aligned(16))) T sV[kDkdvKeys * kRow];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int nkt = (a.Sk + 127) / 128;
   const int kt = blockIdx.x / (a.B * a.Hkv);  // heaviest (earliest) key tiles first
   const int bh = blockIdx.x % (a.B * a.Hkv);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  (void)nkt;
-  const int j0 = kt * 128;
+  const int j0 = kt * kDkdvKeys;
   const int key = j0 + 32 * wave + l32;  // this lane's key (column of S, dP, dK^T, dV^T)
   const int coff = a.Sk - a.Sq;          // key j visible from row i iff j <= i + coff
 
-  // K and V rows of this lane's key: lane half h holds elements 64 h .. 64 h + 63
-  frag kf[8], vf[8];
+  // K rows of this lane's key in registers (lane half h: elements 64 h .. 64 h + 63);
+  // the workgroup's V rows into LDS, one 16-byte chunk per thread and pass
+  frag kf[8];
   {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const T *>(a.k) + b * a.k_sb + hk * a.k_sh, a.k_ext);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const T *>(a.v) + b * a.v_sb + hk * a.v_sh, a.v_ext);
     const bool ok = key < a.Sk;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 8; ++c)
       kf[c] = __builtin_bit_cast(frag, buf_load16(rk, ok ? key * a.k_ss + (64 * h + 8 * c) * 2 : kOOB));
-      vf[c] = __builtin_bit_cast(frag, buf_load16(rv, ok ? key * a.v_ss + (64 * h + 8 * c) * 2 : kOOB));
+#pragma unroll
+    for (int p = 0; p < kDkdvKeys * kCH / 512; ++p) {
+      const int idx = tid + 512 * p;
+      const int r = idx / kCH, c = idx % kCH;
+      const int kj = j0 + r;
+      *reinterpret_cast<u32x4 *>(sV + r * kRow + c * kEPC) = buf_load16(rv, kj < a.Sk ? kj * a.v_ss + c * 16 : kOOB);
     }
   }
   f32x16 dk[4], dv[4];
@@ -209,46 +228,59 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int t_first = i_first / BR;
   const int n_qt = (a.Sq + BR - 1) / BR;
 
-  for (int g = 0; g < a.G; ++g) {
-    const int hq = hk * a.G + g;
+  // the work is the sequence of (query head of the group, query tile) items;
+  // the staging pipeline runs straight through the head changes
+  const int ntl = max(n_qt - t_first, 0);
+  const int n_items = a.G * ntl;
+  Tl tq, tdo;
+  float l_st = 0.f, d_st = 0.f;  // lse2 / row term of row tid of the staged tile (tid < BR)
+  auto load_item = [&](int w) {
+    const int hq = hk * a.G + w / ntl;
+    const int i0 = (t_first + w % ntl) * BR;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
     const __amdgpu_buffer_rsrc_t rdo =
         make_rsrc(static_cast<const T *>(a.dout) + b * a.do_sb + hq * a.do_sh, a.do_ext);
-    const float *lse_row = a.lse + b * a.lse_sb + hq * a.lse_sh;
-    const float *dot_row = a.rowdot + (static_cast<long long>(b) * a.Hq + hq) * a.Sq;
-    Tl tq, tdo;
-    if (t_first < n_qt) {
-      tq.load(rq, a.q_ss, t_first * BR, a.Sq);
-      tdo.load(rdo, a.do_ss, t_first * BR, a.Sq);
+    tq.load(rq, a.q_ss, i0, a.Sq);
+    tdo.load(rdo, a.do_ss, i0, a.Sq);
+    if (tid < BR) {
+      const int i = i0 + tid;
+      l_st = i < a.Sq ? lse2_of(a.lse[b * a.lse_sb + hq * a.lse_sh + i]) : __builtin_inff();
+      d_st = i < a.Sq ? a.rowdot[(static_cast<long long>(b) * a.Hq + hq) * a.Sq + i] : 0.f;
     }
-    for (int qt = t_first; qt < n_qt; ++qt) {
-      const int i0 = qt * BR;
-      __syncthreads();  // the previous tile's readers are done
-      tq.store_rows(sQ);
-      tq.store_transposed(sQt);
-      tdo.store_rows(sDO);
-      tdo.store_transposed(sDOt);
-      if (tid < BR) {
-        const int i = i0 + tid;
-        sL[tid] = i < a.Sq ? lse2_of(lse_row[i]) : __builtin_inff();
-        sD[tid] = i < a.Sq ? dot_row[i] : 0.f;
-      }
-      __syncthreads();
-      if (qt + 1 < n_qt) {  // next tile in flight during this tile's products
-        tq.load(rq, a.q_ss, i0 + BR, a.Sq);
-        tdo.load(rdo, a.do_ss, i0 + BR, a.Sq);
-      }
+  };
+  auto store_item = [&](int st) {
+    tq.store_rows(sQ[st]);
+    tq.store_transposed(sQt[st]);
+    tdo.store_rows(sDO[st]);
+    tdo.store_transposed(sDOt[st]);
+    if (tid < BR) {
+      sL[st][tid] = l_st;
+      sD[st][tid] = d_st;
+    }
+  };
+  if (n_items > 0) {
+    load_item(0);
+    store_item(0);
+  }
+  if (n_items > 1) load_item(1);
+  __syncthreads();
+
+  const T *vrow = sV + (32 * wave + l32) * kRow + 64 * h;  // B operand of dP: this lane's key
+  for (int w = 0; w < n_items; ++w) {
+    const int st = w & 1;
+    const int i0 = (t_first + w % ntl) * BR;
+    {
       // S = Q K^T and dP = dO V^T, rows = queries (permuted), columns = keys
       f32x16 s[MB], dp[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         s[mb] = dp[mb] = f32x16{};
-        const T *qr = sQ + (32 * mb + l32) * kRow + 64 * h;
-        const T *dr = sDO + (32 * mb + l32) * kRow + 64 * h;
+        const T *qr = sQ[st] + (32 * mb + l32) * kRow + 64 * h;
+        const T *dr = sDO[st] + (32 * mb + l32) * kRow + 64 * h;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           s[mb] = M::mma(lds_frag<T>(qr + 8 * c), kf[c], s[mb]);
-          dp[mb] = M::mma(lds_frag<T>(dr + 8 * c), vf[c], dp[mb]);
+          dp[mb] = M::mma(lds_frag<T>(dr + 8 * c), lds_frag<T>(vrow + 8 * c), dp[mb]);
         }
       }
       // P and dS, as B operands over query steps of 16
@@ -258,10 +290,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int r0 = 32 * mb + 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
-          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL + r0);
-          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL + r0 + 4);
-          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(sD + r0);
-          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(sD + r0 + 4);
+          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL[st] + r0);
+          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL[st] + r0 + 4);
+          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(sD[st] + r0);
+          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(sD[st] + r0 + 4);
           unsigned pw[4], dw[4];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
@@ -289,8 +321,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       // dV^T += dO^T P, dK^T += Q^T dS: rows = head dims, columns = keys
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const T *dot = sDOt + (32 * db + l32) * Tl::TROW + 8 * h;
-        const T *qtp = sQt + (32 * db + l32) * Tl::TROW + 8 * h;
+        const T *dot = sDOt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
+        const T *qtp = sQt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
 #pragma unroll
         for (int t = 0; t < BR / 16; ++t) {
           dv[db] = M::mma(lds_frag<T>(dot + 16 * t), pf[t], dv[db]);
@@ -298,6 +330,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
     }
+    if (w + 1 < n_items) store_item(st ^ 1);  // that stage was last read by tile w - 1
+    if (w + 2 < n_items) load_item(w + 2);
+    __syncthreads();
   }
 
   // ---- write dK = tau dK^T^T and dV: lane's key, dims 32 db + 8 m + 4 h .. +3 ----
@@ -319,16 +354,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---- dQ: a workgroup owns 128 query rows, a wavefront 32; key tiles of 64 ----
-template <typename T, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+template <typename T, bool CAUSAL, int BC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const BwdArgs a) {
   using M = BwdMfma<T>;
   typedef typename M::frag frag;
-  constexpr int BC = 64;
   using Tl = Tile<T, BC>;
-  __shared__ __attribute__((aligned(16))) T sK[BC * kRow];
-  __shared__ __attribute__((aligned(16))) T sV[BC * kRow];
-  __shared__ __attribute__((aligned(16))) T sKt[kBD * Tl::TROW];
+  __shared__ __attribute__((aligned(16))) T sK[2][BC * kRow];
+  __shared__ __attribute__((aligned(16))) T sV[2][BC * kRow];
+  __shared__ __attribute__((aligned(16))) T sKt[2][kBD * Tl::TROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -369,28 +403,32 @@ void bwd_dq_kernel(const BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const T *>(a.k) + b * a.k_sb + hk * a.k_sh, a.k_ext);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const T *>(a.v) + b * a.v_sb + hk * a.v_sh, a.v_ext);
   Tl tk, tv;
+  auto store_tile = [&](int st) {
+    tk.store_rows(sK[st]);
+    tk.store_transposed(sKt[st]);
+    tv.store_rows(sV[st]);
+  };
   if (n_kt > 0) {
     tk.load(rk, a.k_ss, 0, a.Sk);
     tv.load(rv, a.v_ss, 0, a.Sk);
+    store_tile(0);
   }
+  if (n_kt > 1) {
+    tk.load(rk, a.k_ss, BC, a.Sk);
+    tv.load(rv, a.v_ss, BC, a.Sk);
+  }
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int j0 = kt * BC;
-    __syncthreads();
-    tk.store_rows(sK);
-    tk.store_transposed(sKt);
-    tv.store_rows(sV);
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      tk.load(rk, a.k_ss, j0 + BC, a.Sk);
-      tv.load(rv, a.v_ss, j0 + BC, a.Sk);
-    }
+    const int st = kt & 1;
     // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), columns = query rows
-    f32x16 s[2], dp[2];
+    constexpr int MB = BC / 32;
+    f32x16 s[MB], dp[MB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       s[mb] = dp[mb] = f32x16{};
-      const T *kr = sK + (32 * mb + l32) * kRow + 64 * h;
-      const T *vr = sV + (32 * mb + l32) * kRow + 64 * h;
+      const T *kr = sK[st] + (32 * mb + l32) * kRow + 64 * h;
+      const T *vr = sV[st] + (32 * mb + l32) * kRow + 64 * h;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         s[mb] = M::mma(lds_frag<T>(kr + 8 * c), qf[c], s[mb]);
@@ -399,7 +437,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     }
     frag dsf[BC / 16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         unsigned dw[4];
@@ -422,10 +460,16 @@ void bwd_dq_kernel(const BwdArgs a) {
     // dQ^T += K^T dS^T: rows = head dims, columns = query rows
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const T *ktp = sKt + (32 * db + l32) * Tl::TROW + 8 * h;
+      const T *ktp = sKt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
 #pragma unroll
       for (int t = 0; t < BC / 16; ++t) dq[db] = M::mma(lds_frag<T>(ktp + 16 * t), dsf[t], dq[db]);
     }
+    if (kt + 1 < n_kt) store_tile(st ^ 1);  // that stage was last read by tile kt - 1
+    if (kt + 2 < n_kt) {
+      tk.load(rk, a.k_ss, j0 + 2 * BC, a.Sk);
+      tv.load(rv, a.v_ss, j0 + 2 * BC, a.Sk);
+    }
+    __syncthreads();
   }
 
   if (row < a.Sq) {
@@ -447,15 +491,15 @@ int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
   const long long rows = static_cast<long long>(a.B) * a.Hq * a.Sq;
   if (rows > 0)
     hipLaunchKernelGGL(bwd_rowdot_kernel<T>, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, a);
-  const unsigned g_kv = static_cast<unsigned>((a.Sk + 127) / 128) * a.B * a.Hkv;
+  const unsigned g_kv = static_cast<unsigned>((a.Sk + kDkdvKeys - 1) / kDkdvKeys) * a.B * a.Hkv;
   const unsigned g_q = static_cast<unsigned>((a.Sq + 127) / 128) * a.B * a.Hq;
-  constexpr int BR = 64;
+  constexpr int BR = 32, BC = 32;  // query rows per dK/dV tile, keys per dQ tile
   if (causal) {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, BR>), dim3(g_kv), dim3(256), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(g_q), dim3(256), 0, s, a);
+    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, BR>), dim3(g_kv), dim3(512), 0, s, a);
+    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true, BC>), dim3(g_q), dim3(256), 0, s, a);
   } else {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, false, BR>), dim3(g_kv), dim3(256), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, false>), dim3(g_q), dim3(256), 0, s, a);
+    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, false, BR>), dim3(g_kv), dim3(512), 0, s, a);
+    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, false, BC>), dim3(g_q), dim3(256), 0, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
