@@ -21,7 +21,8 @@ Modules
   e4m3       OCP E4M3FN byte decoder written from the format's definition.
   quant      the KV-cache write side: per-token-per-head int8 and E4M3FN
              quantisers (and the E4M3FN encoder), and the append of quantised
-             rows into a cache.
+             rows into a cache; the block-scaled fp8 quantiser of prefill
+             inputs with optional random-sign Hadamard rotation.
 
 Every function has a pin in tests/test_oracle.py, tests/test_oracle_kv.py or
 tests/test_oracle_bwd.py
@@ -42,4 +43,11 @@ from .attention import (  # noqa: F401
 from .backward import attention_bwd_fp64  # noqa: F401
 from .brute import attention_brute  # noqa: F401
 from .e4m3 import e4m3_decode  # noqa: F401
-from .quant import e4m3_encode, kv_append_ref, quantize_kv_tokhead  # noqa: F401
+from .quant import (  # noqa: F401
+    dequant_fp8_blocks_fp64,
+    e4m3_encode,
+    hadamard_rotate_fp32,
+    kv_append_ref,
+    quantize_fp8_blocks,
+    quantize_kv_tokhead,
+)

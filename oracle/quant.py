@@ -1,4 +1,4 @@
-"""KV-cache write-side quantisers — TEST INFRASTRUCTURE ONLY (see package doc).
+"""Quantisers of the KV-cache write side and of fp8 prefill inputs — TEST INFRASTRUCTURE ONLY (see package doc).
 
 KV-cache quantisation overview, section 3 ("where quantisation can sit"): before
 a key or value row enters the cache it is turned from FP16/BF16 into a low-bit
@@ -25,6 +25,8 @@ finite 448, no infinities); it shares nothing with the GPU path.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -108,3 +110,73 @@ def kv_append_ref(cache_codes, cache_scales, rows, positions, fmt: str):
                 codes[b, :, s] = qc[b, :, t]
                 scales[b, :, s] = qs[b, :, t]
     return codes, scales
+
+
+# ---- fp8 inputs of the prefill: block scales and incoherent processing ----
+#
+# FlashAttention-3 page, producer/consumer pseudocode box ("FP8 path") and the
+# closing answer: fp8 attention keeps its accuracy with block-wise
+# quantisation of Q, K and V and with incoherent processing (the page gives no
+# formulas).  Readings taken here:
+#   * a block is 64 consecutive rows (tokens) of one (batch, head) slice, with
+#     one fp32 scale s = fp32(absmax / 448); s == 0 stores code 0 everywhere;
+#     code = E4M3FN(clamp(fp32(y) / s, +-448)), nearest even (as above);
+#   * incoherent processing multiplies each row of Q and of K by the same
+#     orthogonal matrix R = diag(signs) H / sqrt(d) (H the Sylvester-Hadamard
+#     matrix, signs a random +-1 vector) before quantising: (Q R)(K R)^T =
+#     Q K^T exactly, while an outlier channel is spread over all d channels.
+#     It is evaluated in float32 as the iterative fast transform — stages
+#     h = 1, 2, 4, ..., d/2, each mapping the pair (a at i, b at i + h) of an
+#     aligned block of 2h to (a + b, a - b) — followed by one multiply by
+#     fp32(1 / sqrt(d)), the order in which the codes are decided.
+
+FP8_BLOCK_ROWS = 64
+
+
+def hadamard_rotate_fp32(x, signs) -> np.ndarray:
+    """Rows x [..., d] (float32 values) times diag(signs) H / sqrt(d), in float32,
+    by the stage order stated above.  d must be a power of two."""
+    y = np.array(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        z = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(*y.shape[:-1], d)
+        h *= 2
+    return y * np.float32(1.0 / math.sqrt(d))
+
+
+def quantize_fp8_blocks(x, signs=None, block_rows: int = FP8_BLOCK_ROWS):
+    """x [B, H, S, d] (bf16/fp16/fp32 values) -> (codes uint8 [B, H, S, d],
+    scales float32 [B, H, ceil(S / block_rows)]), optionally rotated first."""
+    xf = _f32(x)
+    if signs is not None:
+        xf = hadamard_rotate_fp32(xf, signs)
+    B, H, S, d = xf.shape
+    nb = (S + block_rows - 1) // block_rows
+    codes = np.zeros((B, H, S, d), dtype=np.uint8)
+    scales = np.zeros((B, H, nb), dtype=np.float32)
+    for blk in range(nb):
+        r0, r1 = blk * block_rows, min(S, (blk + 1) * block_rows)
+        part = xf[:, :, r0:r1]
+        amax = np.max(np.abs(part), axis=(2, 3)) if r1 > r0 else np.zeros((B, H), np.float32)
+        s = (amax.astype(np.float32) / np.float32(E4M3_QMAX)).astype(np.float32)
+        scales[:, :, blk] = s
+        live = s > 0
+        y = part / np.where(live, s, np.float32(1.0))[:, :, None, None]
+        c = e4m3_encode(np.clip(y.astype(np.float64), -E4M3_QMAX, E4M3_QMAX))
+        codes[:, :, r0:r1] = np.where(live[:, :, None, None], c, np.uint8(0))
+    return codes, scales
+
+
+def dequant_fp8_blocks_fp64(codes, scales, block_rows: int = FP8_BLOCK_ROWS) -> np.ndarray:
+    """codes [B, H, S, d] E4M3FN bytes, scales [B, H, nblk] -> float64 values."""
+    from .e4m3 import e4m3_decode
+
+    S = codes.shape[2]
+    per_row = np.repeat(np.asarray(scales, dtype=np.float64), block_rows, axis=2)[:, :, :S]
+    return e4m3_decode(codes) * per_row[..., None]
