@@ -11,7 +11,7 @@
  * forward also returns the per-row statistic LSE_i = ln sum_j exp(s_ij) that a
  * recomputing backward needs (panel 3, Q3).
  *
- * Four entry points do work:
+ * Five entry points do work:
  *   fa_fwd         prefill (KV-cache quantisation overview, section 1, "prefill"):
  *                  every query row of a sequence against its keys, optional
  *                  causal mask, grouped-query heads, optional LSE output;
@@ -28,6 +28,9 @@
  *                  panel 3, Q3: the backward keeps no score matrix and recomputes
  *                  the local scores and probabilities from O and the per-row
  *                  LSE): dQ, dK, dV for bf16 / fp16.
+ *   fa_fp8_quantize  fp8 inputs for fa_fwd with 64-row block scales and an
+ *                  optional random-sign Hadamard rotation (FlashAttention-3 page,
+ *                  the FP8 path's block quantisation and incoherent processing).
  *   fa_kv_append   the cache's write side (section 3, "before writing the cache"):
  *                  new bf16/fp16 key and value rows are quantised to int8 or
  *                  fp8-e4m3 codes with one fp16 scale per token and head, and
@@ -89,7 +92,8 @@ typedef enum {
  * Hq % Hkv == 0).  d is 64 or 128.
  * Dtype pairs (in_dtype -> out_dtype): F32->F32, BF16->BF16, F16->F16,
  * FP8_E4M3->BF16.  For FP8 the true operands are code * descale (one float32
- * descale per tensor); q/k/v_descale are ignored for the other dtypes.
+ * descale per tensor, or per 64-row block, see below); the descales are
+ * ignored for the other dtypes.
  * causal != 0 masks key j for query i unless j <= i + Sk - Sq (the mask is
  * aligned to the last query and last key; with Sq == Sk it is the usual lower
  * triangle).  A query row that sees no key gets O = 0 and LSE = -inf.
@@ -111,6 +115,14 @@ typedef struct {
   float softmax_scale;
   int32_t causal;
   float q_descale, k_descale, v_descale;
+  /* FP8 only, optional: block descales, one float32 per 64 consecutive rows of
+   * each (batch, head) slice, [B][H][ceil(S / 64)] contiguous (H = Hq for q,
+   * Hkv for k and v), all three or none; when given they replace
+   * q/k/v_descale (the FlashAttention-3 page's block quantisation for fp8).
+   * The V descales should be powers of two (fa_fp8_quantize makes them so):
+   * a V tile's descale ratio to the slice's largest is folded into the
+   * probabilities before they are rounded to e4m3, exactly only then. */
+  const float *q_block_descale, *k_block_descale, *v_block_descale;
 } fa_fwd_params;
 
 int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);
@@ -151,6 +163,35 @@ typedef struct {
 size_t fa_bwd_workspace_size(int32_t B, int32_t Hq, int32_t Sq);
 
 int fa_bwd(const fa_bwd_params *p, fa_stream_t stream);
+
+/*
+ * fp8 inputs for fa_fwd: block-scaled E4M3FN codes, optionally of rotated rows
+ * (FlashAttention-3 page, producer/consumer pseudocode box, "FP8 path": block
+ * quantisation of Q/K/V and incoherent processing to keep fp8's error down).
+ *   x [B, H, S, d] in_dtype (FA_BF16 or FA_F16), strides x_strides
+ *   codes [B, H, S, d] E4M3FN bytes, strides codes_strides
+ *   scales [B, H, ceil(S / 64)] float32, contiguous: one per 64-row block
+ *   signs [d] float32 of +-1 on the device, or NULL for no rotation
+ * Per block: y = x, or y = (x * signs) H / sqrt(d) with H the Sylvester-
+ * Hadamard matrix (evaluated in float32 as the fast transform, stages 1, 2, 4,
+ * ..., d/2, then one multiply by fp32(1/sqrt(d))); s = the smallest power of
+ * two at or above fp32(absmax(y) / 448); code = E4M3FN(clamp(y / s, +-448))
+ * rounded to nearest even, or 0 when s == 0.
+ * The scales are the block descales fa_fwd takes.  Rotate Q and K with the
+ * same signs (Q K^T is unchanged) and leave V unrotated.  d must be 128.
+ */
+typedef struct {
+  const void *x;
+  void *codes;
+  float *scales;
+  const float *signs;
+  int32_t in_dtype; /* fa_dtype: FA_BF16 or FA_F16 */
+  int32_t B, H, S, d;
+  int64_t x_strides[3];     /* batch, head, row — in elements */
+  int64_t codes_strides[3]; /* batch, head, row — in bytes */
+} fa_fp8_quant_params;
+
+int fa_fp8_quantize(const fa_fp8_quant_params *p, fa_stream_t stream);
 
 /*
  * Cache formats.  Both store one code byte per element and one fp16 scale per
@@ -261,6 +302,7 @@ int fa_check_fwd_params(const fa_fwd_params *p);
 int fa_check_decode_params(const fa_decode_params *p);
 int fa_check_kv_append_params(const fa_kv_append_params *p);
 int fa_check_bwd_params(const fa_bwd_params *p);
+int fa_check_fp8_quant_params(const fa_fp8_quant_params *p);
 
 /* Static description of a status code. */
 const char *fa_status_string(int status);

@@ -119,8 +119,13 @@ def kv_append_ref(cache_codes, cache_scales, rows, positions, fmt: str):
 # quantisation of Q, K and V and with incoherent processing (the page gives no
 # formulas).  Readings taken here:
 #   * a block is 64 consecutive rows (tokens) of one (batch, head) slice, with
-#     one fp32 scale s = fp32(absmax / 448); s == 0 stores code 0 everywhere;
-#     code = E4M3FN(clamp(fp32(y) / s, +-448)), nearest even (as above);
+#     one fp32 scale s, the smallest power of two at or above fp32(absmax / 448)
+#     (shared power-of-two block exponents, as the OCP microscaling formats
+#     use); s == 0 stores code 0 everywhere; code = E4M3FN(clamp(y / s, +-448)),
+#     nearest even (y / s is exact).  A power of two keeps every ratio of two
+#     block scales a power of two, so an attention kernel can fold a V block's
+#     scale into the probabilities before their own e4m3 rounding without
+#     adding a rounding step;
 #   * incoherent processing multiplies each row of Q and of K by the same
 #     orthogonal matrix R = diag(signs) H / sqrt(d) (H the Sylvester-Hadamard
 #     matrix, signs a random +-1 vector) before quantising: (Q R)(K R)^T =
@@ -131,6 +136,14 @@ def kv_append_ref(cache_codes, cache_scales, rows, positions, fmt: str):
 #     fp32(1 / sqrt(d)), the order in which the codes are decided.
 
 FP8_BLOCK_ROWS = 64
+
+
+def pow2_at_or_above(v) -> np.ndarray:
+    """Smallest power of two >= v for float32 v > 0 (0 stays 0), in float32."""
+    v = np.asarray(v, dtype=np.float32)
+    m, e = np.frexp(v)  # v = m 2^e, m in [0.5, 1)
+    p = np.where(m == 0.5, np.ldexp(np.float32(1.0), e - 1), np.ldexp(np.float32(1.0), e))
+    return np.where(v > 0, p, np.float32(0.0)).astype(np.float32)
 
 
 def hadamard_rotate_fp32(x, signs) -> np.ndarray:
@@ -164,7 +177,7 @@ def quantize_fp8_blocks(x, signs=None, block_rows: int = FP8_BLOCK_ROWS):
         r0, r1 = blk * block_rows, min(S, (blk + 1) * block_rows)
         part = xf[:, :, r0:r1]
         amax = np.max(np.abs(part), axis=(2, 3)) if r1 > r0 else np.zeros((B, H), np.float32)
-        s = (amax.astype(np.float32) / np.float32(E4M3_QMAX)).astype(np.float32)
+        s = pow2_at_or_above((amax.astype(np.float32) / np.float32(E4M3_QMAX)).astype(np.float32))
         scales[:, :, blk] = s
         live = s > 0
         y = part / np.where(live, s, np.float32(1.0))[:, :, None, None]

@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 STRUCTS = [("fa_fwd_params", fa.FaFwdParams), ("fa_decode_params", fa.FaDecodeParams),
-           ("fa_kv_append_params", fa.FaKvAppendParams), ("fa_bwd_params", fa.FaBwdParams)]
+           ("fa_kv_append_params", fa.FaKvAppendParams), ("fa_bwd_params", fa.FaBwdParams),
+           ("fa_fp8_quant_params", fa.FaFp8QuantParams)]
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -289,3 +290,50 @@ def test_bwd_validator_errors(lib, mutate, status):
     p = good_bwd()
     mutate(p)
     assert fa.fa_check_bwd_params(p) == status
+
+
+def good_quant():
+    p = fa.FaFp8QuantParams()
+    p.x, p.codes, p.scales, p.signs = 0x10000, 0x20000, 0x30000, 0
+    p.in_dtype = fa.FA_BF16
+    p.B, p.H, p.S, p.d = 2, 4, 130, 128
+    p.x_strides = fa.I64x3(4 * 130 * 128, 130 * 128, 128)
+    p.codes_strides = fa.I64x3(4 * 130 * 128, 130 * 128, 128)
+    return p
+
+
+def test_fp8_quant_validator(lib):
+    assert fa.fa_check_fp8_quant_params(good_quant()) == fa.FA_OK
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "in_dtype", fa.FA_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "d", 64), fa.FA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "x", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "scales", 0), fa.FA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "scales", 0x30002), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "signs", 0x40001), fa.FA_ERR_ALIGNMENT),
+    (lambda p: setattr(p, "codes_strides", fa.I64x3(4 * 130 * 128, 130 * 128, 120)), fa.FA_ERR_ALIGNMENT),
+])
+def test_fp8_quant_validator_errors(lib, mutate, status):
+    p = good_quant()
+    mutate(p)
+    assert fa.fa_check_fp8_quant_params(p) == status
+
+
+def test_fwd_block_descales_validation(lib):
+    p = good_fwd()
+    p.in_dtype, p.out_dtype = fa.FA_FP8_E4M3, fa.FA_BF16
+    for name in ("q_strides", "k_strides", "v_strides"):
+        setattr(p, name, fa.I64x3(8 * 100 * 128, 100 * 128, 128))
+    p.o_strides = fa.I64x3(8 * 100 * 128, 100 * 128, 128)
+    p.q_block_descale = p.k_block_descale = p.v_block_descale = 0x50000
+    p.q_descale = p.k_descale = p.v_descale = 0.0  # ignored with block descales
+    assert fa.fa_check_fwd_params(p) == fa.FA_OK
+    p.v_block_descale = 0
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_INVALID_ARG
+    p.v_block_descale = 0x50002
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_ALIGNMENT
+    q = good_fwd()
+    q.q_block_descale = q.k_block_descale = q.v_block_descale = 0x50000
+    assert fa.fa_check_fwd_params(q) == fa.FA_ERR_INVALID_ARG  # bf16 inputs take no descales

@@ -1,0 +1,198 @@
+"""GPU parity of the fp8 accuracy variants:
+
+* fa_fp8_quantize (64-row block scales, optional random-sign Hadamard rotation)
+  against the oracle's quantiser: codes and scales bit-exact;
+* fa_fwd on fp8 codes with block descales against the float64 oracle fed the
+  same dequantised values (O within 8e-2, LSE within 1e-3);
+* the variants' error against exact attention of the unquantised bf16 inputs
+  on the long-context workload's outlier distribution (1 % of key rows x 8),
+  per-tensor scales versus block scales versus block scales with rotation.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 8e-2
+TOL_LSE = 1e-3
+
+
+def _signs(seed, d=128):
+    g = torch.Generator().manual_seed(seed)
+    return torch.where(torch.rand(d, generator=g) < 0.5, -1.0, 1.0).to(torch.float32)
+
+
+def gpu_quant(fa, x, signs=None):
+    B, H, S, d = x.shape
+    codes = torch.full((B, H, S, d), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B, H, (S + 63) // 64), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"fa_fp8_quantize x={tuple(x.shape)} {x.dtype} rotate={signs is not None}", flush=True)
+    fa.fa_fp8_quantize(x.cuda(), codes, scales, None if signs is None else signs.cuda())
+    torch.cuda.synchronize()
+    return codes.cpu(), scales.cpu()
+
+
+QUANT_CASES = [
+    # B, H, S, dtype, rotate
+    (1, 1, 1, torch.bfloat16, False),
+    (2, 3, 150, torch.bfloat16, False),
+    (2, 3, 150, torch.bfloat16, True),
+    (1, 2, 64, torch.float16, True),
+    (1, 2, 333, torch.float16, False),
+]
+
+
+@pytest.mark.parametrize("B,H,S,dt,rot", QUANT_CASES)
+def test_quantise_bit_exact(gpu, B, H, S, dt, rot):
+    g = torch.Generator().manual_seed(S + H)
+    x = torch.randn(B, H, S, 128, generator=g)
+    if S > 100:
+        x[0, 0, 70] *= 8.0  # an outlier row
+        x[0, H - 1, 64:128] = 0.0  # an all-zero block
+        x[B - 1, 0, 3, 9] = 300.0  # an outlier channel entry
+        x[B - 1, 0, 5] *= 1e-6  # tiny values (subnormal codes)
+    x = x.to(dt)
+    signs = _signs(S) if rot else None
+    codes, scales = gpu_quant(gpu, x, signs)
+    rc, rs = oracle.quantize_fp8_blocks(x, None if signs is None else signs.numpy())
+    assert np.array_equal(scales.numpy().view(np.uint32), rs.view(np.uint32))
+    bad = np.argwhere(codes.numpy() != rc)
+    assert len(bad) == 0, f"codes differ at {bad[:5].tolist()} (of {len(bad)})"
+
+
+def _fp8_inputs(cfg, seed, signs=None, block=True):
+    """bf16 draws of the configuration, quantised by the oracle; returns the GPU
+    tensors and the dequantised float64 values."""
+    x = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16", out_dtype=""), seed=seed)
+    out, deq = {}, {}
+    for n in ("q", "k", "v"):
+        s = signs if n in ("q", "k") else None
+        if block:
+            c, sc = oracle.quantize_fp8_blocks(x[n], s)
+            out[n], out[n + "_bs"] = torch.from_numpy(c), torch.from_numpy(sc)
+            deq[n] = oracle.dequant_fp8_blocks_fp64(c, sc)
+        else:
+            xf = x[n].float()
+            if s is not None:
+                xf = torch.from_numpy(oracle.hadamard_rotate_fp32(xf.numpy(), s))
+            c8, ts = fa_inputs.quantize_fp8_per_tensor(xf)
+            out[n], out[n + "_ts"] = c8.view(torch.uint8), ts
+            deq[n] = oracle.e4m3_decode(c8.view(torch.uint8)) * ts
+    return x, out, deq
+
+
+def run_fp8(fa, out, causal, block=True):
+    q, k, v = (out[n].cuda().view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
+    B, Hq, Sq, d = q.shape
+    o = torch.full((B, Hq, Sq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, Sq), float("nan"), device="cuda")
+    print(f"fa_fwd fp8 q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} block={block}", flush=True)
+    if block:
+        bds = tuple(out[n + "_bs"].cuda().contiguous() for n in ("q", "k", "v"))
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, block_descales=bds)
+    else:
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, q_descale=out["q_ts"], k_descale=out["k_ts"],
+                  v_descale=out["v_ts"])
+    torch.cuda.synchronize()
+    return o, lse
+
+
+FWD_CASES = [
+    # B, Hq, Hkv, Sq, Sk, causal
+    (1, 2, 2, 64, 64, False),
+    (2, 4, 2, 200, 200, True),
+    (1, 4, 1, 130, 333, False),
+    (1, 2, 2, 300, 129, True),
+    (1, 8, 8, 512, 512, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", FWD_CASES)
+def test_block_descale_forward(gpu, B, Hq, Hkv, Sq, Sk, causal):
+    # the fp8 workload's distribution (N(0,1) draws, no outlier rows)
+    cfg = fa_inputs.FwdConfig("t", "fp8", B, Hq, Hkv, Sq, Sk, 128, causal)
+    _, out, deq = _fp8_inputs(cfg, seed=Sq + Sk)
+    o, lse = run_fp8(gpu, out, causal)
+    ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], causal)
+    og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert not np.isnan(og).any()
+    assert float(np.max(np.abs(og - ro))) <= TOL_O
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert float(np.max(np.abs(lg[fin] - rl[fin]))) <= TOL_LSE
+
+
+def _variant_errors(fa, cfg, channel_outlier=False, seed=11):
+    """max |O - exact| and max |LSE - exact| of per-tensor, block and
+    block + rotation fp8 attention, exact = the float64 oracle on the bf16
+    inputs before quantisation."""
+    signs = _signs(5).numpy()
+    base = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16", out_dtype=""), seed=seed)
+    if channel_outlier:  # the alternative reading: one key channel x 8 in every row
+        base["k"] = (base["k"].float() * torch.where(torch.arange(128) == 5, 8.0, 1.0)).to(torch.bfloat16)
+    ro, rl = oracle.attention_fp64(base["q"], base["k"], base["v"], cfg.causal)
+    errs = {}
+    for name, block, sg in (("per-tensor", False, None), ("block", True, None), ("block+rotation", True, signs)):
+        out = {}
+        for n in ("q", "k", "v"):
+            s = sg if n in ("q", "k") else None
+            if block:
+                c, sc = oracle.quantize_fp8_blocks(base[n], s)
+                out[n], out[n + "_bs"] = torch.from_numpy(c), torch.from_numpy(sc)
+            else:
+                c8, ts = fa_inputs.quantize_fp8_per_tensor(base[n].float())
+                out[n], out[n + "_ts"] = c8.view(torch.uint8), ts
+        o, lse = run_fp8(fa, out, cfg.causal, block=block)
+        errs[name] = (float(np.max(np.abs(o.double().cpu().numpy() - ro))),
+                      float(np.max(np.abs(lse.double().cpu().numpy() - rl))))
+    return errs
+
+
+def test_variants_against_exact_on_outliers(gpu):
+    """fp8 error against exact attention of the unquantised bf16 inputs, GQA 4/1,
+    causal, S = 1024, for the long-context workload's outliers read two ways:
+    1 % of key rows x 8 (the reading the workload uses), where block scales cut
+    the error of per-tensor scales; and one key channel x 8, where the rotation
+    cuts it further.  Against exact attention the quantisation error of Q, K
+    and V adds to the kernel's own, so these errors exceed the 8e-2 bar, which
+    is stated against an oracle fed the same codes; they are printed for the
+    record."""
+    cfg = fa_inputs.FwdConfig("t", "fp8", 1, 4, 1, 1024, 1024, 128, True, outlier_frac=0.01)
+    rows = _variant_errors(gpu, cfg)
+    chan = _variant_errors(gpu, dataclasses.replace(cfg, outlier_frac=0.0), channel_outlier=True)
+    print("row outliers: max |O - exact|, max |LSE - exact|:", rows)
+    print("channel outlier: max |O - exact|, max |LSE - exact|:", chan)
+    assert rows["block"][0] < rows["per-tensor"][0]
+    assert chan["block+rotation"][0] < chan["block"][0]
+
+
+def test_quantise_then_forward_full_size_sampled(gpu):
+    """The fp8 workload's shape (B=8, H=16, S=4096) quantised on the GPU with
+    block scales and rotation, then the block-descale forward; sampled heads
+    against the oracle on the dequantised codes."""
+    cfg = fa_inputs.CONFIGS["fp8_b8_h16_s4096"]
+    x = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16", out_dtype=""), seed=0, device="cuda")
+    signs = _signs(7).cuda()
+    out = {}
+    for n in ("q", "k", "v"):
+        t = x[n]
+        codes = torch.empty(t.shape, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(t.shape[0], t.shape[1], t.shape[2] // 64, dtype=torch.float32, device="cuda")
+        gpu.fa_fp8_quantize(t, codes, sc, signs if n != "v" else None)
+        out[n], out[n + "_bs"] = codes, sc
+    o, lse = run_fp8(gpu, out, False)
+    for b, h in [(0, 0), (5, 11), (7, 15)]:
+        deq = {n: oracle.dequant_fp8_blocks_fp64(out[n][b:b + 1, h:h + 1].cpu().numpy(),
+                                                 out[n + "_bs"][b:b + 1, h:h + 1].cpu().numpy())
+               for n in ("q", "k", "v")}
+        rows = [0, 1, 2047, 4095]
+        ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], False, rows=rows)
+        assert float(np.max(np.abs(o[b, h, rows].double().cpu().numpy() - ro[0, 0]))) <= TOL_O
+        assert float(np.max(np.abs(lse[b, h, rows].double().cpu().numpy() - rl[0, 0]))) <= TOL_LSE

@@ -1,4 +1,4 @@
-"""Pins of the oracle's fp8 prefill-input quantiser (64-row block scales) and
+"""Pins of the oracle's fp8 prefill-input quantiser (64-row power-of-two block scales) and
 its random-sign Hadamard rotation: the rotation against scipy's Hadamard
 matrix and its closed forms and invariances, the block quantiser against
 torch's float8_e4m3fn cast and its error bound, and planted mistakes.  CPU only."""
@@ -62,8 +62,13 @@ def test_block_quantiser_matches_torch_cast_and_bounds():
         r0, r1 = 64 * blk, min(150, 64 * blk + 64)
         part = xf[:, :, r0:r1]
         amax = part.abs().amax(dim=(2, 3))
-        s = (amax / 448.0).numpy().astype(np.float32)
-        assert np.array_equal(scales[:, :, blk], s)
+        q = (amax / 448.0).numpy().astype(np.float32)
+        s = scales[:, :, blk]
+        # a power of two in [absmax/448, 2 absmax/448), or 0 for a zero block
+        live = q > 0
+        assert np.all(s[~live] == 0)
+        mant, _ = np.frexp(s[live])
+        assert np.all(mant == 0.5) and np.all(s[live] >= q[live]) and np.all(s[live] < 2 * q[live])
         safe = torch.from_numpy(np.where(s > 0, s, 1.0).astype(np.float32))
         ref = (part / safe[:, :, None, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         ref = np.where((s > 0)[:, :, None, None], ref, 0)
@@ -75,8 +80,9 @@ def test_block_quantiser_matches_torch_cast_and_bounds():
     e = np.clip(np.floor(np.log2(np.where(y > 0, y, 1))), -6, 8)
     step = np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :150, None]
     assert np.all(np.abs(xf.double().numpy() - deq) <= (np.exp2(e - 4) + y * 2e-7) * step + 1e-30)
-    top = [int(codes[0, 0, 64:128].reshape(-1)[np.argmax(np.abs(xf[0, 0, 64:128].numpy()).reshape(-1))])]
-    assert all((c & 0x7F) == 0x7E for c in top)
+    # the absmax element of a live block lands in [224, 448]
+    top = int(codes[0, 0, 64:128].reshape(-1)[np.argmax(np.abs(xf[0, 0, 64:128].numpy()).reshape(-1))])
+    assert 224.0 <= abs(oracle.e4m3_decode(np.array([top], dtype=np.uint8))[0]) <= 448.0
 
 
 def test_rotated_quantisation_reduces_channel_outlier_error():
@@ -121,7 +127,14 @@ def test_planted_fp8_quantiser_mistakes_are_caught(kind):
         codes, scales = oracle.quantize_fp8_blocks(x, block_rows=63)
     if kind == "per_tensor":
         amax = float(x.abs().max())
-        scales = np.full((1, 2, 3), amax / 448, dtype=np.float32)
-    want = np.stack([x[:, :, 64 * b:64 * b + 64].abs().amax(dim=(2, 3)).numpy() / 448 for b in range(3)], axis=-1)
-    caught |= scales.shape != want.shape or bool(np.max(np.abs(scales - want)) > 1e-7 * np.max(want))
+        scales = np.full((1, 2, 3), oracle.quant.pow2_at_or_above(np.float32(amax / 448)), dtype=np.float32)
+    q = np.stack([x[:, :, 64 * b:64 * b + 64].abs().amax(dim=(2, 3)).numpy() / 448 for b in range(3)], axis=-1)
+    caught |= scales.shape != q.shape or bool(np.any(scales < q) or np.any(scales >= 2 * q))
     assert caught, kind
+
+
+def test_pow2_at_or_above_closed_forms():
+    f = oracle.quant.pow2_at_or_above
+    v = np.array([1.0, 0.75, 0.5, 3.0, 2.0 ** -130, 1e-45, 0.0, 6.1e4], dtype=np.float32)
+    want = np.array([1.0, 1.0, 0.5, 4.0, 2.0 ** -130, 2.0 ** -149, 0.0, 65536.0], dtype=np.float32)
+    assert np.array_equal(f(v), want)

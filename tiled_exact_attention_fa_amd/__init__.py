@@ -12,9 +12,11 @@ been built, load() raises.
     fa_decode_workspace_size(B, Hq, d, num_splits)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=False, ...)
     fa_bwd_workspace_size(B, Hq, Sq)
+    fa_fp8_quantize(x, codes, scales, signs=None)
     fa_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=None, ...)
     fa_check_fwd_params(params) / fa_check_bwd_params(params) /
-    fa_check_decode_params(params) / fa_check_kv_append_params(params)
+    fa_check_decode_params(params) / fa_check_kv_append_params(params) /
+    fa_check_fp8_quant_params(params)
     fa_status_string(status) / fa_last_error()
 
 Build with ``python -m tiled_exact_attention_fa_amd.build``.
@@ -50,6 +52,20 @@ class FaFwdParams(ctypes.Structure):
         ("lse_strides", I64x2),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
         ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+        ("q_block_descale", ctypes.c_void_p), ("k_block_descale", ctypes.c_void_p),
+        ("v_block_descale", ctypes.c_void_p),
+    ]
+
+
+class FaFp8QuantParams(ctypes.Structure):
+    """Mirror of fa_fp8_quant_params."""
+
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("signs", ctypes.c_void_p),
+        ("in_dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("S", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("x_strides", I64x3), ("codes_strides", I64x3),
     ]
 
 
@@ -105,8 +121,9 @@ class FaKvAppendParams(ctypes.Structure):
 
 
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_kvq", "fa_decode_workspace_size",
-           "fa_kv_append", "fa_check_fwd_params", "fa_check_bwd_params", "fa_check_decode_params",
-           "fa_check_kv_append_params", "fa_status_string", "fa_last_error"]
+           "fa_kv_append", "fa_fp8_quantize", "fa_check_fwd_params", "fa_check_bwd_params",
+           "fa_check_decode_params", "fa_check_kv_append_params", "fa_check_fp8_quant_params",
+           "fa_status_string", "fa_last_error"]
 
 
 class FaError(RuntimeError):
@@ -137,6 +154,10 @@ def load(path: str | None = None):
     lib.fa_check_fwd_params.restype = ctypes.c_int
     lib.fa_check_decode_params.argtypes = [ctypes.POINTER(FaDecodeParams)]
     lib.fa_check_decode_params.restype = ctypes.c_int
+    lib.fa_fp8_quantize.argtypes = [ctypes.POINTER(FaFp8QuantParams), ctypes.c_void_p]
+    lib.fa_fp8_quantize.restype = ctypes.c_int
+    lib.fa_check_fp8_quant_params.argtypes = [ctypes.POINTER(FaFp8QuantParams)]
+    lib.fa_check_fp8_quant_params.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [ctypes.POINTER(FaBwdParams), ctypes.c_void_p]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_check_bwd_params.argtypes = [ctypes.POINTER(FaBwdParams)]
@@ -169,6 +190,10 @@ def fa_check_fwd_params(params: FaFwdParams) -> int:
 
 def fa_check_decode_params(params: FaDecodeParams) -> int:
     return load().fa_check_decode_params(ctypes.byref(params))
+
+
+def fa_check_fp8_quant_params(params: FaFp8QuantParams) -> int:
+    return load().fa_check_fp8_quant_params(ctypes.byref(params))
 
 
 def fa_check_bwd_params(params: FaBwdParams) -> int:
@@ -217,7 +242,7 @@ def _require_dense_d(name, t):
 
 
 def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
-               q_descale=1.0, k_descale=1.0, v_descale=1.0) -> FaFwdParams:
+               q_descale=1.0, k_descale=1.0, v_descale=1.0, block_descales=None) -> FaFwdParams:
     """fa_fwd_params for BHSD-indexed tensors q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d],
     o [B,Hq,Sq,d], lse [B,Hq,Sq] (any strides with a unit head-dim stride)."""
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
@@ -236,13 +261,19 @@ def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
     p.softmax_scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
     p.causal = 1 if causal else 0
     p.q_descale, p.k_descale, p.v_descale = float(q_descale), float(k_descale), float(v_descale)
+    if block_descales is not None:  # (q, k, v) float32 tensors [B, H, ceil(S / 64)], contiguous
+        for t in block_descales:
+            if not t.is_contiguous():
+                raise ValueError("block descales must be contiguous")
+        p.q_block_descale, p.k_block_descale, p.v_block_descale = (_ptr(t) for t in block_descales)
     return p
 
 
 def fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None,
-           q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None) -> None:
-    """Enqueue the prefill forward on torch's current stream (or ``stream``)."""
-    p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale)
+           q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None, block_descales=None) -> None:
+    """Enqueue the prefill forward on torch's current stream (or ``stream``).
+    ``block_descales``: optional (q, k, v) per-64-row descales for fp8 inputs."""
+    p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale, block_descales)
     st = load().fa_fwd(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd", fa_last_error())
@@ -260,6 +291,31 @@ def _kv_format(cache, kv_format):
     if cache.dtype in (torch.float8_e4m3fn, torch.uint8):
         return FA_KV_FP8_E4M3_TOKHEAD_F16SCALE
     raise TypeError(f"cannot infer the cache format from dtype {cache.dtype}")
+
+
+def fp8_quant_params(x, codes, scales, signs=None) -> FaFp8QuantParams:
+    """fa_fp8_quant_params for x [B,H,S,d] bf16/fp16, codes [B,H,S,d] uint8 or
+    float8_e4m3fn, scales [B,H,ceil(S/64)] float32 contiguous, signs [d] float32."""
+    _require_dense_d("x", x)
+    _require_dense_d("codes", codes)
+    if not scales.is_contiguous():
+        raise ValueError("scales must be contiguous")
+    B, H, S, d = x.shape
+    p = FaFp8QuantParams()
+    p.x, p.codes, p.scales, p.signs = _ptr(x), _ptr(codes), _ptr(scales), _ptr(signs)
+    p.in_dtype = _dtype_code(x)
+    p.B, p.H, p.S, p.d = B, H, S, d
+    p.x_strides = I64x3(*x.stride()[:3])
+    p.codes_strides = I64x3(*codes.stride()[:3])
+    return p
+
+
+def fa_fp8_quantize(x, codes, scales, signs=None, stream=None) -> None:
+    """Enqueue the block-scaled fp8 quantisation (optionally rotated) of x."""
+    p = fp8_quant_params(x, codes, scales, signs)
+    st = load().fa_fp8_quantize(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fp8_quantize", fa_last_error())
 
 
 def bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=None,

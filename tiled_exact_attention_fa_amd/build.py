@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["fa_fwd_mfma.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_kv_append.hip", "fa_bwd.hip"]
+HIP_SOURCES = ["fa_fwd_mfma.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_kv_append.hip", "fa_bwd.hip", "fa_fp8_quant.hip"]
 CPP_SOURCES = ["fa_check.cpp", "fa_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]

@@ -29,3 +29,10 @@ extern "C" int fa_bwd(const fa_bwd_params *p, fa_stream_t stream) {
   if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return FA_OK;
   return fa_launch_bwd(p, stream);
 }
+
+extern "C" int fa_fp8_quantize(const fa_fp8_quant_params *p, fa_stream_t stream) {
+  const int st = fa_check_fp8_quant_params(p);
+  if (st != FA_OK) return st;
+  if (p->B == 0 || p->S == 0) return FA_OK;
+  return fa_launch_fp8_quantize(p, stream);
+}

@@ -91,7 +91,15 @@ extern "C" int fa_check_fwd_params(const fa_fwd_params *p) {
     return fa_set_error(FA_ERR_UNSUPPORTED, "dtype pair in=%d out=%d not supported", in, out);
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
     return fa_set_error(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (in == FA_FP8_E4M3) {
+  const int nblk = (p->q_block_descale != nullptr) + (p->k_block_descale != nullptr) + (p->v_block_descale != nullptr);
+  if (nblk != 0 && nblk != 3)
+    return fa_set_error(FA_ERR_INVALID_ARG, "block descales: give all three of q, k, v or none");
+  if (nblk == 3) {
+    if (in != FA_FP8_E4M3) return fa_set_error(FA_ERR_INVALID_ARG, "block descales need fp8 inputs");
+    for (const float *bp : {p->q_block_descale, p->k_block_descale, p->v_block_descale})
+      if ((reinterpret_cast<uintptr_t>(bp) & 3u) != 0)
+        return fa_set_error(FA_ERR_ALIGNMENT, "block descales not 4-byte aligned");
+  } else if (in == FA_FP8_E4M3) {
     const float ds[3] = {p->q_descale, p->k_descale, p->v_descale};
     for (float x : ds)
       if (!(std::isfinite(x) && x > 0.f))
@@ -246,5 +254,27 @@ extern "C" int fa_check_bwd_params(const fa_bwd_params *p) {
   if (p->workspace == nullptr || p->workspace_bytes < need)
     return fa_set_error(FA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", p->workspace_bytes, need);
   if (!aligned16(p->workspace)) return fa_set_error(FA_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  return FA_OK;
+}
+
+extern "C" int fa_check_fp8_quant_params(const fa_fp8_quant_params *p) {
+  fa_clear_error();
+  if (p == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "params is NULL");
+  if (p->in_dtype != FA_BF16 && p->in_dtype != FA_F16)
+    return fa_set_error(FA_ERR_UNSUPPORTED, "quantise input dtype %d not supported (bf16 or fp16)", p->in_dtype);
+  if (p->B < 0 || p->H <= 0 || p->S < 0 || p->d <= 0)
+    return fa_set_error(FA_ERR_INVALID_ARG, "bad sizes B=%d H=%d S=%d d=%d", p->B, p->H, p->S, p->d);
+  if (p->d != 128) return fa_set_error(FA_ERR_UNSUPPORTED, "quantise head dim %d not supported (128)", p->d);
+  if (static_cast<int64_t>(p->B) * p->H * ((p->S + 63) / 64) >= (int64_t(1) << 31))
+    return fa_set_error(FA_ERR_UNSUPPORTED, "too many blocks");
+  if (p->B == 0 || p->S == 0) return FA_OK;
+  int st;
+  if ((st = check_tensor("x", p->x, p->x_strides, 3, p->S, p->d, 2)) != FA_OK) return st;
+  if ((st = check_tensor("codes", p->codes, p->codes_strides, 3, p->S, p->d, 1)) != FA_OK) return st;
+  if (p->scales == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "scales is NULL");
+  if ((reinterpret_cast<uintptr_t>(p->scales) & 3u) != 0)
+    return fa_set_error(FA_ERR_ALIGNMENT, "scales not 4-byte aligned");
+  if (p->signs != nullptr && (reinterpret_cast<uintptr_t>(p->signs) & 3u) != 0)
+    return fa_set_error(FA_ERR_ALIGNMENT, "signs not 4-byte aligned");
   return FA_OK;
 }

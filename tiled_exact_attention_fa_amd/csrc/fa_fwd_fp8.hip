@@ -1,5 +1,5 @@
-// Prefill forward for fp8 (OCP E4M3FN) Q/K/V with per-tensor descales,
-// bf16 output, on gfx950 8-bit matrix cores.
+// Prefill forward for fp8 (OCP E4M3FN) Q/K/V with per-tensor or per-block
+// descales, bf16 output, on gfx950 8-bit matrix cores.
 //
 // Method: as the 16-bit kernel (FlashAttention interview canvas, panel 1
 // "one-sentence answer" and "online softmax key state" boxes), with both
@@ -25,6 +25,16 @@
 //     256 rows; P V of tile t carries the first half of tile t+1's softmax
 //     between its MFMAs and S^T of tile t+2 the second half, with the K/V
 //     staging riding along and one barrier per tile.
+//   * Block descales (one per 64 rows of a (batch, head) slice; the
+//     FlashAttention-3 page's block quantisation for fp8) cost no work per
+//     element: the query row's descale sits in the lane's score constant; a K
+//     tile's descale multiplies that constant once per tile (the tiles are the
+//     64-row blocks); a V tile's descale sv enters the exponent as
+//     log2(sv / sv_max), so P is rounded to e4m3 already weighted by it, and
+//     the tile's row sum is divided by the same ratio once; sv_max, the
+//     largest V descale of the slice, multiplies the output in the epilogue.
+//     The descales of tile j travel with the staging unit loaded two
+//     iterations ahead.
 #include "fa_device.hpp"
 #include "fa_fwd_common.hpp"
 #include "fa_internal.h"
@@ -73,9 +83,15 @@ __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
 
 }  // namespace f8
 
-template <bool CAUSAL>
+// Per-block descales: [B][H][nb] float32, one per 64 rows
+struct Fp8BlockScales {
+  const float *q, *k, *v;
+  int nbq, nbk, Hkv;
+};
+
+template <bool CAUSAL, bool BLK>
 __global__ __attribute__((amdgpu_flat_work_group_size(f8::NT, f8::NT), amdgpu_waves_per_eu(2)))
-void fwd_fp8_kernel(const FwdArgs a) {
+void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   using namespace f8;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   unsigned char *kbuf = lds;                 // [2][BC][KROW]
@@ -125,6 +141,45 @@ void fwd_fp8_kernel(const FwdArgs a) {
   u32x4 kreg[2];
   unsigned vreg[2][4];
   auto load_k_to = [&](u32x4 &dst, int j) { dst = buf_load16(tile_rsrc(kbase, a.k_ss, a.k_ext, j), koff); };
+  // ---- block descales: the lane's query-row descale in the score constant,
+  // the largest V descale of the slice, and per-tile descales loaded ahead
+  // (vector buffer loads, so their waits stay in order with the staging) ----
+  float cs_base = a.c;
+  float sv_max = 1.f;
+  float skr[2] = {1.f, 1.f}, svr[2] = {1.f, 1.f};
+  // (without block descales these are never used; they point at the K/V codes)
+  const float *kbs = BLK ? bs.k + static_cast<long long>(b * bs.Hkv + hk) * bs.nbk : static_cast<const float *>(a.k);
+  const float *vbs = BLK ? bs.v + static_cast<long long>(b * bs.Hkv + hk) * bs.nbk : static_cast<const float *>(a.v);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(kbs, BLK ? 4u * bs.nbk : 0u);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vbs, BLK ? 4u * bs.nbk : 0u);
+  if constexpr (BLK) {
+    const float *qbs = bs.q + static_cast<long long>(b * a.Hq + hq) * bs.nbq;
+    cs_base = a.c * fmaxf(qbs[min(row, a.Sq - 1) / BC], 1e-30f);
+    float vm = 0.f;
+    for (int j = lane; j < bs.nbk; j += 64) vm = fmaxf(vm, vbs[j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vm = fmaxf(vm, __shfl_xor(vm, off, 64));
+    sv_max = vm > 0.f ? vm : 1.f;
+  }
+  auto load_scales = [&](int set, int j) {
+    if constexpr (BLK) {
+      skr[set] = __builtin_bit_cast(float, buf_load4(rks, 4u * static_cast<unsigned>(j)));
+      svr[set] = __builtin_bit_cast(float, buf_load4(rvs, 4u * static_cast<unsigned>(j)));
+    }
+  };
+  // score constant, log2 of the V-descale ratio and its inverse, of the tile
+  // whose softmax runs next
+  float cscale = a.c;
+  float lr_t = 0.f, inv_t = 1.f;
+  auto tile_consts = [&](float sk, float sv) {
+    if constexpr (BLK) {
+      cscale = cs_base * fmaxf(sk, 1e-30f);
+      const float ratio = fmaxf(sv / sv_max, 0x1p-20f);
+      lr_t = __log2f(ratio);
+      inv_t = 1.f / ratio;
+    }
+  };
+
   auto load_v = [&](int set, int j) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
 #pragma unroll
@@ -176,8 +231,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
   float l_run = 0.f;
   float alpha_p = 1.f;
   bool move_p = false;
-  float m_use = 0.f;  // running max minus log2 kPScale
-  const float cscale = a.c;
+  float m_use = 0.f;  // running max minus log2 kPScale (minus the tile's V-descale log ratio)
 
   // accumulator (block mb, register i, half h) is key 32h + 16mb + i
   auto mask = [&](f32x16 s[2], int j) {
@@ -226,7 +280,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
       alpha_p = move_p ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
       m_run = m_new;
       // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
-      m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale;
+      m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale - lr_t;
       pin(alpha_p);
       pin(m_use);
     } else if constexpr (st < 15) {
@@ -282,7 +336,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
           pin(qa[i]);
         }
       } else {
-        l_run = __builtin_fmaf(l_run, alpha_p, (qa[0] + qa[2]) + (qa[1] + qa[3]));
+        l_run = __builtin_fmaf(l_run, alpha_p, ((qa[0] + qa[2]) + (qa[1] + qa[3])) * inv_t);
         pin(l_run);
       }
     }
@@ -380,7 +434,9 @@ void fwd_fp8_kernel(const FwdArgs a) {
   // softmax, S^T of tile 1 formed, staging units 0 and 1 in flight; the first
   // tiles and the Q rows are fetched together ----
   // unit u = (K of tile u+3, V of tile u+1), written to LDS in iteration u
+  // (with block descales, the unit also brings those of tile u + 1)
   auto load_unit = [&](int set, int u) {
+    load_scales(set, u + 1);
     load_k_to(kreg[set], u + 3);
     load_v(set, u + 1);
   };
@@ -398,6 +454,10 @@ void fwd_fp8_kernel(const FwdArgs a) {
       const unsigned base = ok ? row * a.q_ss + 64u * h + 32u * s : kOOB;
       qf[s] = join(buf_load16(rq, base), buf_load16(rq, ok ? base + 16u : kOOB));
     }
+  }
+  if constexpr (BLK) {  // tile 0's descales, before set 0 is reused for tile 1
+    load_scales(0, 0);
+    tile_consts(skr[0], svr[0]);
   }
   store_k_from(k0, 0);
   store_k_from(k1, 1);
@@ -428,6 +488,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
     // V of tile t and K of tile t+2 both sit in buffer cur
     u32x4 vf[RA][2], kf[RA][2];
     v_init(cur, vf);  // first, so the reads overlap the rescale and mask
+    tile_consts(skr[cur], svr[cur]);  // of tile t+1, loaded with unit t-1 (or in the prologue)
     rescale_o();
     mask(sc[nxt], t + 1);
     block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
@@ -472,7 +533,7 @@ void fwd_fp8_kernel(const FwdArgs a) {
   // store writes whole rows ----
   const float l_tot = l_run + swap_halves(l_run);
   {
-    const float inv = l_tot > 0.f ? a.o_mul / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (BLK ? sv_max : a.o_mul) / l_tot : 0.f;
     __bf16 *slab = reinterpret_cast<__bf16 *>(lds) + wave * 32 * ORow;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -497,9 +558,9 @@ void fwd_fp8_kernel(const FwdArgs a) {
     a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PScale) * kLn2 : neg_inf();
 }
 
-template <bool CAUSAL> int launch_fp8(const FwdArgs &args, hipStream_t stream) {
+template <bool CAUSAL, bool BLK> int launch_fp8(const FwdArgs &args, const Fp8BlockScales &bs, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
-  hipLaunchKernelGGL(fwd_fp8_kernel<CAUSAL>, dim3(grid), dim3(f8::NT), 0, stream, args);
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, BLK>), dim3(grid), dim3(f8::NT), 0, stream, args, bs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "fp8 launch: %s", hipGetErrorString(e));
   return FA_OK;
@@ -510,7 +571,16 @@ template <bool CAUSAL> int launch_fp8(const FwdArgs &args, hipStream_t stream) {
 int fa_launch_fwd_fp8(const fa_fwd_params *p, void *stream) {
   using namespace fa;
   if (p->d != 128) return fa_set_error(FA_ERR_UNSUPPORTED, "fp8 forward supports d = 128 only");
-  const FwdArgs args = make_fwd_args(p, f8::BR, 1);
+  FwdArgs args = make_fwd_args(p, f8::BR, 1);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return p->causal ? launch_fp8<true>(args, s) : launch_fp8<false>(args, s);
+  if (p->q_block_descale != nullptr) {
+    // block descales replace the per-tensor ones
+    args.c = p->softmax_scale * 1.4426950408889634f;
+    args.o_mul = 1.f;
+    const Fp8BlockScales bs{p->q_block_descale, p->k_block_descale, p->v_block_descale,
+                            (p->Sq + f8::BC - 1) / f8::BC, (p->Sk + f8::BC - 1) / f8::BC, p->Hkv};
+    return p->causal ? launch_fp8<true, true>(args, bs, s) : launch_fp8<false, true>(args, bs, s);
+  }
+  const Fp8BlockScales none{};
+  return p->causal ? launch_fp8<true, false>(args, none, s) : launch_fp8<false, false>(args, none, s);
 }

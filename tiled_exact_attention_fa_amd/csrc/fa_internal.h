@@ -18,3 +18,4 @@ int fa_launch_fwd_fp8(const fa_fwd_params *p, void *stream);
 int fa_launch_decode(const fa_decode_params *p, void *stream);
 int fa_launch_kv_append(const fa_kv_append_params *p, void *stream);
 int fa_launch_bwd(const fa_bwd_params *p, void *stream);
+int fa_launch_fp8_quantize(const fa_fp8_quant_params *p, void *stream);
