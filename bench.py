@@ -9,11 +9,12 @@ S=2048, d=128 with LSE output; its TFLOP/s counts 4*d flops per visible
 (query, key) pair (S*(S+1)/2 pairs per head under the causal mask).  The other
 workloads are timed the same way and reported under "workloads": long-context
 GQA prefill, fp8 prefill and the backward of the two causal bf16 workloads in
-TFLOP/s (10 d flops per visible pair for the backward); int8-KV and fp8-KV split decode, the
-decode with a bf16 residual window, and the quantise-on-append of a 4096-token
-chunk in GB/s of the bytes the method must move (codes + scales + window +
-query + output + LSE for decode; rows read and codes + scales written for the
-append).
+TFLOP/s (10 d flops per visible pair for the backward), the fp8 prefill on
+64-row block-scaled, rotated codes in TFLOP/s; int8-KV and fp8-KV split decode, the
+decode with a bf16 residual window, the quantise-on-append of a 4096-token
+chunk and the fp8 block quantiser of one prefill's Q, K and V in GB/s of the
+bytes the method must move (codes + scales + window + query + output + LSE for
+decode; rows read and codes + scales written for the append and the quantiser).
 
 Timing uses HIP events on the stream the kernels are launched on (torch's
 current stream), bracketed by device synchronisations, after at least W
@@ -110,7 +111,17 @@ def bwd_hbm_bytes(cfg) -> int:
     return 3 * q + 2 * kv + cfg.B * cfg.Hq * cfg.Sq * 4 + q + 2 * kv
 
 
+def quant_bytes(cfg) -> int:
+    """Block quantiser over Q, K and V: bf16 rows read once, 1-byte codes and one
+    float32 scale per 64-row block written once (the 128 signs are not counted)."""
+    n = cfg.B * cfg.H * cfg.S * cfg.d
+    blocks = cfg.B * cfg.H * ((cfg.S + 63) // 64)
+    return 3 * (n * 2 + n + blocks * 4)
+
+
 def algorithmic_bytes(cfg) -> int:
+    if isinstance(cfg, fa_inputs.QuantConfig):
+        return quant_bytes(cfg)
     if isinstance(cfg, fa_inputs.BwdConfig):
         return bwd_hbm_bytes(cfg)
     if isinstance(cfg, fa_inputs.DecodeConfig):
@@ -121,7 +132,7 @@ def algorithmic_bytes(cfg) -> int:
 
 
 def workload(name):
-    for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS):
+    for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -174,6 +185,54 @@ def _fwd_runner(cfg, seed=0):
     def run():
         fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale,
                   q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
+
+    return run
+
+
+def _quantise_block_fp8(fa, x, signs):
+    """q, k, v (bf16 on the GPU) -> codes and 64-row block scales, Q and K rotated
+    when signs are given, by the library's quantiser."""
+    import torch
+
+    out = {}
+    for n in ("q", "k", "v"):
+        t = x[n]
+        codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+        sc = torch.empty(t.shape[0], t.shape[1], (t.shape[2] + 63) // 64, dtype=torch.float32, device=t.device)
+        fa.fa_fp8_quantize(t, codes, sc, signs if n != "v" else None)
+        out[n], out[n + "_bs"] = codes, sc
+    return out
+
+
+def _fp8_block_runner(cfg, seed=0):
+    import dataclasses
+
+    import torch
+
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16"), seed=seed, device="cuda")
+    signs = fa_inputs.make_rotation_signs(cfg.d, seed, "cuda") if cfg.rotate else None
+    c = _quantise_block_fp8(fa, x, signs)
+    del x
+    q, k, v = (c[n].view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
+    bds = (c["q_bs"], c["k_bs"], c["v_bs"])
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda")
+
+    def run():
+        fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale, block_descales=bds)
+
+    return run
+
+
+def _quant_runner(cfg, seed=0):
+    import tiled_exact_attention_fa_amd as fa
+
+    x = fa_inputs.make_quant_inputs(cfg, seed=seed, device="cuda")
+
+    def run():
+        _quantise_block_fp8(fa, x, x["signs"])
 
     return run
 
@@ -237,10 +296,13 @@ KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_device.hpp"],
     "append": ["fa_kv_append.hip", "fa_device.hpp"],
     "bwd": ["fa_bwd.hip", "fa_device.hpp"],
+    "quant": ["fa_fp8_quant.hip", "fa_device.hpp"],
 }
 
 
 def kernel_family(cfg) -> str:
+    if isinstance(cfg, fa_inputs.QuantConfig):
+        return "quant"
     if isinstance(cfg, fa_inputs.DecodeConfig):
         return "decode"
     if isinstance(cfg, fa_inputs.AppendConfig):
@@ -280,8 +342,13 @@ def measure(name, steps, warmup):
     cfg = workload(name)
     import torch
 
-    if isinstance(cfg, (fa_inputs.DecodeConfig, fa_inputs.AppendConfig)):
-        run = _decode_runner(cfg) if isinstance(cfg, fa_inputs.DecodeConfig) else _append_runner(cfg)
+    if isinstance(cfg, (fa_inputs.DecodeConfig, fa_inputs.AppendConfig, fa_inputs.QuantConfig)):
+        if isinstance(cfg, fa_inputs.DecodeConfig):
+            run = _decode_runner(cfg)
+        elif isinstance(cfg, fa_inputs.AppendConfig):
+            run = _append_runner(cfg)
+        else:
+            run = _quant_runner(cfg)
         ms, wall = _time_region(run, steps, warmup)
         work = algorithmic_bytes(cfg)
         gbs = work / (ms * 1e-3) / 1e9
@@ -290,7 +357,12 @@ def measure(name, steps, warmup):
                             "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic(name)}}
     else:
         bwd = isinstance(cfg, fa_inputs.BwdConfig)
-        run = _bwd_runner(cfg) if bwd else _fwd_runner(cfg)
+        if bwd:
+            run = _bwd_runner(cfg)
+        elif isinstance(cfg, fa_inputs.Fp8BlockConfig):
+            run = _fp8_block_runner(cfg)
+        else:
+            run = _fwd_runner(cfg)
         ms, wall = _time_region(run, steps, warmup)
         work = bwd_flops(cfg) if bwd else fwd_flops(cfg)
         tf = work / (ms * 1e-3) / 1e12
@@ -439,7 +511,7 @@ def main():
 
     extras = {}
     names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.BWD_CONFIGS) + list(fa_inputs.KV_CONFIGS)
-             if n != a.workload]
+             + list(fa_inputs.FP8_VARIANT_CONFIGS) if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":

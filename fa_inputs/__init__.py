@@ -29,7 +29,11 @@ runs, so CPU and GPU draws differ but each is deterministic for a given seed):
 * append: new key rows then value rows [B, H, T, d] bf16 N(0,1) from seed
   (seed << 20) + 7, written at each sequence's position pos0;
 * backward: the forward's inputs, then dO [B, Hq, Sq, d] N(0,1) from seed
-  (seed << 20) + 5, cast like the inputs.
+  (seed << 20) + 5, cast like the inputs;
+* fp8 block-scaled prefill and its quantiser: the bf16 draws of the forward
+  recipe (the library's own quantiser turns them into codes); the rotation's
+  +-1 signs [d] are drawn from seed (seed << 20) + 9, uniform [0, 1) < 0.5
+  giving -1.
 """
 
 from __future__ import annotations
@@ -98,6 +102,25 @@ class AppendConfig:
     pos0: int = 0
 
 
+@dataclass(frozen=True)
+class Fp8BlockConfig(FwdConfig):
+    """fp8 prefill on codes with 64-row block scales (Q and K rotated when
+    ``rotate``), quantised from the bf16 draws of the same shape."""
+    rotate: bool = False
+
+
+@dataclass(frozen=True)
+class QuantConfig:
+    """The block quantiser over Q, K and V of one prefill (Q and K rotated when
+    ``rotate``)."""
+    name: str
+    B: int
+    H: int
+    S: int
+    d: int
+    rotate: bool
+
+
 # The five workloads: a tiny fp32 case, causal bf16 prefill, long-context GQA
 # prefill with outlier keys, fp8 prefill and int8-KV split decode.
 CONFIGS = {
@@ -128,6 +151,14 @@ KV_CONFIGS = {
         "decode_int8_window128_b64_gqa32x8_L32768", 64, 32, 8, 32768, 128, 16, W=128),
     "append_int8_b64_h8_t4096": AppendConfig("append_int8_b64_h8_t4096", 64, 8, 4096, 32768, 128, "int8", 28672),
     "append_fp8_b64_h8_t4096": AppendConfig("append_fp8_b64_h8_t4096", 64, 8, 4096, 32768, 128, "fp8", 28672),
+}
+
+# The fp8 accuracy variants at the fp8 workload's shape: the forward on
+# block-scaled codes, and the quantiser that makes them.
+FP8_VARIANT_CONFIGS = {
+    "fp8_block_rot_b8_h16_s4096": Fp8BlockConfig("fp8_block_rot_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128,
+                                                 False, out_dtype="bf16", rotate=True),
+    "fp8_quant_rot_b8_h16_s4096": QuantConfig("fp8_quant_rot_b8_h16_s4096", 8, 16, 4096, 128, True),
 }
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -266,3 +297,18 @@ def make_append_inputs(cfg: AppendConfig, seed: int = 0, device="cpu"):
     pos = torch.full((cfg.B,), cfg.pos0, dtype=torch.int32, device=device)
     return {"k_new": kn, "v_new": vn, "k_cache": kc, "v_cache": vc, "k_scale": ks, "v_scale": vs,
             "positions": pos}
+
+
+def make_rotation_signs(d: int, seed: int = 0, device="cpu"):
+    """+-1 float32 signs [d] of the random-sign Hadamard rotation."""
+    g = _gen(device, (seed << 20) + 9)
+    u = torch.rand(d, generator=g, device=device)
+    return torch.where(u < 0.5, -1.0, 1.0).to(torch.float32)
+
+
+def make_quant_inputs(cfg: QuantConfig, seed: int = 0, device="cpu"):
+    """bf16 q, k, v [B, H, S, d] of the forward recipe and the rotation signs."""
+    fc = FwdConfig(cfg.name, "bf16", cfg.B, cfg.H, cfg.H, cfg.S, cfg.S, cfg.d, False)
+    x = make_fwd_inputs(fc, seed=seed, device=device)
+    x["signs"] = make_rotation_signs(cfg.d, seed, device) if cfg.rotate else None
+    return x

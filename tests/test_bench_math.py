@@ -51,6 +51,19 @@ def test_kv_workload_bytes():
     assert bench.append_bytes(a) == 2 * rows * 256 + 2 * (rows * 128 + rows * 2) == 1619001344
 
 
+def test_fp8_variant_workloads():
+    v = fa_inputs.FP8_VARIANT_CONFIGS
+    fb = v["fp8_block_rot_b8_h16_s4096"]
+    # the block-scaled forward does the same work as the per-tensor one
+    assert bench.fwd_flops(fb) == bench.fwd_flops(C["fp8_b8_h16_s4096"])
+    assert bench.kernel_family(fb) == "fwd8"
+    qc = v["fp8_quant_rot_b8_h16_s4096"]
+    n = 8 * 16 * 4096 * 128
+    # per tensor: 2-byte rows read, 1-byte codes and a 4-byte scale per 64 rows written
+    assert bench.quant_bytes(qc) == 3 * (3 * n + 8 * 16 * 64 * 4)
+    assert bench.kernel_family(qc) == "quant" and bench.workload(qc.name) is qc
+
+
 def test_counter_digest_follows_each_kernel_family():
     fams = {n: bench.kernel_family(bench.workload(n)) for n in list(C) + list(fa_inputs.KV_CONFIGS)}
     assert fams["bf16_b4_h16_s2048_causal"] == "fwd16" and fams["fp8_b8_h16_s4096"] == "fwd8"

@@ -104,3 +104,17 @@ def test_kv_config_table():
     for f in ("int8", "fp8"):
         x = k[f"append_{f}_b64_h8_t4096"]
         assert (x.B, x.H, x.T, x.L, x.pos0, x.kv_format) == (64, 8, 4096, 32768, 28672, f)
+
+
+def test_rotation_signs_and_quant_inputs():
+    s = fa_inputs.make_rotation_signs(128, seed=3)
+    assert s.dtype == torch.float32 and set(s.tolist()) == {-1.0, 1.0}
+    assert torch.equal(s, fa_inputs.make_rotation_signs(128, seed=3))
+    assert not torch.equal(s, fa_inputs.make_rotation_signs(128, seed=4))
+    cfg = fa_inputs.QuantConfig("t", 1, 2, 70, 128, True)
+    x = fa_inputs.make_quant_inputs(cfg, seed=1)
+    assert x["q"].shape == (1, 2, 70, 128) and x["q"].dtype == torch.bfloat16
+    assert torch.equal(x["signs"], fa_inputs.make_rotation_signs(128, seed=1))
+    # the same bf16 draws as the forward recipe of that shape
+    fx = fa_inputs.make_fwd_inputs(fa_inputs.FwdConfig("t", "bf16", 1, 2, 2, 70, 70, 128, False), seed=1)
+    assert torch.equal(x["v"], fx["v"])

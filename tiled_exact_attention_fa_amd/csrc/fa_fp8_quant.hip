@@ -20,10 +20,13 @@
 // MI355X design.  One workgroup of 256 threads per block: 16 lane groups of 16,
 // each lane holding one 16-byte chunk (8 elements) of a row, a group 4 rows.
 // The transform's first three stages stay inside a lane, the last four are
-// lane exchanges within the group (xor 1, 2, 4, 8); the block absmax goes
-// through the group's lanes and then 16 LDS words; codes leave as one 8-byte
-// store per lane and row.  The whole block stays in registers between the
-// absmax and the encode, so every input byte is read once.
+// lane exchanges within the group (xor 1, 2, 4, 8), each one or two DPP moves
+// on the vector ALU rather than an LDS permute; the block absmax goes through
+// the group's lanes and then 16 LDS words; y / s is one exponent adjustment
+// (s is a power of two, so y * 2^-k is the correctly rounded quotient); codes
+// leave as one 8-byte store per lane and row.  The whole block stays in
+// registers between the absmax and the encode, so every input byte is read
+// once.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -40,6 +43,33 @@ struct QuantArgs {
 };
 
 constexpr int kQRows = 64;  // rows per block
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// the value lane (l ^ X) holds, within each row of 16 lanes (X = 1, 2, 4, 8)
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8, "lane_xor: 1, 2, 4 or 8");
+  if constexpr (X == 1) return dpp_mov<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
+  else if constexpr (X == 2) return dpp_mov<0x4E>(v);             // quad_perm [2, 3, 0, 1]
+  else if constexpr (X == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // l ^ 7, then l ^ 3
+  else return dpp_mov<0x141>(dpp_mov<0x140>(v));                  // l ^ 15, then l ^ 7
+}
+
+// one transform stage across lanes: the lane whose chunk has bit X clear holds
+// a (takes a + b), the other holds b (takes a - b)
+template <int X>
+__device__ __forceinline__ void xstage(float (&y)[8], int c) {
+  const bool upper = (c & X) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = lane_xor<X>(y[e]);
+    y[e] = upper ? other - y[e] : y[e] + other;
+  }
+}
 
 template <bool BF16, bool ROT>
 __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a) {
@@ -90,25 +120,21 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
             y[r][e] = p + q;
             y[r][e + hs] = p - q;
           }
-      // stages h = 8, 16, 32, 64 across the group: the lane whose chunk has the
-      // stage bit clear holds a (takes a + b), the other holds b (takes a - b)
-#pragma unroll
-      for (int ls = 1; ls < 16; ls <<= 1) {
-        const bool upper = (c & ls) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float other = __shfl_xor(y[r][e], ls, 16);
-          y[r][e] = upper ? other - y[r][e] : y[r][e] + other;
-        }
-      }
+      // stages h = 8, 16, 32, 64 across the group
+      xstage<1>(y[r], c);
+      xstage<2>(y[r], c);
+      xstage<4>(y[r], c);
+      xstage<8>(y[r], c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[r][e] *= 0.08838834764831845f;  // fp32(1/sqrt(128))
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[r][e]));
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  amax = fmaxf(amax, lane_xor<8>(amax));
+  amax = fmaxf(amax, lane_xor<4>(amax));
+  amax = fmaxf(amax, lane_xor<2>(amax));
+  amax = fmaxf(amax, lane_xor<1>(amax));
   if (c == 0) s_max[g] = amax;
   __syncthreads();
   float bmax = 0.f;
@@ -118,7 +144,8 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
   const float q448 = bmax / 448.f;
   int ex;
   const float mant = frexpf(q448, &ex);
-  const float sc = q448 > 0.f ? ldexpf(1.f, mant == 0.5f ? ex - 1 : ex) : 0.f;
+  const int sexp = mant == 0.5f ? ex - 1 : ex;  // s = 2^sexp
+  const float sc = q448 > 0.f ? ldexpf(1.f, sexp) : 0.f;
   if (tid == 0) a.scales[bh * static_cast<long long>(a.nb) + blk] = sc;
 
 #pragma unroll
@@ -131,7 +158,7 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
       for (int hh = 0; hh < 2; ++hh) {
         float q[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(y[r][4 * hh + e] / sc, -448.f), 448.f);
+        for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(ldexpf(y[r][4 * hh + e], -sexp), -448.f), 448.f);
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
         out[hh] = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true));
       }
