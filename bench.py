@@ -131,6 +131,12 @@ def algorithmic_bytes(cfg) -> int:
     return fwd_hbm_bytes(cfg)
 
 
+def launches_per_call(cfg) -> int:
+    """Launches of the workload's dominant kernel in one call (the quantiser
+    runs once per tensor: Q, K and V)."""
+    return 3 if isinstance(cfg, fa_inputs.QuantConfig) else 1
+
+
 def workload(name):
     for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS):
         if name in table:
@@ -455,7 +461,7 @@ def summarize_pmc(a):
     fetch = wf * 1024.0 * f_scale
     write = ww * 1024.0 * w_scale
     cfg = workload(a.workload)
-    algo = algorithmic_bytes(cfg)
+    algo = algorithmic_bytes(cfg) // launches_per_call(cfg)  # per launch, like the counters
     path = os.path.join(PROFILES, "hbm_traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[a.workload] = {"kernel": a.kernel, "bytes_per_launch": fetch + write, "fetch_bytes": fetch,
