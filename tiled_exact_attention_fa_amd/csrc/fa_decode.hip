@@ -341,53 +341,6 @@ void decode_split_kernel(const DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rvs =
       make_rsrc(static_cast<const _Float16 *>(a.vs) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
 
-  // ---- query: lane (n, g) holds q[n][32g + 8s + j], prescaled into fp16 ----
-  f16x8 qf[4];
-  float cq;  // score multiplier for query n: softmax scale * log2 e / 2^eq
-  {
-    float qv[32];
-    const bool real = n < G;
-    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + b * a.q_sb + (kvh * G + (real ? n : 0)) * a.q_sh;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 raw = real ? *reinterpret_cast<const u32x4 *>(qrow + 32 * g + 8 * c) : u32x4{0, 0, 0, 0};
-      const bf16x8 hv = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[8 * c + e] = static_cast<float>(hv[e]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(qv[e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    const int eq = amax > 0.f ? min(14 - exp_of(amax), 100) : 0;  // amax * 2^eq in [2^13, 2^14)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<_Float16>(ldexpf(qv[8 * c + e], eq));
-    cq = ldexpf(a.c, -eq);
-  }
-
-  // ---- value-scale prescale of this wavefront: vs * 2^fw < 2^6, so with
-  // p < 2^kRescaleSlack (= 2^8) every w = p * vs * 2^fw stays below 2^14 ----
-  int fw = 0;
-  {
-    float vmax = 0.f;
-    // w0 is a multiple of 32 tokens, so every 16-byte load is aligned
-    for (int t = w0 + 8 * lane; t < w1; t += 8 * 64) {
-      const u32x2 lo = load_scales4<SCVEC>(rvs, t);
-      const u32x2 hi = load_scales4<SCVEC>(rvs, t + 4);
-      const f16x8 sv = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t + e < w1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
-    fw = vmax > 0.f ? min(6 - exp_of(vmax), 100) : 0;
-  }
-  const float wmul = ldexpf(1.f, fw);
-
   // ---- tile loads.  Each tile gets buffer resources based at its first token
   // and ending at the wavefront's last token, so tokens past the range read
   // as zero without per-lane checks, and every per-lane offset is a loop
@@ -434,6 +387,67 @@ void decode_split_kernel(const DecodeArgs a) {
       r.vs[tb] = load_scales4_at<SCVEC>(tvs, s_off + 32u * tb);
     }
   };
+
+  // The first two tiles are requested before the query and the value-scale
+  // pass below, so the workgroup waits on one memory round trip, not three.
+  TileRegs r0, r1, r2;
+  load_tile(r0, w0);
+  load_tile(r1, w0 + kTile);
+  // value scales of the first step of the prescale pass below (8 tokens per
+  // lane; w0 is a multiple of 32 tokens, so every 16-byte load is aligned, and
+  // tokens past the range are dropped there)
+  const int vt0 = w0 + 8 * lane;
+  const u32x2 vs_lo0 = load_scales4<SCVEC>(rvs, vt0);
+  const u32x2 vs_hi0 = load_scales4<SCVEC>(rvs, vt0 + 4);
+
+  // ---- query: lane (n, g) holds q[n][32g + 8s + j], prescaled into fp16 ----
+  f16x8 qf[4];
+  float cq;  // score multiplier for query n: softmax scale * log2 e / 2^eq
+  {
+    float qv[32];
+    const bool real = n < G;
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + b * a.q_sb + (kvh * G + (real ? n : 0)) * a.q_sh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // padding columns read row 0 (a valid address) and drop it, so the four
+      // loads issue back to back without a branch
+      u32x4 raw = *reinterpret_cast<const u32x4 *>(qrow + 32 * g + 8 * c);
+      if (!real) raw = u32x4{0, 0, 0, 0};
+      const bf16x8 hv = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[8 * c + e] = static_cast<float>(hv[e]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(qv[e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const int eq = amax > 0.f ? min(14 - exp_of(amax), 100) : 0;  // amax * 2^eq in [2^13, 2^14)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<_Float16>(ldexpf(qv[8 * c + e], eq));
+    cq = ldexpf(a.c, -eq);
+  }
+
+  // ---- value-scale prescale of this wavefront: vs * 2^fw < 2^6, so with
+  // p < 2^kRescaleSlack (= 2^8) every w = p * vs * 2^fw stays below 2^14 ----
+  int fw = 0;
+  {
+    float vmax = 0.f;
+    auto fold = [&](int t, u32x2 lo, u32x2 hi) {
+      const f16x8 sv = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t + e < w1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
+    };
+    fold(vt0, vs_lo0, vs_hi0);
+    for (int t = vt0 + 8 * 64; t < w1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    fw = vmax > 0.f ? min(6 - exp_of(vmax), 100) : 0;
+  }
+  const float wmul = ldexpf(1.f, fw);
 
   float m_run = neg_inf();
   float l_run = 0.f;
@@ -528,9 +542,6 @@ void decode_split_kernel(const DecodeArgs a) {
   // three register tiles; loads past the range read zeros without touching
   // memory, so the loop body issues them unconditionally) ----
   if (ntiles > 0) {
-    TileRegs r0, r1, r2;
-    load_tile(r0, w0);
-    load_tile(r1, w0 + kTile);
     int t = 0;
     for (; t + 2 < ntiles; t += 3) {
       load_tile(r2, w0 + (t + 2) * kTile);

@@ -98,7 +98,9 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   unsigned char *vbuf = lds + 2 * K_TILE;    // [2][D][VROW]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave-uniform: the causal tile ranges, loop bounds and buffer resources stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
 
   int bh, qt;
