@@ -14,9 +14,10 @@
 //   * Kernel 1 (decode_split_kernel): one workgroup per (batch, cache head,
 //     split).  All G query heads that share the cache head are served by the
 //     same pass over the chunk, so every K/V byte is read from HBM once.  The
-//     chunk is cut into four contiguous quarters, one per wavefront; each
-//     wavefront streams 32-token tiles with a one-tile register prefetch and
-//     no barrier, and the four partial states are merged through LDS at the end.
+//     chunk's 32-token tiles are dealt to the four wavefronts in turn, so the
+//     workgroup streams one contiguous stretch at a time; each wavefront keeps
+//     two tiles of register prefetch and no barrier, and the four partial
+//     states are merged through LDS at the end.
 //   * The dequantisation is fused into the tile load and folded into the math:
 //     int8 codes become exact fp16 values with two byte permutes and a packed
 //     subtract (1024 + u in fp16 is 0x6400 | u); E4M3FN codes (every one of
@@ -31,8 +32,8 @@
 //     which lets each lane load one contiguous 8-byte piece per token.
 //   * The bf16 query is prescaled by a power of two per head so it converts to
 //     fp16 exactly; the probabilities times value scales are prescaled by a
-//     power of two per wavefront, chosen from the largest value scale of its
-//     range, so they neither overflow nor lose range in fp16 (probabilities
+//     power of two per workgroup, chosen from the largest value scale of its
+//     chunk, so they neither overflow nor lose range in fp16 (probabilities
 //     reach 2^8 under the lazy running max, see kRescaleSlack).  Both factors are
 //     undone in fp32.
 //   * The residual window (decode_window_kernel, launched before the split
@@ -315,6 +316,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
+  __shared__ float s_vmax[4];
 
   const int bid = blockIdx.x;
 
@@ -333,10 +335,17 @@ void decode_split_kernel(const DecodeArgs a) {
   len = min(max(len, 0), a.L);
   const int c0 = split * a.chunk;
   const int c1 = min(c0 + a.chunk, len);
+  // The chunk's 32-token tiles are dealt to the four wavefronts in turn (tile
+  // i of a wavefront is tile 4i + wave of the chunk), so at any moment the
+  // workgroup streams one contiguous stretch of the cache: measured on this
+  // part, that reads about 7 % faster than four separate stretches.
+  const int n_ct = c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0;
+  const int ntiles = n_ct > wave ? (n_ct - wave + 3) / 4 : 0;
+  auto tile_t0 = [&](int i) { return c0 + kTile * (4 * i + wave); };
+  // the value-scale pass below gives each wavefront one contiguous quarter
   const int quarter = ((a.chunk + 3) / 4 + kTile - 1) / kTile * kTile;
-  const int w0 = c0 + wave * quarter;
-  const int w1 = min(w0 + quarter, c1);
-  const int ntiles = w1 > w0 ? (w1 - w0 + kTile - 1) / kTile : 0;
+  const int v0 = c0 + wave * quarter;
+  const int v1 = min(v0 + quarter, c1);
 
   const __amdgpu_buffer_rsrc_t rvs =
       make_rsrc(static_cast<const _Float16 *>(a.vs) + b * a.sc_sb + kvh * a.sc_sh, a.sc_ext);
@@ -359,7 +368,7 @@ void decode_split_kernel(const DecodeArgs a) {
     v_off[j] = (4u * g + (j & 3) + 16u * (j >> 2)) * ss + 8u * n;
   const unsigned s_off = 8u * g;  // scales of tokens 4g .. 4g+3 (+ 16 tb)
   auto load_tile = [&](TileRegs &r, int t0) {
-    const int left = w1 - t0;  // tokens of the range from t0 on
+    const int left = c1 - t0;  // tokens of the chunk from t0 on
     const unsigned kv_rec = left > 0 ? static_cast<unsigned>(left - 1) * ss + kD : 0u;
     // The range check of a buffer load is made per dword: a dword that
     // straddles the end of the range reads as zero in full.  The 8-byte scale
@@ -391,12 +400,12 @@ void decode_split_kernel(const DecodeArgs a) {
   // The first two tiles are requested before the query and the value-scale
   // pass below, so the workgroup waits on one memory round trip, not three.
   TileRegs r0, r1, r2;
-  load_tile(r0, w0);
-  load_tile(r1, w0 + kTile);
+  load_tile(r0, tile_t0(0));
+  load_tile(r1, tile_t0(1));
   // value scales of the first step of the prescale pass below (8 tokens per
-  // lane; w0 is a multiple of 32 tokens, so every 16-byte load is aligned, and
+  // lane; v0 is a multiple of 32 tokens, so every 16-byte load is aligned, and
   // tokens past the range are dropped there)
-  const int vt0 = w0 + 8 * lane;
+  const int vt0 = v0 + 8 * lane;
   const u32x2 vs_lo0 = load_scales4<SCVEC>(rvs, vt0);
   const u32x2 vs_hi0 = load_scales4<SCVEC>(rvs, vt0 + 4);
 
@@ -430,7 +439,7 @@ void decode_split_kernel(const DecodeArgs a) {
     cq = ldexpf(a.c, -eq);
   }
 
-  // ---- value-scale prescale of this wavefront: vs * 2^fw < 2^6, so with
+  // ---- value-scale prescale of this workgroup: vs * 2^fw < 2^6, so with
   // p < 2^kRescaleSlack (= 2^8) every w = p * vs * 2^fw stays below 2^14 ----
   int fw = 0;
   {
@@ -439,12 +448,16 @@ void decode_split_kernel(const DecodeArgs a) {
       const f16x8 sv = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (t + e < w1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
+        if (t + e < v1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
     };
     fold(vt0, vs_lo0, vs_hi0);
-    for (int t = vt0 + 8 * 64; t < w1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
+    for (int t = vt0 + 8 * 64; t < v1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    // every wavefront's tiles spread over the whole chunk: take the chunk's maximum
+    if (lane == 0) s_vmax[wave] = vmax;
+    __syncthreads();
+    vmax = fmaxf(fmaxf(s_vmax[0], s_vmax[1]), fmaxf(s_vmax[2], s_vmax[3]));
     fw = vmax > 0.f ? min(6 - exp_of(vmax), 100) : 0;
   }
   const float wmul = ldexpf(1.f, fw);
@@ -486,7 +499,7 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * tb + 4 * g + i;
         float s = sacc[tb][i] * (static_cast<float>(kscale[i]) * cq);
-        s = tok < w1 ? s : neg_inf();
+        s = tok < c1 ? s : neg_inf();
         sc[4 * tb + i] = s;
         mx = fmaxf(mx, s);
       }
@@ -544,15 +557,15 @@ void decode_split_kernel(const DecodeArgs a) {
   if (ntiles > 0) {
     int t = 0;
     for (; t + 2 < ntiles; t += 3) {
-      load_tile(r2, w0 + (t + 2) * kTile);
-      compute_tile(r0, w0 + t * kTile);
-      load_tile(r0, w0 + (t + 3) * kTile);
-      compute_tile(r1, w0 + (t + 1) * kTile);
-      load_tile(r1, w0 + (t + 4) * kTile);
-      compute_tile(r2, w0 + (t + 2) * kTile);
+      load_tile(r2, tile_t0(t + 2));
+      compute_tile(r0, tile_t0(t));
+      load_tile(r0, tile_t0(t + 3));
+      compute_tile(r1, tile_t0(t + 1));
+      load_tile(r1, tile_t0(t + 4));
+      compute_tile(r2, tile_t0(t + 2));
     }
-    if (t < ntiles) compute_tile(r0, w0 + t * kTile);
-    if (t + 1 < ntiles) compute_tile(r1, w0 + (t + 1) * kTile);
+    if (t < ntiles) compute_tile(r0, tile_t0(t));
+    if (t + 1 < ntiles) compute_tile(r1, tile_t0(t + 1));
   }
 
   // ---- wavefront partial: O_w = O_acc / (l 2^fw), lse2_w = m + log2 l ----
