@@ -148,3 +148,35 @@ def test_decode_ragged_tail_tokens(gpu, fmt, vec_scales):
             x[key] = big[..., 1:]
     o, lse = run_decode(gpu, x, 7)
     compare(o, lse, xc)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_decode_value_scales_spanning_the_chunk(gpu, fmt):
+    """Value scales 4096 times larger on one 32-token tile of a split, which a
+    wavefront other than the one scanning that stretch of scales consumes: the
+    fp16 prescale of P * v_scale must cover the whole chunk, or that tile's
+    weights overflow.  The query points at one of those tokens, so they carry
+    most of the probability.  Compared relative to the output's magnitude
+    (the dequantised values reach about 1e4 here)."""
+    B, Hq, Hkv, L, splits = 1, 4, 1, 1024, 4   # chunks of 256 tokens: 8 tiles, two per wavefront
+    cfg = fa_inputs.DecodeConfig("t", B, Hq, Hkv, L, 128, splits, (), fmt)
+    xc = fa_inputs.make_decode_inputs(cfg, seed=23)
+    for s in range(splits):   # tile 5 of every chunk
+        lo = s * 256 + 5 * 32
+        xc["v_scale"][0, 0, lo:lo + 32] = (xc["v_scale"][0, 0, lo:lo + 32].float() * 4096).half()
+    deq = oracle.dequant_int8_fp64 if fmt == "int8" else oracle.dequant_fp8_fp64
+    tok = 2 * 256 + 5 * 32 + 7
+    key = deq(xc["k"][0, 0, tok:tok + 1].numpy(), xc["k_scale"][0, 0, tok:tok + 1].numpy())[0]
+    for h in range(Hq):
+        xc["q"][0, h] = torch.from_numpy(key * (1.0 + h) / float(np.abs(key).max())).to(torch.bfloat16)
+    x = {k: v.cuda() for k, v in xc.items()}
+    o, lse = run_decode(gpu, x, splits)
+    ro, rl = oracle.decode_fp64(xc["q"], xc["k"].numpy(), xc["k_scale"].numpy(), xc["v"].numpy(),
+                                xc["v_scale"].numpy(), xc["seq_lens"].numpy(), kv_format=fmt)
+    og = o.double().cpu().numpy()
+    assert np.isfinite(og).all()
+    scale = float(np.abs(ro).max())
+    assert scale > 100.0   # the large-scale tokens dominate
+    err = float(np.max(np.abs(og - ro))) / scale
+    assert err <= 1e-2, f"relative O err {err}"
+    assert float(np.max(np.abs(lse.double().cpu().numpy() - rl))) <= TOL_LSE
