@@ -91,9 +91,9 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
   for (int r = 0; r < 4; ++r) {
     const int row = blk * kQRows + 4 * g + r;
     u32x4 raw{0u, 0u, 0u, 0u};
-    if (row < a.S)
-      raw = *reinterpret_cast<const u32x4 *>(static_cast<const unsigned short *>(a.x) + b * a.x_sb + h * a.x_sh +
-                                             row * a.x_ss + 8 * c);
+    if (row < a.S)  // read once: non-temporal
+      raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+          static_cast<const unsigned short *>(a.x) + b * a.x_sb + h * a.x_sh + row * a.x_ss + 8 * c));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const unsigned w = raw[i];
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
         out[hh] = static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true));
       }
     }
-    *reinterpret_cast<u32x2 *>(a.codes + b * a.c_sb + h * a.c_sh + row * a.c_ss + 8 * c) = out;
+    // written once, read by a later kernel: non-temporal
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(a.codes + b * a.c_sb + h * a.c_sh + row * a.c_ss + 8 * c));
   }
 }
 

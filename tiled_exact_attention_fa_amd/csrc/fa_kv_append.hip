@@ -148,8 +148,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(const AppendA
     const u32x2 kq = quantise8<BF16, FP8>(kx[i], ks);
     const u32x2 vq = quantise8<BF16, FP8>(vx[i], vs);
     if (write[i]) {
-      *reinterpret_cast<u32x2 *>(a.k_cache + c_off[i]) = kq;
-      *reinterpret_cast<u32x2 *>(a.v_cache + c_off[i]) = vq;
+      // the cache is written once here and read by a later decode step, not by
+      // this kernel: stream the codes past the caches (non-temporal stores)
+      __builtin_nontemporal_store(kq, reinterpret_cast<u32x2 *>(a.k_cache + c_off[i]));
+      __builtin_nontemporal_store(vq, reinterpret_cast<u32x2 *>(a.v_cache + c_off[i]));
       if (c == 0) {
         a.k_scale[s_off[i]] = ks;
         a.v_scale[s_off[i]] = vs;
