@@ -21,8 +21,22 @@
 // workgroups as rows / 16.  The absmax is reduced over
 // the group with lane exchanges only (no LDS, no barrier).  fp8 codes come from
 // the hardware's packed E4M3FN conversion (round to nearest even), int8 codes
-// from rint; the division stays a true IEEE division because the code is an
-// integer decision that must not depend on a reciprocal's rounding.
+// from rint.
+//
+// The quotient x / sc is not a full IEEE division, yet every code equals the
+// one the correctly rounded quotient gives.  With r the hardware reciprocal of
+// sc, q0 = x r and one residual step q1 = q0 + (x - sc q0) r leave q1 within
+// about one ulp of x / sc, and exactly equal to it whenever x / sc is
+// representable.  A code can only depend on that ulp where x / sc lies next to
+// a rounding boundary of the code (a half-integer for int8, a midpoint between
+// neighbouring E4M3 values for fp8).  A boundary t = T 2^c has T below 2^9, sc
+// = S 2^b has S below 2^11 (fp16) and x at most 11 significant bits (bf16 or
+// fp16), so x - t sc is a multiple of 2^(b+c) or of x's own last bit: when x
+// is close to t sc it is either zero or at least x / (T S) > 2^-20 x in size.
+// x / sc is then either exactly on the boundary (q1 is exact and the tie goes
+// to even, as for the correctly rounded quotient) or at least 2^-20 of its
+// size away from it, well beyond the 2^-23 of an fp32 ulp.  The same holds
+// for the clamp at +-QMAX.
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -84,8 +98,13 @@ __device__ __forceinline__ u32x2 quantise8(const u32x4 raw, _Float16 &sc16) {
   u32x2 out{0u, 0u};
   if (scf > 0.f) {
     float y[8];
+    const float r = __builtin_amdgcn_rcpf(scf);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] / scf, -kQmax), kQmax);
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = x[i] * r;
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-scf, q0, x[i]), r, q0);
+      y[i] = fminf(fmaxf(q1, -kQmax), kQmax);
+    }
     if constexpr (FP8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
