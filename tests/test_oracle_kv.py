@@ -313,3 +313,38 @@ def test_planted_quantiser_mistakes_are_caught(kind):
             bad_brute = False
         caught |= bool(bad_scale or bad_err or bad_brute)
     assert caught, f"mutant {kind} slipped through"
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("in_dtype", [torch.bfloat16, torch.float16])
+def test_code_boundaries_are_hit_exactly_or_missed_by_a_margin(fmt, in_dtype):
+    """The margin the append kernel's quotient relies on: for bf16/fp16 x and
+    an fp16 scale sc, x - t * sc (t the code's rounding boundary nearest x / sc:
+    an int8 half-integer, an E4M3 midpoint, or the clamp) is either exactly 0
+    or at least 2^-20 |x|, so a quotient within a few fp32 ulps (2^-23) of
+    x / sc that is exact on the boundary decides every code as the correctly
+    rounded quotient does.  Checked on the boundary rows of the GPU test, in
+    float64, where t * sc (at most 20 significant bits) and the difference are
+    exact."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from kv_boundary import boundary_rows
+
+    rows = boundary_rows(fmt, in_dtype, 1024, seed=31)
+    _, sc = oracle.quantize_kv_tokhead(rows, fmt)
+    x = rows.double().numpy()
+    s = sc.astype(np.float64)[:, None]
+    qmax = INT8_QMAX if fmt == "int8" else E4M3_QMAX
+    if fmt == "int8":
+        bnd = np.arange(128) + 0.5
+    else:
+        vals = np.unique([abs(e4m3_value(c)) for c in range(256) if math.isfinite(e4m3_value(c))])
+        bnd = (vals[1:] + vals[:-1]) / 2
+    bnd = np.concatenate([bnd[bnd < qmax], [qmax]])
+    ay = np.abs(x) / s
+    i = np.clip(np.searchsorted(bnd, ay), 1, len(bnd) - 1)
+    dist = np.minimum(np.abs(np.abs(x) - bnd[i] * s), np.abs(np.abs(x) - bnd[i - 1] * s))
+    nz = (dist > 0) & (x != 0)
+    assert int((dist == 0).sum()) > 1000                      # plenty of exact ties in the rows
+    assert np.all(dist[nz] >= 2.0 ** -20 * np.abs(x[nz]))
