@@ -590,38 +590,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128)))
 void decode_combine_kernel(const DecodeArgs a) {
   // one workgroup per (batch, query head); thread d owns output column d.
   // Partial slots (the splits, then the window's) are taken 16 at a time with
-  // all loads of a group in flight.
+  // all loads of a group in flight, in one pass: each group's maximum joins
+  // the running one and rescales what is summed so far (with 16 splits there
+  // is a single group and no rescale).
   const int d = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const long long stride = static_cast<long long>(a.B) * a.Hq;
   constexpr int kGroup = 16;
-  float M = neg_inf();
+  float M = neg_inf(), tot = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < a.nslots; s0 += kGroup) {
-    float l[kGroup];
+    float l[kGroup], v[kGroup];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) l[i] = s0 + i < a.nslots ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
+    for (int i = 0; i < kGroup; ++i) {
+      const bool ok = s0 + i < a.nslots;
+      l[i] = ok ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
+      v[i] = ok ? a.ws_o[((s0 + i) * stride + bh) * kD + d] : 0.f;
+    }
+    float Mg = M;
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) M = fmaxf(M, l[i]);
-  }
-  float lse2 = neg_inf(), o = 0.f;
-  if (M != neg_inf()) {
-    float tot = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < a.nslots; s0 += kGroup) {
-      float l[kGroup], v[kGroup];
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const bool ok = s0 + i < a.nslots;
-        l[i] = ok ? a.ws_l[(s0 + i) * stride + bh] : neg_inf();
-        v[i] = ok ? a.ws_o[((s0 + i) * stride + bh) * kD + d] : 0.f;
-      }
+    for (int i = 0; i < kGroup; ++i) Mg = fmaxf(Mg, l[i]);
+    if (Mg != neg_inf()) {
+      const float r = fast_exp2(M - Mg);  // 0 while nothing has been summed (M = -inf)
+      tot *= r;
+      acc *= r;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        const float w = fast_exp2(l[i] - M);  // 0 for empty splits
+        const float w = fast_exp2(l[i] - Mg);  // 0 for empty splits
         tot += w;
         acc += w * v[i];
       }
+      M = Mg;
     }
+  }
+  float lse2 = neg_inf(), o = 0.f;
+  if (M != neg_inf()) {
     lse2 = M + __log2f(tot);
     o = acc / tot;
   }
