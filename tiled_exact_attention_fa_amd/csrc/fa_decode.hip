@@ -17,7 +17,10 @@
 //     chunk's 32-token tiles are dealt to the four wavefronts in turn, so the
 //     workgroup streams one contiguous stretch at a time; each wavefront keeps
 //     two tiles of register prefetch and no barrier, and the four partial
-//     states are merged through LDS at the end.
+//     states are merged through LDS at the end.  When the scale rows allow
+//     16-byte loads and a chunk has at most 2048 tokens, the chunk's key and
+//     value scales are staged in LDS once, with two coalesced loads per
+//     thread, instead of four tiny loads per tile and wavefront.
 //   * The dequantisation is fused into the tile load and folded into the math:
 //     int8 codes become exact fp16 values with two byte permutes and a packed
 //     subtract (1024 + u in fp16 is 0x6400 | u); E4M3FN codes (every one of
@@ -311,12 +314,20 @@ void decode_window_kernel(const DecodeArgs a) {
   merge_waves_to_slot(a, s_o, s_l, a.nsplit, b, kvh);
 }
 
-template <bool SCVEC, bool FP8>
+// Scales of a chunk of at most this many tokens are staged in LDS once per
+// workgroup (two coalesced 16-byte loads per thread) instead of being fetched
+// tile by tile: four tiny global loads per tile cost about 5 % of the
+// bandwidth of a stream shaped like this one.
+constexpr int kStageTok = 2048;
+
+template <bool SCVEC, bool FP8, bool STAGED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const DecodeArgs a) {
+  static_assert(!STAGED || SCVEC, "staged scales use 16-byte loads of aligned scale rows");
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
   __shared__ float s_vmax[4];
+  __shared__ __attribute__((aligned(16))) _Float16 s_sc[STAGED ? 2 * kStageTok : 8];  // key scales, then value scales
 
   const int bid = blockIdx.x;
 
@@ -367,8 +378,21 @@ void decode_split_kernel(const DecodeArgs a) {
   for (int j = 0; j < 8; ++j)  // codes 8n .. 8n+7 of token 4g + (j & 3) + 16 (j >> 2)
     v_off[j] = (4u * g + (j & 3) + 16u * (j >> 2)) * ss + 8u * n;
   const unsigned s_off = 8u * g;  // scales of tokens 4g .. 4g+3 (+ 16 tb)
-  auto load_tile = [&](TileRegs &r, int t0) {
+  // staged scales of a tile, from LDS; a tile past the chunk reads the first
+  // tile's (its scores are masked)
+  auto load_sc = [&](TileRegs &r, int t0) {
+    const int rel = c1 - t0 > 0 ? t0 - c0 : 0;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      r.ks[tb] = *reinterpret_cast<const u32x2 *>(&s_sc[rel + 16 * tb + 4 * g]);
+      r.vs[tb] = *reinterpret_cast<const u32x2 *>(&s_sc[kStageTok + rel + 16 * tb + 4 * g]);
+    }
+  };
+  auto load_tile = [&](TileRegs &r, int t0, bool staged_sc = true) {
     const int left = c1 - t0;  // tokens of the chunk from t0 on
+    if constexpr (STAGED) {
+      if (staged_sc) load_sc(r, t0);
+    }
     const unsigned kv_rec = left > 0 ? static_cast<unsigned>(left - 1) * ss + kD : 0u;
     // The range check of a buffer load is made per dword: a dword that
     // straddles the end of the range reads as zero in full.  The 8-byte scale
@@ -390,24 +414,39 @@ void decode_split_kernel(const DecodeArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) r.v[j] = buf_load8_nt(tv, v_off[j]);
+    if constexpr (!STAGED) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      r.ks[tb] = load_scales4_at<SCVEC>(tks, s_off + 32u * tb);
-      r.vs[tb] = load_scales4_at<SCVEC>(tvs, s_off + 32u * tb);
+      for (int tb = 0; tb < 2; ++tb) {
+        r.ks[tb] = load_scales4_at<SCVEC>(tks, s_off + 32u * tb);
+        r.vs[tb] = load_scales4_at<SCVEC>(tvs, s_off + 32u * tb);
+      }
     }
   };
 
   // The first two tiles are requested before the query and the value-scale
   // pass below, so the workgroup waits on one memory round trip, not three.
   TileRegs r0, r1, r2;
-  load_tile(r0, tile_t0(0));
-  load_tile(r1, tile_t0(1));
+  // staged scales: 8 tokens per thread and array, the chunk starting at c0 (a
+  // multiple of 32 tokens, so the 16-byte loads are aligned); tokens past L
+  // read as zero, those past c1 are masked where they are used
+  u32x4 st_k{0u, 0u, 0u, 0u}, st_v{0u, 0u, 0u, 0u};
+  if constexpr (STAGED) {
+    const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksslice, a.sc_ext);
+    const bool in = 8 * tid < a.chunk;
+    st_k = buf_load16_nt(rks, in ? static_cast<unsigned>(c0 + 8 * tid) * 2u : kOOB);
+    st_v = buf_load16_nt(rvs, in ? static_cast<unsigned>(c0 + 8 * tid) * 2u : kOOB);
+  }
+  load_tile(r0, tile_t0(0), false);  // staged scales of these two: after the barrier below
+  load_tile(r1, tile_t0(1), false);
   // value scales of the first step of the prescale pass below (8 tokens per
   // lane; v0 is a multiple of 32 tokens, so every 16-byte load is aligned, and
   // tokens past the range are dropped there)
   const int vt0 = v0 + 8 * lane;
-  const u32x2 vs_lo0 = load_scales4<SCVEC>(rvs, vt0);
-  const u32x2 vs_hi0 = load_scales4<SCVEC>(rvs, vt0 + 4);
+  u32x2 vs_lo0{0u, 0u}, vs_hi0{0u, 0u};
+  if constexpr (!STAGED) {
+    vs_lo0 = load_scales4<SCVEC>(rvs, vt0);
+    vs_hi0 = load_scales4<SCVEC>(rvs, vt0 + 4);
+  }
 
   // ---- query: lane (n, g) holds q[n][32g + 8s + j], prescaled into fp16 ----
   f16x8 qf[4];
@@ -450,8 +489,20 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int e = 0; e < 8; ++e)
         if (t + e < v1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
     };
-    fold(vt0, vs_lo0, vs_hi0);
-    for (int t = vt0 + 8 * 64; t < v1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
+    if constexpr (STAGED) {
+      // the staged value scales of this thread's 8 tokens
+      if (8 * tid < a.chunk) {
+        *reinterpret_cast<u32x4 *>(&s_sc[8 * tid]) = st_k;
+        *reinterpret_cast<u32x4 *>(&s_sc[kStageTok + 8 * tid]) = st_v;
+      }
+      const f16x8 sv = __builtin_bit_cast(f16x8, st_v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + 8 * tid + e < c1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
+    } else {
+      fold(vt0, vs_lo0, vs_hi0);
+      for (int t = vt0 + 8 * 64; t < v1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
     // every wavefront's tiles spread over the whole chunk: take the chunk's maximum
@@ -459,6 +510,10 @@ void decode_split_kernel(const DecodeArgs a) {
     __syncthreads();
     vmax = fmaxf(fmaxf(s_vmax[0], s_vmax[1]), fmaxf(s_vmax[2], s_vmax[3]));
     fw = vmax > 0.f ? min(6 - exp_of(vmax), 100) : 0;
+  }
+  if constexpr (STAGED) {  // the barrier above published the staged scales
+    load_sc(r0, tile_t0(0));
+    load_sc(r1, tile_t0(1));
   }
   const float wmul = ldexpf(1.f, fw);
 
@@ -696,7 +751,10 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
   const dim3 g1(grid1), b1(kDecodeThreads);
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
-  if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);
+  const bool staged = a.sc_vec && a.chunk <= kStageTok;
+  if (staged && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true, true>), g1, b1, 0, s, a);
+  else if (staged) hipLaunchKernelGGL((decode_split_kernel<true, false, true>), g1, b1, 0, s, a);
+  else if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);
   else if (a.sc_vec) hipLaunchKernelGGL((decode_split_kernel<true, false>), g1, b1, 0, s, a);
   else if (fp8) hipLaunchKernelGGL((decode_split_kernel<false, true>), g1, b1, 0, s, a);
   else hipLaunchKernelGGL((decode_split_kernel<false, false>), g1, b1, 0, s, a);
