@@ -39,14 +39,12 @@
 //     chunk, so they neither overflow nor lose range in fp16 (probabilities
 //     reach 2^8 under the lazy running max, see kRescaleSlack).  Both factors are
 //     undone in fp32.
-//   * The residual window (decode_window_kernel, launched before the split
-//     kernel when it is used) gives one workgroup to the window of each
-//     (batch, cache head).  Its tokens are few and unquantised, so this path
-//     is plain fp32 arithmetic: a lane scores one token against all G query
-//     rows, and the probabilities are broadcast lane by lane into the P V
-//     update, each lane owning two head-dim columns.  Its partial goes to one
-//     more workspace slot.  A kernel of its own keeps the split kernel's
-//     register allocation untouched.
+//   * The residual window (decode_window_wg) gives one workgroup to the
+//     window of each (batch, cache head).  These workgroups are appended to
+//     the split kernel's grid, so they run in the tail of its stream rather
+//     than in a launch of their own ahead of it.  The window's tokens are few
+//     and unquantised bf16: it walks them with 16x16x32 bf16 MFMAs and an
+//     exact running max, and writes its partial to one more workspace slot.
 //   * Kernel 2 (decode_combine_kernel) merges the splits of one (batch, head):
 //     with M = max_s lse_s and w_s = 2^(lse_s - M), LSE = M + log2 sum_s w_s and
 //     O = sum_s w_s O_s / sum_s w_s, in the log2 domain; it writes bf16 O and
@@ -200,12 +198,11 @@ __device__ __forceinline__ void merge_waves_to_slot(const DecodeArgs &a, const f
 // and V^T built from 16-byte row loads with 16-bit permutes (block j of the
 // output holds head-dim column 8m + j in row m).  The running max is exact
 // (no lazy slack), so probabilities stay <= 1.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void decode_window_kernel(const DecodeArgs a) {
-  __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
-  __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
-  const int b = blockIdx.x / a.Hkv;
-  const int kvh = blockIdx.x % a.Hkv;
+__device__ __attribute__((always_inline)) void decode_window_wg(const DecodeArgs &a, int wid,
+                                                              float (*s_o)[FA_DECODE_MAX_GROUP][kD],
+                                                              float (*s_l)[FA_DECODE_MAX_GROUP]) {
+  const int b = wid / a.Hkv;
+  const int kvh = wid % a.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -330,6 +327,14 @@ void decode_split_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_sc[STAGED ? 2 * kStageTok : 8];  // key scales, then value scales
 
   const int bid = blockIdx.x;
+  // workgroups past the splits' own take the window, one per (batch, KV head),
+  // and run in the tail of the split workgroups instead of in a launch of
+  // their own ahead of them
+  const int split_wgs = a.nsplit * a.Hkv * a.B;
+  if (bid >= split_wgs) {
+    decode_window_wg(a, bid - split_wgs, s_o, s_l);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -743,12 +748,7 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   a.ws_l = reinterpret_cast<float *>(static_cast<char *>(p->workspace) +
                                      ((rows * kD * sizeof(float) + 255) & ~size_t(255)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (window) {
-    hipLaunchKernelGGL(decode_window_kernel, dim3(static_cast<unsigned>(p->B) * p->Hkv), dim3(kDecodeThreads), 0, s, a);
-    const hipError_t ew = hipGetLastError();
-    if (ew != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode window launch: %s", hipGetErrorString(ew));
-  }
-  const unsigned grid1 = static_cast<unsigned>(p->num_splits) * p->Hkv * p->B;
+  const unsigned grid1 = static_cast<unsigned>(p->num_splits + (window ? 1 : 0)) * p->Hkv * p->B;
   const dim3 g1(grid1), b1(kDecodeThreads);
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
   const bool staged = a.sc_vec && a.chunk <= kStageTok;
