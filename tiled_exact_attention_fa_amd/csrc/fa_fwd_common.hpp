@@ -26,11 +26,20 @@ struct FwdArgs {
 // each XCD gets a contiguous range of (batch, head) pairs (consecutive query
 // heads share one K/V head under GQA), so every K/V stream is read through one
 // XCD's L2.  Within an XCD:
-//   * causal (tiles of unequal length): longest tiles first across all heads of
-//     the range, so the short tiles fill the tail of the launch;
+//   * causal (tiles of unequal length): longest tiles first, so the short
+//     tiles fill the tail of the launch.  When a head has at most 8 query
+//     tiles, the range is cut into groups of heads (whole GQA groups, so the
+//     query heads of one K/V head stay together) whose tiles together about
+//     fill the XCD's 32 compute units once, and each group is issued longest
+//     first across its heads: a compute unit that drew a long tile then draws
+//     a short one, so the pairs even out as under one order over the whole
+//     range, while the K/V read at any one time is one group's.  Measured, that
+//     cut the fetched bytes of B=4 H=16 S=2048 by 18 % and ran B=8 at that
+//     length 5 % faster; with 16 or more tiles per head it ran 2 % slower, so
+//     longer heads keep one longest-first order over the whole range;
 //   * non-causal (equal tiles): head by head, so the workgroups resident at
 //     any time read the K/V of only one or two heads, which stay in L2.
-__device__ __forceinline__ void map_block(int bid, int nq, int nbh, bool longest_first, int &bh, int &qt) {
+__device__ __forceinline__ void map_block(int bid, int nq, int nbh, int G, bool longest_first, int &bh, int &qt) {
   int base = 0, per = nbh, slot = bid;
   if ((nbh & 7) == 0) {
     per = nbh >> 3;
@@ -38,8 +47,13 @@ __device__ __forceinline__ void map_block(int bid, int nq, int nbh, bool longest
     slot = bid >> 3;
   }
   if (longest_first) {
-    bh = base + slot % per;
-    qt = nq - 1 - slot / per;
+    constexpr int kCusPerXcd = 32;
+    int hg = per;  // heads per group
+    if ((nbh & 7) == 0 && nq <= 8) hg = min(per, (kCusPerXcd / nq + G - 1) / G * G);
+    const int grp = slot / (hg * nq), within = slot % (hg * nq);
+    const int nh = min(hg, per - grp * hg);  // the last group may hold fewer heads
+    bh = base + grp * hg + within % nh;
+    qt = nq - 1 - within / nh;
   } else {
     bh = base + slot / nq;
     qt = slot % nq;

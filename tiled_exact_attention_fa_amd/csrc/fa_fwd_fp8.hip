@@ -104,7 +104,7 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   const int l32 = lane & 31, h = lane >> 5;
 
   int bh, qt;
-  map_block(blockIdx.x, a.nq, a.B * a.Hq, CAUSAL, bh, qt);
+  map_block(blockIdx.x, a.nq, a.B * a.Hq, a.G, CAUSAL, bh, qt);
   const int b = bh / a.Hq, hq = bh - b * a.Hq, hk = hq / a.G;
   const int i0 = qt * BR;
   const int wrow0 = i0 + 32 * wave;
