@@ -85,6 +85,10 @@ SHAPES = [
     (1, 8, 2, 300, 300),
     (2, 2, 2, 100, 260),   # Sq < Sk
     (1, 2, 2, 260, 100),   # Sq > Sk: causal leaves leading rows empty
+    # 136 (batch, head) pairs: 17 per XCD, so the causal issue order of short
+    # heads cuts them into a group of 16 (four whole GQA groups) and a ragged
+    # group of one
+    (2, 68, 17, 300, 300),
 ]
 
 
@@ -172,6 +176,7 @@ FP8_SHAPES = [
     (1, 4, 2, 300, 300),
     (1, 2, 2, 100, 260),
     (1, 2, 2, 260, 100),
+    (2, 68, 17, 300, 300),  # grouped causal order with a ragged last group
 ]
 
 
