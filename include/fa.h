@@ -38,8 +38,12 @@
  *
  * Conventions shared by every call.
  *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
- *     caller owns every buffer; the library allocates nothing and keeps no state,
+ *     caller owns every buffer and the library allocates nothing.  The only
+ *     state it keeps between calls is the per-thread message of fa_last_error(),
  *     so calls from several host threads are safe.
+ *   - With the environment variable FA_LOG set to a value other than "0", every
+ *     kernel launch prints one line to stderr before it is enqueued: the
+ *     kernel, its grid, block and LDS bytes, and the sizes it was chosen for.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy default
  *     stream) and return after enqueueing.  Nothing synchronises implicitly.
  *   - Parameters are validated on the host before anything is launched; on a
@@ -100,6 +104,15 @@ typedef enum {
  * lse may be NULL; otherwise it receives float32 natural-log LSE values.
  * softmax_scale multiplies Q K^T before the softmax (1/sqrt(d) for the usual
  * scaled dot-product attention); it must be finite and > 0.
+ * FP8 needs d = 128.  For FP8 the probabilities P are rounded once before the
+ * P V product (the row sum behind O's normaliser and the LSE uses them
+ * unrounded), in the precision fp8_p_bf16 selects:
+ *   0  e4m3, and P V runs on fp8 matrix cores (twice the bf16 rate).  Each
+ *      probability then carries up to 2^-4 relative rounding, so a row whose
+ *      softmax rests on a few keys can be off by up to about 2^-4 max|V|.
+ *   1  bf16, with the V codes converted exactly to bf16, and P V runs on bf16
+ *      matrix cores (2^-9 relative rounding per probability).
+ * fp8_p_bf16 must be 0 for the other input dtypes.
  */
 typedef struct {
   const void *q, *k, *v;
@@ -119,10 +132,15 @@ typedef struct {
    * each (batch, head) slice, [B][H][ceil(S / 64)] contiguous (H = Hq for q,
    * Hkv for k and v), all three or none; when given they replace
    * q/k/v_descale (the FlashAttention-3 page's block quantisation for fp8).
-   * The V descales should be powers of two (fa_fp8_quantize makes them so):
-   * a V tile's descale ratio to the slice's largest is folded into the
-   * probabilities before they are rounded to e4m3, exactly only then. */
+   * They are read on the device, so the host-side checks cannot see them:
+   * they must be finite and >= 0 (fa_fp8_quantize writes powers of two).
+   * A V tile's descale enters as its ratio to the slice's largest, folded
+   * into the probabilities before their rounding (see fp8_p_bf16); a ratio
+   * below 2^-20 is taken as 2^-20, which moves the output by at most
+   * 2^-19 max|V|.  With fp8_p_bf16 = 0, tiles whose ratio is below about
+   * 2^-6 also lose relative precision in e4m3's subnormal range. */
   const float *q_block_descale, *k_block_descale, *v_block_descale;
+  int32_t fp8_p_bf16; /* FP8 only: 0 = P in e4m3, 1 = P in bf16 (see above) */
 } fa_fwd_params;
 
 int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);

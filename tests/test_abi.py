@@ -337,3 +337,191 @@ def test_fwd_block_descales_validation(lib):
     q = good_fwd()
     q.q_block_descale = q.k_block_descale = q.v_block_descale = 0x50000
     assert fa.fa_check_fwd_params(q) == fa.FA_ERR_INVALID_ARG  # bf16 inputs take no descales
+
+
+def test_fwd_fp8_head_dim_and_p_precision(lib):
+    # the host check predicts the launcher: fp8 has a kernel for d = 128 only
+    p = good_fwd()
+    p.in_dtype = fa.FA_FP8_E4M3
+    p.q_descale = p.k_descale = p.v_descale = 1.0
+    for n in ("q_strides", "k_strides", "v_strides"):
+        setattr(p, n, fa.I64x3(8 * 100 * 128, 100 * 128, 128))
+    assert fa.fa_check_fwd_params(p) == fa.FA_OK
+    for pb in (0, 1):
+        p.fp8_p_bf16 = pb
+        assert fa.fa_check_fwd_params(p) == fa.FA_OK
+    p.fp8_p_bf16 = 2
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_INVALID_ARG
+    p.fp8_p_bf16 = 0
+    p.d = 64
+    for n in ("q_strides", "k_strides", "v_strides", "o_strides"):
+        setattr(p, n, fa.I64x3(8 * 100 * 64, 100 * 64, 64))
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_UNSUPPORTED
+    assert "128" in fa.fa_last_error()
+    q = good_fwd()
+    q.fp8_p_bf16 = 1  # bf16 inputs: the flag has no meaning
+    assert fa.fa_check_fwd_params(q) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fa_log_prints_the_launch(lib, tmp_path):
+    """FA_LOG=1 prints the chosen kernel, grid, block and LDS bytes before the
+    launch.  Run in a child process with no GPU visible, where the launch
+    itself then fails with FA_ERR_HIP after the line is printed."""
+    import subprocess
+    import sys
+
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("needs a process without a GPU: the call below passes fake device pointers")
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "import tiled_exact_attention_fa_amd as fa\n"
+        "sys.path.insert(0, " + repr(os.path.join(ROOT, "tests")) + ")\n"
+        "from test_abi import good_fwd\n"
+        "p = good_fwd(); p.causal = 1\n"
+        "print('status', fa.load().fa_fwd(ctypes.byref(p), None))\n"
+    )
+    env = dict(os.environ, FA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert f"status {fa.FA_ERR_HIP}" in r.stdout
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[fa] ")]
+    assert len(lines) == 1, r.stderr
+    ln = lines[0]
+    # 2 batches x 8 heads x one 256-row block of 100 rows
+    assert ln.startswith("[fa] fwd_mfma16_kernel grid=16 block=512 lds=")
+    assert "dtype=bf16 d=128 causal=1 B=2 Hq=8 G=4 Sq=100 Sk=100" in ln
+    r0 = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, FA_LOG="0"), capture_output=True,
+                        text=True, timeout=120)
+    assert "[fa] " not in r0.stderr
+
+
+# ---- the binding's own checks (the C ABI cannot see tensor shapes) -----------
+
+def _cpu(shape, dtype=None):
+    import torch
+
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _fwd_set():
+    import torch
+
+    q, k, v = _cpu((2, 8, 100, 128)), _cpu((2, 2, 100, 128)), _cpu((2, 2, 100, 128))
+    o, lse = _cpu((2, 8, 100, 128)), _cpu((2, 8, 100), torch.float32)
+    return dict(q=q, k=k, v=v, o=o, lse=lse)
+
+
+def test_binding_fwd_rejects_mismatches():
+    import torch
+
+    bad = [
+        ("v", _cpu((2, 2, 99, 128)), ValueError),            # shorter V: read past its end
+        ("o", _cpu((2, 8, 99, 128)), ValueError),            # shorter O: written past its end
+        ("k", _cpu((2, 2, 100, 128), torch.float16), TypeError),
+        ("o", _cpu((2, 8, 100, 128), torch.float16), TypeError),
+        ("lse", _cpu((2, 8, 100)), TypeError),               # bf16 lse gets 4-byte writes
+        ("lse", _cpu((2, 8, 100, 2), torch.float32)[..., 0], ValueError),  # sequence stride 2
+        ("q", _cpu((2, 8, 100, 128), torch.int8), TypeError),
+    ]
+    for name, t, exc in bad:
+        x = _fwd_set()
+        x[name] = t
+        with pytest.raises(exc):
+            fa.fwd_params(**x)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.fwd_params(**_fwd_set())
+
+
+def test_binding_fwd_block_descales_checked():
+    import torch
+
+    x = _fwd_set()
+    for n in ("q", "k", "v"):
+        x[n] = x[n].to(torch.float8_e4m3fn)
+    good = (_cpu((2, 8, 2), torch.float32), _cpu((2, 2, 2), torch.float32), _cpu((2, 2, 2), torch.float32))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.fwd_params(**x, block_descales=good)
+    with pytest.raises(ValueError):
+        fa.fwd_params(**x, block_descales=(good[0], good[1], _cpu((2, 2, 1), torch.float32)))
+    with pytest.raises(TypeError):
+        fa.fwd_params(**x, block_descales=(good[0], good[1], _cpu((2, 2, 2))))
+
+
+def _decode_set():
+    import torch
+
+    B, Hq, Hkv, L = 3, 8, 2, 64
+    return dict(q=_cpu((B, Hq, 128)), k_cache=_cpu((B, Hkv, L, 128), torch.int8),
+                v_cache=_cpu((B, Hkv, L, 128), torch.int8), k_scale=_cpu((B, Hkv, L), torch.float16),
+                v_scale=_cpu((B, Hkv, L), torch.float16), o=_cpu((B, Hq, 128)),
+                lse=_cpu((B, Hq), torch.float32), seq_lens=torch.full((B,), L, dtype=torch.int32))
+
+
+def test_binding_decode_rejects_mismatches():
+    import torch
+
+    bad = [
+        ("seq_lens", torch.full((3,), 64, dtype=torch.int64), TypeError),  # int64 would be misread
+        ("seq_lens", torch.full((2,), 64, dtype=torch.int32), ValueError),
+        ("v_cache", _cpu((3, 2, 63, 128), torch.int8), ValueError),
+        ("v_cache", _cpu((3, 2, 64, 128), torch.uint8), TypeError),
+        ("k_scale", _cpu((3, 2, 64), torch.float32), TypeError),
+        ("o", _cpu((3, 8, 128), torch.float16), TypeError),
+        ("lse", _cpu((3, 8)), TypeError),
+        ("q", _cpu((3, 8, 128), torch.float16), TypeError),
+    ]
+    for name, t, exc in bad:
+        x = _decode_set()
+        x[name] = t
+        with pytest.raises(exc):
+            fa.decode_params(**x)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.decode_params(**_decode_set())
+    x = _decode_set()
+    with pytest.raises(TypeError):   # window lengths must be int32 too
+        fa.decode_params(**x, k_recent=_cpu((3, 2, 4, 128)), v_recent=_cpu((3, 2, 4, 128)),
+                         recent_lens=torch.zeros(3, dtype=torch.int64))
+
+
+def test_binding_bwd_append_quant_reject_mismatches():
+    import torch
+
+    q, k = _cpu((1, 4, 50, 128)), _cpu((1, 2, 50, 128))
+    args = dict(q=q, k=k, v=k.clone(), o=q.clone(), dout=q.clone(), lse=_cpu((1, 4, 50), torch.float32),
+                dq=q.clone(), dk=k.clone(), dv=k.clone())
+    for name, t, exc in [("dv", _cpu((1, 2, 49, 128)), ValueError), ("lse", _cpu((1, 4, 50)), TypeError),
+                         ("dout", _cpu((1, 4, 50, 128), torch.float16), TypeError)]:
+        x = dict(args)
+        x[name] = t
+        with pytest.raises(exc):
+            fa.bwd_params(**x)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.bwd_params(**args)
+
+    ap = dict(k_new=_cpu((2, 2, 5, 128)), v_new=_cpu((2, 2, 5, 128)), k_cache=_cpu((2, 2, 16, 128), torch.int8),
+              v_cache=_cpu((2, 2, 16, 128), torch.int8), k_scale=_cpu((2, 2, 16), torch.float16),
+              v_scale=_cpu((2, 2, 16), torch.float16), positions=torch.zeros(2, dtype=torch.int32))
+    for name, t, exc in [("positions", torch.zeros(2, dtype=torch.int64), TypeError),
+                         ("v_new", _cpu((2, 2, 4, 128)), ValueError),
+                         ("v_scale", _cpu((2, 2, 15), torch.float16), ValueError)]:
+        x = dict(ap)
+        x[name] = t
+        with pytest.raises(exc):
+            fa.kv_append_params(**x)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.kv_append_params(**ap)
+
+    qp = dict(x=_cpu((1, 2, 70, 128)), codes=_cpu((1, 2, 70, 128), torch.uint8),
+              scales=_cpu((1, 2, 2), torch.float32))
+    for name, t, exc in [("scales", _cpu((1, 2, 1), torch.float32), ValueError),
+                         ("codes", _cpu((1, 2, 70, 128), torch.int8), TypeError),
+                         ("signs", _cpu((64,), torch.float32), ValueError)]:
+        x = dict(qp)
+        x[name] = t
+        with pytest.raises(exc):
+            fa.fp8_quant_params(**x)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        fa.fp8_quant_params(**qp)

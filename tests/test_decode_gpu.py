@@ -180,3 +180,39 @@ def test_decode_value_scales_spanning_the_chunk(gpu, fmt):
     err = float(np.max(np.abs(og - ro))) / scale
     assert err <= 1e-2, f"relative O err {err}"
     assert float(np.max(np.abs(lse.double().cpu().numpy() - rl))) <= TOL_LSE
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("path", ["staged", "vec8", "scalar2"])
+def test_decode_poisoned_cache_tail(gpu, fmt, path):
+    """Cache slots at or past seq_lens[b] hold +-Inf and NaN fp16 scales
+    (0x7C00, 0xFC00, 0x7E00) and, for fp8, the NaN codes 0x7F / 0xFF: only
+    the first seq_lens[b] tokens may reach the result.  Lengths are not
+    multiples of 32 or 4.  The three scale paths: scales staged in LDS (chunks
+    of at most 2048 tokens), 8-byte per-tile scale loads (longer chunks), and
+    2-byte loads (scale rows offset by one element)."""
+    lens = [184, 1, 3001, 2047, 33, 4095]
+    B, Hq, Hkv, L = len(lens), 8, 2, 4096
+    splits = 4 if path == "staged" else 1  # chunks of 1024 or 4096 tokens
+    cfg = fa_inputs.DecodeConfig("t", B, Hq, Hkv, L, 128, splits, tuple(lens), fmt)
+    xc = fa_inputs.make_decode_inputs(cfg, seed=31)
+    x = {k: v.clone() for k, v in xc.items()}
+    bits = torch.tensor([0x7C00, 0xFC00, 0x7E00], dtype=torch.int32).to(torch.int16)
+    for b, n in enumerate(lens):
+        pat = bits[torch.arange(L - n) % 3].view(torch.float16)
+        for key in ("k_scale", "v_scale"):
+            x[key][b, :, n:] = pat
+        for key in ("k", "v"):
+            if fmt == "fp8":
+                x[key][b, :, n:] = torch.where(torch.arange(L - n)[:, None] % 2 == 0, 0x7F, 0xFF).to(torch.uint8)
+            else:
+                x[key][b, :, n:] = 127
+    x = {k: v.cuda() for k, v in x.items()}
+    if path == "scalar2":
+        for key in ("k_scale", "v_scale"):
+            big = torch.zeros(B, Hkv, L + 1, dtype=torch.float16, device="cuda")
+            big[..., 1:] = x[key]
+            x[key] = big[..., 1:]
+    o, lse = run_decode(gpu, x, splits)
+    assert bool(torch.isfinite(o.float()).all()), "a token past seq_lens reached the output"
+    compare(o, lse, xc)

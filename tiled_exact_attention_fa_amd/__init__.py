@@ -54,6 +54,7 @@ class FaFwdParams(ctypes.Structure):
         ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
         ("q_block_descale", ctypes.c_void_p), ("k_block_descale", ctypes.c_void_p),
         ("v_block_descale", ctypes.c_void_p),
+        ("fp8_p_bf16", ctypes.c_int32),
     ]
 
 
@@ -241,14 +242,90 @@ def _require_dense_d(name, t):
         raise ValueError(f"{name}: the last (head) dimension must have stride 1")
 
 
+# The C ABI sees pointers and the sizes taken from q and k only, so every other
+# tensor is checked here against them: a shorter o or v, a bf16 lse or an int64
+# seq_lens would otherwise be read or written past its end by the kernels.
+
+def _dims(name, t, n):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != n:
+        raise ValueError(f"{name}: expected {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _expect(name, t, shape, dtypes):
+    """t has exactly `shape` and one of `dtypes` (a torch dtype or a tuple)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+
+
+def _expect_vector(name, t, n, dtype):
+    """A contiguous 1-D tensor of n elements of `dtype` (per-sequence lengths,
+    positions, rotation signs)."""
+    _expect(name, t, (n,), dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _unit_last_stride(name, t):
+    if t is not None and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must have stride 1")
+
+
+def _same_gpu(**tensors):
+    """Every given tensor lives on one GPU: a host pointer handed to a kernel
+    would fault the device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} is not on a GPU (device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
-               q_descale=1.0, k_descale=1.0, v_descale=1.0, block_descales=None) -> FaFwdParams:
-    """fa_fwd_params for BHSD-indexed tensors q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d],
-    o [B,Hq,Sq,d], lse [B,Hq,Sq] (any strides with a unit head-dim stride)."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _require_dense_d(n, t)
+               q_descale=1.0, k_descale=1.0, v_descale=1.0, block_descales=None,
+               p_bf16=False) -> FaFwdParams:
+    """fa_fwd_params for BHSD-indexed tensors q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d]
+    (q's dtype), o [B,Hq,Sq,d] (q's dtype, bf16 for fp8 inputs), lse [B,Hq,Sq]
+    float32 (any strides with a unit last stride), all on one GPU.  p_bf16
+    sets fp8_p_bf16 (fp8 inputs only)."""
+    import torch
+
+    _dims("q", q, 4)
+    _dims("k", k, 4)
     B, Hq, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
+    out_dt = {torch.float32: torch.float32, torch.float16: torch.float16, torch.bfloat16: torch.bfloat16,
+              torch.float8_e4m3fn: torch.bfloat16}.get(q.dtype)
+    if out_dt is None:
+        raise TypeError(f"q: dtype {q.dtype} is not an fa_fwd input type")
+    _expect("k", k, (B, Hkv, Sk, d), q.dtype)
+    _expect("v", v, (B, Hkv, Sk, d), q.dtype)
+    _expect("o", o, (B, Hq, Sq, d), out_dt)
+    if lse is not None:
+        _expect("lse", lse, (B, Hq, Sq), torch.float32)
+        _unit_last_stride("lse", lse)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _require_dense_d(n, t)
+    if block_descales is not None:
+        if len(block_descales) != 3:
+            raise ValueError("block_descales is a (q, k, v) triple")
+        for n, t, rows in zip(("q", "k", "v"), block_descales, (Sq, Sk, Sk)):
+            _expect(f"{n} block descales", t, (B, Hq if n == "q" else Hkv, (rows + 63) // 64), torch.float32)
+            if not t.is_contiguous():
+                raise ValueError("block descales must be contiguous")
+    bd = block_descales or (None, None, None)
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse, q_block_descale=bd[0], k_block_descale=bd[1], v_block_descale=bd[2])
     p = FaFwdParams()
     p.q, p.k, p.v, p.o, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)
     p.in_dtype, p.out_dtype = _dtype_code(q), _dtype_code(o)
@@ -262,18 +339,20 @@ def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
     p.causal = 1 if causal else 0
     p.q_descale, p.k_descale, p.v_descale = float(q_descale), float(k_descale), float(v_descale)
     if block_descales is not None:  # (q, k, v) float32 tensors [B, H, ceil(S / 64)], contiguous
-        for t in block_descales:
-            if not t.is_contiguous():
-                raise ValueError("block descales must be contiguous")
         p.q_block_descale, p.k_block_descale, p.v_block_descale = (_ptr(t) for t in block_descales)
+    p.fp8_p_bf16 = 1 if p_bf16 else 0
     return p
 
 
 def fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None,
-           q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None, block_descales=None) -> None:
+           q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None, block_descales=None,
+           p_bf16=False) -> None:
     """Enqueue the prefill forward on torch's current stream (or ``stream``).
-    ``block_descales``: optional (q, k, v) per-64-row descales for fp8 inputs."""
-    p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale, block_descales)
+    ``block_descales``: optional (q, k, v) per-64-row descales for fp8 inputs;
+    ``p_bf16``: fp8 inputs only, probabilities rounded to bf16 for P V instead
+    of e4m3."""
+    p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale, block_descales,
+                   p_bf16)
     st = load().fa_fwd(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd", fa_last_error())
@@ -296,11 +375,20 @@ def _kv_format(cache, kv_format):
 def fp8_quant_params(x, codes, scales, signs=None) -> FaFp8QuantParams:
     """fa_fp8_quant_params for x [B,H,S,d] bf16/fp16, codes [B,H,S,d] uint8 or
     float8_e4m3fn, scales [B,H,ceil(S/64)] float32 contiguous, signs [d] float32."""
-    _require_dense_d("x", x)
-    _require_dense_d("codes", codes)
+    import torch
+
+    _dims("x", x, 4)
+    B, H, S, d = x.shape
+    _expect("x", x, (B, H, S, d), (torch.bfloat16, torch.float16))
+    _expect("codes", codes, (B, H, S, d), (torch.uint8, torch.float8_e4m3fn))
+    _expect("scales", scales, (B, H, (S + 63) // 64), torch.float32)
     if not scales.is_contiguous():
         raise ValueError("scales must be contiguous")
-    B, H, S, d = x.shape
+    if signs is not None:
+        _expect_vector("signs", signs, d, torch.float32)
+    _require_dense_d("x", x)
+    _require_dense_d("codes", codes)
+    _same_gpu(x=x, codes=codes, scales=scales, signs=signs)
     p = FaFp8QuantParams()
     p.x, p.codes, p.scales, p.signs = _ptr(x), _ptr(codes), _ptr(scales), _ptr(signs)
     p.in_dtype = _dtype_code(x)
@@ -322,10 +410,25 @@ def bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=No
                workspace=None) -> FaBwdParams:
     """fa_bwd_params for q/o/dout/dq [B,Hq,Sq,d], k/v/dk/dv [B,Hkv,Sk,d] and
     lse [B,Hq,Sq] float32 (any strides with a unit head-dim stride)."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
-        _require_dense_d(n, t)
+    import torch
+
+    _dims("q", q, 4)
+    _dims("k", k, 4)
     B, Hq, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"q: dtype {q.dtype}, expected torch.bfloat16 or torch.float16")
+    for n, t in (("o", o), ("dout", dout), ("dq", dq)):
+        _expect(n, t, (B, Hq, Sq, d), q.dtype)
+    for n, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _expect(n, t, (B, Hkv, Sk, d), q.dtype)
+    _expect("lse", lse, (B, Hq, Sq), torch.float32)
+    _unit_last_stride("lse", lse)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _require_dense_d(n, t)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _same_gpu(q=q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
     p = FaBwdParams()
     p.q, p.k, p.v, p.o, p.dout, p.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse)
     p.dq, p.dk, p.dv = _ptr(dq), _ptr(dk), _ptr(dv)
@@ -362,6 +465,23 @@ def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=N
     o [B,Hq,d], lse [B,Hq], and an optional bf16 window k_recent/v_recent
     [B,Hkv,W,d]; k and v caches (and their scales, and the two window tensors)
     must share strides."""
+    import torch
+
+    _dims("q", q, 3)
+    _dims("k_cache", k_cache, 4)
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    codes = (torch.int8, torch.uint8, torch.float8_e4m3fn)
+    _expect("q", q, (B, Hq, d), torch.bfloat16)
+    _expect("k_cache", k_cache, (B, Hkv, L, d), codes)
+    _expect("v_cache", v_cache, (B, Hkv, L, d), k_cache.dtype)
+    _expect("k_scale", k_scale, (B, Hkv, L), torch.float16)
+    _expect("v_scale", v_scale, (B, Hkv, L), torch.float16)
+    _expect("o", o, (B, Hq, d), torch.bfloat16)
+    if lse is not None:
+        _expect("lse", lse, (B, Hq), torch.float32)
+    if seq_lens is not None:
+        _expect_vector("seq_lens", seq_lens, B, torch.int32)
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o),
                  ("k_scale", k_scale), ("v_scale", v_scale), ("k_recent", k_recent), ("v_recent", v_recent)):
         _require_dense_d(n, t)
@@ -369,10 +489,20 @@ def decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=N
         raise ValueError("k and v caches (and their scales) must have identical strides")
     if (k_recent is None) != (v_recent is None):
         raise ValueError("k_recent and v_recent go together")
-    if k_recent is not None and k_recent.stride() != v_recent.stride():
-        raise ValueError("k_recent and v_recent must have identical strides")
-    B, Hq, d = q.shape
-    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    if k_recent is not None:
+        _dims("k_recent", k_recent, 4)
+        W = k_recent.shape[2]
+        _expect("k_recent", k_recent, (B, Hkv, W, d), torch.bfloat16)
+        _expect("v_recent", v_recent, (B, Hkv, W, d), torch.bfloat16)
+        if k_recent.stride() != v_recent.stride():
+            raise ValueError("k_recent and v_recent must have identical strides")
+        if recent_lens is not None:
+            _expect_vector("recent_lens", recent_lens, B, torch.int32)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _same_gpu(q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale, o=o, lse=lse,
+              seq_lens=seq_lens, workspace=workspace, k_recent=k_recent, v_recent=v_recent,
+              recent_lens=recent_lens if k_recent is not None else None)
     p = FaDecodeParams()
     p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
     p.k_scale, p.v_scale, p.seq_lens = _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens)
@@ -422,13 +552,28 @@ def kv_append_params(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions
                      kv_format=None) -> FaKvAppendParams:
     """fa_kv_append_params for new rows k_new/v_new [B,H,T,d] (bf16 or fp16),
     caches [B,H,L,d] and scales [B,H,L]; positions [B] int32 or None."""
+    import torch
+
+    _dims("k_new", k_new, 4)
+    _dims("k_cache", k_cache, 4)
+    B, H, T, d = k_new.shape
+    L = k_cache.shape[2]
+    _expect("k_new", k_new, (B, H, T, d), (torch.bfloat16, torch.float16))
+    _expect("v_new", v_new, (B, H, T, d), k_new.dtype)
+    _expect("k_cache", k_cache, (B, H, L, d), (torch.int8, torch.uint8, torch.float8_e4m3fn))
+    _expect("v_cache", v_cache, (B, H, L, d), k_cache.dtype)
+    _expect("k_scale", k_scale, (B, H, L), torch.float16)
+    _expect("v_scale", v_scale, (B, H, L), torch.float16)
+    if positions is not None:
+        _expect_vector("positions", positions, B, torch.int32)
     for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("k_scale", k_scale), ("v_scale", v_scale)):
         _require_dense_d(n, t)
     if k_new.stride() != v_new.stride() or k_cache.stride() != v_cache.stride() \
             or k_scale.stride() != v_scale.stride():
         raise ValueError("k and v tensors of each kind must have identical strides")
-    B, H, T, d = k_new.shape
+    _same_gpu(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale,
+              positions=positions)
     p = FaKvAppendParams()
     p.k_new, p.v_new = _ptr(k_new), _ptr(v_new)
     p.k_cache, p.v_cache = _ptr(k_cache), _ptr(v_cache)

@@ -34,6 +34,8 @@
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 
 struct BwdArgs {
@@ -489,11 +491,20 @@ void bwd_dq_kernel(const BwdArgs a) {
 template <typename T>
 int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
   const long long rows = static_cast<long long>(a.B) * a.Hq * a.Sq;
-  if (rows > 0)
+  const char *dt = std::is_same<T, __bf16>::value ? "bf16" : "f16";
+  if (rows > 0) {
+    fa_log_launch("bwd_rowdot_kernel", static_cast<unsigned>((rows + 15) / 16), 256, 0, "dtype=%s rows=%lld", dt, rows);
     hipLaunchKernelGGL(bwd_rowdot_kernel<T>, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, a);
+  }
   const unsigned g_kv = static_cast<unsigned>((a.Sk + kDkdvKeys - 1) / kDkdvKeys) * a.B * a.Hkv;
   const unsigned g_q = static_cast<unsigned>((a.Sq + 127) / 128) * a.B * a.Hq;
   constexpr int BR = 32, BC = 32;  // query rows per dK/dV tile, keys per dQ tile
+  if (g_kv)
+    fa_log_launch("bwd_dkdv_kernel", g_kv, 512, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
+                  causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
+  if (g_q)
+    fa_log_launch("bwd_dq_kernel", g_q, 256, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
+                  causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
   if (causal) {
     if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, BR>), dim3(g_kv), dim3(512), 0, s, a);
     if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true, BC>), dim3(g_q), dim3(256), 0, s, a);

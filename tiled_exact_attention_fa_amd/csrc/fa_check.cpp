@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <initializer_list>
 
 namespace {
@@ -22,6 +24,25 @@ int fa_set_error(int status, const char *fmt, ...) {
 }
 
 void fa_clear_error() { g_last_error[0] = '\0'; }
+
+bool fa_log_enabled() {
+  static const bool on = [] {
+    const char *e = std::getenv("FA_LOG");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void fa_log_launch(const char *kernel, unsigned grid, unsigned block, unsigned lds_bytes, const char *fmt, ...) {
+  if (!fa_log_enabled()) return;
+  char what[256];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(what, sizeof(what), fmt, ap);
+  va_end(ap);
+  // one fprintf per line, so lines from several threads do not interleave
+  std::fprintf(stderr, "[fa] %s grid=%u block=%u lds=%u %s\n", kernel, grid, block, lds_bytes, what);
+}
 
 extern "C" const char *fa_status_string(int status) {
   switch (status) {
@@ -89,6 +110,12 @@ extern "C" int fa_check_fwd_params(const fa_fwd_params *p) {
                        (in == FA_F16 && out == FA_F16) || (in == FA_FP8_E4M3 && out == FA_BF16);
   if (!pair_ok)
     return fa_set_error(FA_ERR_UNSUPPORTED, "dtype pair in=%d out=%d not supported", in, out);
+  if (in == FA_FP8_E4M3 && p->d != 128)
+    return fa_set_error(FA_ERR_UNSUPPORTED, "fp8 forward supports head dim 128 only (d=%d)", p->d);
+  if (p->fp8_p_bf16 != 0 && p->fp8_p_bf16 != 1)
+    return fa_set_error(FA_ERR_INVALID_ARG, "fp8_p_bf16 must be 0 or 1");
+  if (p->fp8_p_bf16 != 0 && in != FA_FP8_E4M3)
+    return fa_set_error(FA_ERR_INVALID_ARG, "fp8_p_bf16 applies to fp8 inputs only");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
     return fa_set_error(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   const int nblk = (p->q_block_descale != nullptr) + (p->k_block_descale != nullptr) + (p->v_block_descale != nullptr);

@@ -495,15 +495,20 @@ void decode_split_kernel(const DecodeArgs a) {
         if (t + e < v1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
     };
     if constexpr (STAGED) {
-      // the staged value scales of this thread's 8 tokens
-      if (8 * tid < a.chunk) {
-        *reinterpret_cast<u32x4 *>(&s_sc[8 * tid]) = st_k;
-        *reinterpret_cast<u32x4 *>(&s_sc[kStageTok + 8 * tid]) = st_v;
-      }
-      const f16x8 sv = __builtin_bit_cast(f16x8, st_v);
+      // the staged value scales of this thread's 8 tokens.  Slots at or past
+      // c1 (the sequence's end inside this chunk) hold whatever the caller
+      // left there, possibly Inf or NaN: they are zeroed, because a masked
+      // token's weight is p * v_scale with p = 0, and 0 * Inf is NaN.
+      f16x8 sv = __builtin_bit_cast(f16x8, st_v);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (c0 + 8 * tid + e < c1) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
+        if (c0 + 8 * tid + e >= c1) sv[e] = static_cast<_Float16>(0.f);
+      if (8 * tid < a.chunk) {
+        *reinterpret_cast<u32x4 *>(&s_sc[8 * tid]) = st_k;
+        *reinterpret_cast<u32x4 *>(&s_sc[kStageTok + 8 * tid]) = __builtin_bit_cast(u32x4, sv);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, fabsf(static_cast<float>(sv[e])));
     } else {
       fold(vt0, vs_lo0, vs_hi0);
       for (int t = vt0 + 8 * 64; t < v1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
@@ -581,7 +586,14 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(sc[4 * tb + i] - m_use);
         lsum += p;
-        pf[4 * tb + i] = static_cast<_Float16>(p * (static_cast<float>(vscale[i]) * wmul));
+        float vsc = static_cast<float>(vscale[i]);
+        if constexpr (SCVEC && !STAGED) {
+          // the 8-byte scale loads reach up to three slots past c1, which may
+          // hold Inf or NaN; a masked token must weigh 0, not 0 * Inf
+          const int tok = t0 + 16 * tb + 4 * g + i;
+          vsc = tok < c1 ? vsc : 0.f;
+        }
+        pf[4 * tb + i] = static_cast<_Float16>(p * (vsc * wmul));
       }
     }
     l_run = l_run * alpha + lsum;
@@ -752,6 +764,9 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   const dim3 g1(grid1), b1(kDecodeThreads);
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
   const bool staged = a.sc_vec && a.chunk <= kStageTok;
+  fa_log_launch("decode_split_kernel", grid1, kDecodeThreads, 0,
+                "kv=%s scales=%s B=%d Hq=%d Hkv=%d L=%d splits=%d chunk=%d window=%d", fp8 ? "fp8" : "int8",
+                staged ? "staged" : (a.sc_vec ? "vec8" : "scalar2"), a.B, a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, a.W);
   if (staged && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true, true>), g1, b1, 0, s, a);
   else if (staged) hipLaunchKernelGGL((decode_split_kernel<true, false, true>), g1, b1, 0, s, a);
   else if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);
@@ -760,6 +775,7 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   else hipLaunchKernelGGL((decode_split_kernel<false, false>), g1, b1, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode split launch: %s", hipGetErrorString(e));
+  fa_log_launch("decode_combine_kernel", static_cast<unsigned>(p->B) * p->Hq, kD, 0, "slots=%d", a.nslots);
   hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(p->B) * p->Hq), dim3(kD), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "decode combine launch: %s", hipGetErrorString(e));

@@ -189,6 +189,8 @@ int fa_launch_fp8_quantize(const fa_fp8_quant_params *p, void *stream) {
   const dim3 grid(static_cast<unsigned>(p->B) * p->H * a.nb), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->in_dtype == FA_BF16, rot = p->signs != nullptr;
+  fa_log_launch("fp8_block_quant_kernel", grid.x, 256, 0, "in=%s rotate=%d B=%d H=%d S=%d", bf16 ? "bf16" : "f16",
+                rot ? 1 : 0, p->B, p->H, p->S);
   if (bf16 && rot) hipLaunchKernelGGL((fp8_block_quant_kernel<true, true>), grid, block, 0, s, a);
   else if (bf16) hipLaunchKernelGGL((fp8_block_quant_kernel<true, false>), grid, block, 0, s, a);
   else if (rot) hipLaunchKernelGGL((fp8_block_quant_kernel<false, true>), grid, block, 0, s, a);

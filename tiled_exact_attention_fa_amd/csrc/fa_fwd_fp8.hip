@@ -562,6 +562,9 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 
 template <bool CAUSAL, bool BLK> int launch_fp8(const FwdArgs &args, const Fp8BlockScales &bs, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
+  fa_log_launch("fwd_fp8_kernel", grid, f8::NT, f8::LDS_BYTES,
+                "causal=%d block_descales=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d", CAUSAL ? 1 : 0,
+                BLK ? 1 : 0, args.B, args.Hq, args.G, args.Sq, args.Sk, f8::BR);
   hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, BLK>), dim3(grid), dim3(f8::NT), 0, stream, args, bs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "fp8 launch: %s", hipGetErrorString(e));

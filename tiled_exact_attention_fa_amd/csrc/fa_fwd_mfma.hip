@@ -844,6 +844,11 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
     kern = fwd_mfma_kernel<T, D, CAUSAL>;
     lds_bytes = Cfg<T, D>::LDS_BYTES;
   }
+  const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
+  fa_log_launch(sizeof(T) == 2 ? "fwd_mfma16_kernel" : "fwd_mfma_kernel", grid, NT, lds_bytes,
+                "dtype=%s d=%d causal=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d",
+                sizeof(T) == 4 ? "f32" : (std::is_same<T, __bf16>::value ? "bf16" : "f16"), D, CAUSAL ? 1 : 0,
+                args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR);
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -852,7 +857,6 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
   });
   if (attr_err != hipSuccess)
     return fa_set_error(FA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
-  const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds_bytes, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "launch: %s", hipGetErrorString(e));

@@ -11,6 +11,13 @@ int fa_set_error(int status, const char *fmt, ...);
 void fa_clear_error();
 int fa_dtype_size(int dt);
 
+// FA_LOG: when the environment variable FA_LOG is set to anything but "0"
+// (read once), every launch prints one line to stderr before it is enqueued:
+// "[fa] <kernel> grid=<n> block=<n> lds=<bytes> <what fmt describes>".
+bool fa_log_enabled();
+void fa_log_launch(const char *kernel, unsigned grid, unsigned block, unsigned lds_bytes, const char *fmt, ...)
+    __attribute__((format(printf, 5, 6)));
+
 // Kernel launchers, one per kernel family (defined in the .hip files).  They
 // assume validated parameters and return FA_OK or FA_ERR_HIP.
 int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream);

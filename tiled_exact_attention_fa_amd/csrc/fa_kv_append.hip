@@ -208,6 +208,8 @@ int fa_launch_kv_append(const fa_kv_append_params *p, void *stream) {
   const bool bf16 = p->in_dtype == FA_BF16;
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
   const dim3 grid(blocks), block(kAppendThreads);
+  fa_log_launch("kv_append_kernel", blocks, kAppendThreads, 0, "in=%s kv=%s B=%d H=%d T=%d L=%d",
+                bf16 ? "bf16" : "f16", fp8 ? "fp8" : "int8", p->B, p->H, p->T, p->L);
   if (bf16 && fp8) hipLaunchKernelGGL((kv_append_kernel<true, true>), grid, block, 0, s, a);
   else if (bf16) hipLaunchKernelGGL((kv_append_kernel<true, false>), grid, block, 0, s, a);
   else if (fp8) hipLaunchKernelGGL((kv_append_kernel<false, true>), grid, block, 0, s, a);
