@@ -4,23 +4,28 @@
                     [--extra all|none|NAME,...] [--no-cpu-baseline]
 
 A step is one call of the hot path over one batch of synthetic input already
-resident in HBM.  The headline workload is causal bf16 prefill, B=4, H=16,
-S=2048, d=128 with LSE output; its TFLOP/s counts 4*d flops per visible
-(query, key) pair (S*(S+1)/2 pairs per head under the causal mask).  The other
-workloads are timed the same way and reported under "workloads": long-context
-GQA prefill, fp8 prefill and the backward of the two causal bf16 workloads in
-TFLOP/s (10 d flops per visible pair for the backward), the fp8 prefill on
-64-row block-scaled, rotated codes in TFLOP/s; int8-KV and fp8-KV split decode, the
-decode with a bf16 residual window, the quantise-on-append of a 4096-token
-chunk and the fp8 block quantiser of one prefill's Q, K and V in GB/s of the
-bytes the method must move (codes + scales + window + query + output + LSE for
-decode; rows read and codes + scales written for the append and the quantiser).
+resident in HBM.  The headline workload is the largest prefill configuration:
+causal bf16 long-context grouped-query prefill, B=1, Hq=32, Hkv=8, S=16384,
+d=128, 1 % of the key rows scaled by 8, with LSE output; its TFLOP/s counts
+4*d flops per visible (query, key) pair (S*(S+1)/2 pairs per head under the
+causal mask).  The other workloads are timed the same way and reported under
+"workloads": the other four configurations (fp32 S=128, causal bf16 B=4 H=16
+S=2048, fp8 B=8 H=16 S=4096, int8-KV split decode), the backward of the two
+causal bf16 workloads in TFLOP/s (10 d flops per visible pair), the fp8
+prefill on 64-row block-scaled, rotated codes, the fp8 prefill with bf16
+probabilities, fp8-KV decode, the decode with a bf16 residual window, the
+quantise-on-append of a 4096-token chunk and the fp8 block quantiser in GB/s
+of the bytes the method must move.
 
 Timing uses HIP events on the stream the kernels are launched on (torch's
 current stream), bracketed by device synchronisations, after at least W
-untimed calls and at least 0.3 s of untimed work, so the clocks have settled.  The CPU baseline is the
-float64 oracle timed on this host's cores over a bounded sample of the headline
-workload, rescaled to the same unit.  Prints ONE JSON line.
+untimed calls and at least 0.3 s of untimed work, so the clocks have settled.
+"ms_per_call" is the mean over the timed region; a second pass with an event
+pair around every call gives "ms_median" and "ms_min".  For each of the five
+configurations the float64 oracle is then timed on this host's cores over a
+bounded sample (whole heads, or whole batch entries for decode), reported as
+"cpu_baseline" in the workload's unit, and the GPU outputs of that sample are
+compared with it ("max_abs_err").  Prints ONE JSON line.
 """
 
 from __future__ import annotations
@@ -43,7 +48,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-HEADLINE = "bf16_b4_h16_s2048_causal"
+HEADLINE = "bf16_gqa32x8_s16384_causal_outlier"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -176,7 +181,121 @@ def _time_region(fn, steps, warmup):
     return start.elapsed_time(stop) / steps, wall
 
 
-def _fwd_runner(cfg, seed=0):
+def _time_each(fn, steps):
+    """Per-call times (ms) from an event pair around every call, on the launch
+    stream; run right after _time_region, so the clocks are settled."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+
+class Runner:
+    """One workload on the GPU: run() enqueues one call; check(budget_s), when
+    given, times the float64 oracle on a bounded sample of the same inputs and
+    compares the GPU outputs of that sample with it."""
+
+    def __init__(self, run, check=None):
+        self.run = run
+        self.check = check
+
+
+def _cores():
+    return len(os.sched_getaffinity(0))
+
+
+def _fwd_oracle_check(cfg, x, o, lse, budget_s):
+    """The oracle over whole (batch, head) pairs of a prefill workload, as many
+    as fit the budget (whole passes repeated when the workload is smaller).
+    The inputs are upcast (fp8: decoded and descaled) to float64 once, before
+    the timed part."""
+    import numpy as np
+
+    import oracle
+    from oracle.e4m3 import e4m3_decode
+
+    if cfg.dtype == "fp8":
+        qf = e4m3_decode(x["q"].cpu()) * x["q_scale"]
+        kf = e4m3_decode(x["k"].cpu()) * x["k_scale"]
+        vf = e4m3_decode(x["v"].cpu()) * x["v_scale"]
+    else:
+        qf, kf, vf = (x[n].cpu().double().numpy() for n in ("q", "k", "v"))
+    og = o.cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    cores = _cores()
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    n = min(len(heads), cores)
+    done, elapsed, err_o, err_l, checked = 0, 0.0, 0.0, 0.0, 0
+    while done == 0 or elapsed < budget_s * 0.85:
+        start = done % len(heads)
+        part = heads[start:start + n]
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention_fp64(qf, kf, vf, cfg.causal, cfg.scale, heads=part, threads=cores)
+        elapsed += time.perf_counter() - t0
+        if done < len(heads):  # first pass: compare
+            bi = [b for b, _ in part]
+            hi = [h for _, h in part]
+            err_o = max(err_o, float(np.max(np.abs(og[bi, hi] - ro[bi, hi]))))
+            fin = np.isfinite(rl[bi, hi])
+            err_l = max(err_l, float(np.max(np.abs(lg[bi, hi][fin] - rl[bi, hi][fin]), initial=0.0)))
+            checked += len(part)
+        done += len(part)
+        # stop before a chunk that would overrun the budget
+        if elapsed / done * (done + n) > budget_s:
+            break
+    flops = fwd_flops(cfg) * done / len(heads)
+    if done <= len(heads):
+        sample = f"{done} of {len(heads)} (batch, head) pairs"
+    else:
+        sample = f"{done / len(heads):.1f} passes over all {len(heads)} (batch, head) pairs"
+    cpu = {"value": flops / elapsed / 1e9, "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{sample} of {cfg.name}, float64 numpy two-pass, {elapsed:.1f} s wall"}
+    err = {"O": err_o, "LSE": err_l, "sample": f"{checked} of {len(heads)} (batch, head) pairs, every row"}
+    return cpu, err
+
+
+def _decode_oracle_check(cfg, x, o, lse, budget_s):
+    """The oracle over whole batch entries of a decode workload (every query
+    head of the entry), as many as fit the budget; the oracle dequantises the
+    codes it reads.  GB/s of the entries' share of the algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+
+    cores = _cores()
+    og = o.cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    done, elapsed, err_o, err_l = 0, 0.0, 0.0, 0.0
+    order = [0, cfg.B - 1] + list(range(1, cfg.B - 1))
+    per_entry = decode_bytes(cfg) / cfg.B
+    while done < cfg.B:
+        b = order[done]
+        sub = {n: x[n][b:b + 1].cpu() for n in ("q", "k", "v", "k_scale", "v_scale", "seq_lens")}
+        t0 = time.perf_counter()
+        ro, rl = oracle.decode_fp64(sub["q"], sub["k"].numpy(), sub["k_scale"].numpy(), sub["v"].numpy(),
+                                    sub["v_scale"].numpy(), sub["seq_lens"].numpy(), scale=cfg.scale,
+                                    threads=cores, kv_format=cfg.kv_format)
+        elapsed += time.perf_counter() - t0
+        err_o = max(err_o, float(np.max(np.abs(og[b:b + 1] - ro))))
+        fin = np.isfinite(rl)
+        err_l = max(err_l, float(np.max(np.abs(lg[b:b + 1][fin] - rl[fin]), initial=0.0)))
+        done += 1
+        if elapsed / done * (done + 1) > budget_s:
+            break
+    cpu = {"value": per_entry * done / elapsed / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done} of {cfg.B} batch entries of {cfg.name} (all {cfg.Hq} heads each), float64 numpy, "
+                     f"{elapsed:.1f} s wall"}
+    err = {"O": err_o, "LSE": err_l, "sample": f"{done} of {cfg.B} batch entries, every head"}
+    return cpu, err
+
+
+def _fwd_runner(cfg, seed=0, p_bf16=False):
     import torch
 
     import tiled_exact_attention_fa_amd as fa
@@ -190,9 +309,9 @@ def _fwd_runner(cfg, seed=0):
 
     def run():
         fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale,
-                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
+                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], p_bf16=p_bf16)
 
-    return run
+    return Runner(run, lambda budget: _fwd_oracle_check(cfg, x, o, lse, budget))
 
 
 def _quantise_block_fp8(fa, x, signs):
@@ -229,7 +348,7 @@ def _fp8_block_runner(cfg, seed=0):
     def run():
         fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale, block_descales=bds)
 
-    return run
+    return Runner(run)
 
 
 def _quant_runner(cfg, seed=0):
@@ -240,7 +359,7 @@ def _quant_runner(cfg, seed=0):
     def run():
         _quantise_block_fp8(fa, x, x["signs"])
 
-    return run
+    return Runner(run)
 
 
 def _decode_runner(cfg, seed=0):
@@ -261,7 +380,8 @@ def _decode_runner(cfg, seed=0):
                          seq_lens=x["seq_lens"], num_splits=cfg.num_splits,
                          softmax_scale=cfg.scale, workspace=ws, kv_format=cfg.kv_format, **win)
 
-    return run
+    check = None if cfg.W > 0 else (lambda budget: _decode_oracle_check(cfg, x, o, lse, budget))
+    return Runner(run, check)
 
 
 def _bwd_runner(cfg, seed=0):
@@ -280,7 +400,7 @@ def _bwd_runner(cfg, seed=0):
     def run():
         fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=cfg.causal, softmax_scale=cfg.scale, workspace=ws)
 
-    return run
+    return Runner(run)
 
 
 def _append_runner(cfg, seed=0):
@@ -292,7 +412,7 @@ def _append_runner(cfg, seed=0):
         fa.fa_kv_append(x["k_new"], x["v_new"], x["k_cache"], x["v_cache"], x["k_scale"], x["v_scale"],
                         positions=x["positions"], kv_format=cfg.kv_format)
 
-    return run
+    return Runner(run)
 
 
 # the files that hold each kernel family's device code
@@ -344,84 +464,50 @@ def stored_traffic(name: str):
     return ent.get("bytes_per_launch")
 
 
-def measure(name, steps, warmup):
+def measure(name, steps, warmup, check_budget=0.0):
+    """Times one workload; with check_budget > 0 and an oracle check for it,
+    also the CPU baseline and the max error on the oracle's sample."""
     cfg = workload(name)
     import torch
 
+    if isinstance(cfg, fa_inputs.DecodeConfig):
+        r = _decode_runner(cfg)
+    elif isinstance(cfg, fa_inputs.AppendConfig):
+        r = _append_runner(cfg)
+    elif isinstance(cfg, fa_inputs.QuantConfig):
+        r = _quant_runner(cfg)
+    elif isinstance(cfg, fa_inputs.BwdConfig):
+        r = _bwd_runner(cfg)
+    elif isinstance(cfg, fa_inputs.Fp8BlockConfig):
+        r = _fp8_block_runner(cfg)
+    else:
+        r = _fwd_runner(cfg, p_bf16=isinstance(cfg, fa_inputs.Fp8PBf16Config))
+    ms, wall = _time_region(r.run, steps, warmup)
+    each = _time_each(r.run, steps)
+    med, mn = each[len(each) // 2], each[0]
     if isinstance(cfg, (fa_inputs.DecodeConfig, fa_inputs.AppendConfig, fa_inputs.QuantConfig)):
-        if isinstance(cfg, fa_inputs.DecodeConfig):
-            run = _decode_runner(cfg)
-        elif isinstance(cfg, fa_inputs.AppendConfig):
-            run = _append_runner(cfg)
-        else:
-            run = _quant_runner(cfg)
-        ms, wall = _time_region(run, steps, warmup)
         work = algorithmic_bytes(cfg)
         gbs = work / (ms * 1e-3) / 1e9
-        res = {"unit": "GB/s", "value": gbs, "ms_per_call": ms, "bytes_per_call": work,
+        res = {"unit": "GB/s", "value": gbs, "bytes_per_call": work,
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic(name)}}
     else:
-        bwd = isinstance(cfg, fa_inputs.BwdConfig)
-        if bwd:
-            run = _bwd_runner(cfg)
-        elif isinstance(cfg, fa_inputs.Fp8BlockConfig):
-            run = _fp8_block_runner(cfg)
-        else:
-            run = _fwd_runner(cfg)
-        ms, wall = _time_region(run, steps, warmup)
-        work = bwd_flops(cfg) if bwd else fwd_flops(cfg)
+        work = bwd_flops(cfg) if isinstance(cfg, fa_inputs.BwdConfig) else fwd_flops(cfg)
         tf = work / (ms * 1e-3) / 1e12
         # a contraction is priced against the dense MFMA peak of its own input type
         peak = {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
-        res = {"unit": "TFLOP/s", "value": tf, "ms_per_call": ms, "flops_per_call": work,
+        res = {"unit": "TFLOP/s", "value": tf, "flops_per_call": work,
                "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
                             "frac": tf / peak, "traffic": stored_traffic(name)}}
         if cfg.dtype == "fp8":
             # the prefill target is stated against the bf16 peak for every input type
             res["frac_of_bf16_peak"] = tf / PEAK_BF16_TFLOPS
-    res["wall_s"] = wall
-    del run
+    res.update({"ms_per_call": ms, "ms_median": med, "ms_min": mn, "wall_s": wall})
+    if check_budget > 0 and r.check is not None:
+        res["cpu_baseline"], res["max_abs_err"] = r.check(check_budget)
+    del r
     torch.cuda.empty_cache()
     return res
-
-
-# ---- CPU baseline -------------------------------------------------------------
-
-def cpu_baseline(name, budget_s=12.0):
-    """The float64 oracle on this host's cores over whole heads of the workload,
-    as many as fit the time budget; reported in the workload's own unit.  When
-    the whole workload takes less than the budget, it is run again (whole
-    passes) until the budget is used, so that the rate is not a sub-second
-    sample."""
-    import oracle
-
-    cfg = fa_inputs.CONFIGS[name]
-    cores = len(os.sched_getaffinity(0))
-    x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cpu")
-    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
-    # calibrate on as many heads as there are cores, then scale up to the budget
-    n = min(len(heads), cores)
-    t0 = time.perf_counter()
-    oracle.attention_fp64(x["q"], x["k"], x["v"], cfg.causal, cfg.scale, heads=heads[:n], threads=cores)
-    dt = time.perf_counter() - t0
-    done, elapsed = n, dt
-    while elapsed + dt * 1.2 < budget_s:
-        start = done % len(heads)
-        m = min(len(heads) - start, n)
-        t0 = time.perf_counter()
-        oracle.attention_fp64(x["q"], x["k"], x["v"], cfg.causal, cfg.scale,
-                              heads=heads[start:start + m], threads=cores)
-        dt = time.perf_counter() - t0
-        done += m
-        elapsed += dt
-    flops = fwd_flops(cfg) * done / len(heads)
-    if done <= len(heads):
-        sample = f"{done} of {len(heads)} (batch, head) pairs of {name}"
-    else:
-        sample = f"{done / len(heads):.1f} passes over all {len(heads)} (batch, head) pairs of {name}"
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample}, float64 numpy two-pass, {elapsed:.1f} s wall"}
 
 
 # ---- HBM traffic from rocprofv3 counters ------------------------------------
@@ -519,7 +605,8 @@ def main():
 
     fa.load()
     torch.cuda.set_device(0)
-    head = measure(a.workload, a.steps, a.warmup)
+    cpu_on = not a.no_cpu_baseline
+    head = measure(a.workload, a.steps, a.warmup, check_budget=12.0 if cpu_on else 0.0)
     cfg = workload(a.workload)
 
     extras = {}
@@ -530,15 +617,20 @@ def main():
     elif a.extra != "all":
         names = [n for n in a.extra.split(",") if n]
     for n in names:
+        # the five configurations also get the oracle baseline and error check
+        budget = 4.0 if cpu_on and n in fa_inputs.CONFIGS else 0.0
         try:
-            extras[n] = measure(n, max(3, a.steps // 5), max(2, a.warmup // 2))
+            extras[n] = measure(n, max(3, a.steps // 5), max(2, a.warmup // 2), check_budget=budget)
         except Exception as e:  # an unbuilt kernel is reported, not hidden
             extras[n] = {"error": f"{type(e).__name__}: {e}"}
         print(f"# {n}: {json.dumps(extras[n])}", file=sys.stderr, flush=True)
 
     cpu = None
-    if not a.no_cpu_baseline and isinstance(cfg, fa_inputs.FwdConfig):
-        cpu = cpu_baseline(a.workload)
+    if "cpu_baseline" in head:
+        # in the metric's own unit (TFLOP/s or GB/s)
+        cpu = dict(head["cpu_baseline"])
+        if cpu["unit"] == "GFLOP/s":
+            cpu["value"], cpu["unit"] = cpu["value"] / 1e3, "TFLOP/s"
 
     dtype = {"f32": "f32", "bf16": "bf16", "f16": "f16", "fp8": "fp8_e4m3"}.get(getattr(cfg, "dtype", ""), "bf16")
     conf = {"workload": a.workload}
@@ -559,8 +651,11 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": conf,
+        "ms_median": head["ms_median"],
+        "ms_min": head["ms_min"],
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "max_abs_err": head.get("max_abs_err"),
         "workloads": extras,
         "device": torch.cuda.get_device_name(0),
     }

@@ -153,9 +153,18 @@ KV_CONFIGS = {
     "append_fp8_b64_h8_t4096": AppendConfig("append_fp8_b64_h8_t4096", 64, 8, 4096, 32768, 128, "fp8", 28672),
 }
 
+@dataclass(frozen=True)
+class Fp8PBf16Config(FwdConfig):
+    """An fp8 prefill workload run with the probabilities rounded to bf16 for
+    P V (fa_fwd_params.fp8_p_bf16 = 1); same inputs as FwdConfig."""
+
+
 # The fp8 accuracy variants at the fp8 workload's shape: the forward on
-# block-scaled codes, and the quantiser that makes them.
+# block-scaled codes, the quantiser that makes them, and the per-tensor fp8
+# workload with bf16 probabilities.
 FP8_VARIANT_CONFIGS = {
+    "fp8_pbf16_b8_h16_s4096": Fp8PBf16Config("fp8_pbf16_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128, False,
+                                             out_dtype="bf16"),
     "fp8_block_rot_b8_h16_s4096": Fp8BlockConfig("fp8_block_rot_b8_h16_s4096", "fp8", 8, 16, 16, 4096, 4096, 128,
                                                  False, out_dtype="bf16", rotate=True),
     "fp8_quant_rot_b8_h16_s4096": QuantConfig("fp8_quant_rot_b8_h16_s4096", 8, 16, 4096, 128, True),

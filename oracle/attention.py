@@ -72,14 +72,15 @@ def _two_pass_rows(qh, kh, vh, scale, n_vis, row_block):
     Pass 2: O_i = sum_j exp(s_ij - m_i) / l_i * V_j ;  LSE_i = m_i + ln l_i.
     """
     Sq = qh.shape[0]
-    Sk = kh.shape[0]
     o = np.zeros((Sq, vh.shape[1]), dtype=np.float64)
     lse = np.full((Sq,), -np.inf, dtype=np.float64)
-    cols = np.arange(Sk)
     for r0 in range(0, Sq, row_block):
         r1 = min(Sq, r0 + row_block)
-        s = (qh[r0:r1] @ kh.T) * scale  # [R, Sk]
-        vis = cols[None, :] < n_vis[r0:r1, None]
+        # keys past the block's last visible one are never evaluated: under the
+        # mask they would enter only as exact zeros
+        nk = int(n_vis[r0:r1].max(initial=0))
+        s = (qh[r0:r1] @ kh[:nk].T) * scale  # [R, nk]
+        vis = np.arange(nk)[None, :] < n_vis[r0:r1, None]
         s = np.where(vis, s, -np.inf)
         has = n_vis[r0:r1] > 0
         # pass 1: row max and normaliser
@@ -88,7 +89,7 @@ def _two_pass_rows(qh, kh, vh, scale, n_vis, row_block):
         l = e.sum(axis=1)
         # pass 2: normalised probabilities times V
         p = e / np.where(has, l, 1.0)[:, None]
-        o[r0:r1] = p @ vh
+        o[r0:r1] = p @ vh[:nk]
         lse[r0:r1] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
     return o, lse
 

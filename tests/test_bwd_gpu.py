@@ -129,18 +129,15 @@ def test_bwd_workspace_too_small(gpu):
     assert e.value.status == gpu.FA_ERR_WORKSPACE
 
 
-def test_bwd_full_size_sampled(gpu):
-    """The causal bf16 workload at full size (B=4, H=16, S=2048, d=128); with
-    one query head per kv head, a sampled head's oracle gives its complete
-    dQ, dK and dV."""
+def test_bwd_full_size(gpu):
+    """The causal bf16 workload at full size (B=4, H=16, S=2048, d=128), in
+    the launch configuration the benchmark times: every element of dQ, dK and
+    dV against the oracle."""
     cfg = fa_inputs.CONFIGS["bf16_b4_h16_s2048_causal"]
     x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(99)
     dout = torch.randn(cfg.B, cfg.Hq, cfg.Sq, cfg.d, generator=g, device="cuda").to(torch.bfloat16)
     dq, dk, dv = run_bwd(gpu, x, dout, True)
-    for b, h in [(0, 0), (1, 7), (3, 15)]:
-        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
-        rq, rk, rv = oracle.attention_bwd_fp64(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(dout), True)
-        check(dq[b:b + 1, h:h + 1], rq, "dQ")
-        check(dk[b:b + 1, h:h + 1], rk, "dK")
-        check(dv[b:b + 1, h:h + 1], rv, "dV")
+    rq, rk, rv = oracle.attention_bwd_fp64(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), dout.cpu(), True)
+    errs = [check(dq, rq, "dQ"), check(dk, rk, "dK"), check(dv, rv, "dV")]
+    print("full-size backward, every element: relative max errors dQ/dK/dV", errs, flush=True)

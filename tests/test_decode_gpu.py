@@ -101,24 +101,19 @@ def test_decode_workspace_too_small(gpu):
     assert e.value.status == gpu.FA_ERR_WORKSPACE
 
 
-def test_decode_full_size_sampled(gpu):
+def test_decode_full_size(gpu):
     """The int8 cache workload at full size (B=64, 32/8 heads, L=32768, 16
-    splits), inputs drawn on the GPU; outputs checked on sampled heads."""
+    splits), inputs drawn on the GPU, in the launch configuration the
+    benchmark times; every (batch, head) row of O and LSE is compared with the
+    oracle, and all of O is checked for unwritten (NaN) elements."""
     cfg = fa_inputs.CONFIGS["decode_int8_b64_gqa32x8_L32768"]
     x = fa_inputs.make_decode_inputs(cfg, seed=0, device="cuda")
     o, lse = run_decode(gpu, x, cfg.num_splits)
-    samples = [(0, 0), (0, 31), (17, 5), (33, 12), (63, 30), (40, 19)]
-    for b, h in samples:
-        kvh = h // (cfg.Hq // cfg.Hkv)
-        sub = {
-            "q": x["q"][b:b + 1, h:h + 1].cpu(),
-            "k": x["k"][b:b + 1, kvh:kvh + 1].cpu(),
-            "v": x["v"][b:b + 1, kvh:kvh + 1].cpu(),
-            "k_scale": x["k_scale"][b:b + 1, kvh:kvh + 1].cpu(),
-            "v_scale": x["v_scale"][b:b + 1, kvh:kvh + 1].cpu(),
-            "seq_lens": x["seq_lens"][b:b + 1].cpu(),
-        }
-        compare(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], sub)
+    assert not bool(torch.isnan(o.float()).any()) and not bool(torch.isnan(lse).any())
+    xc = {k: v.cpu() for k, v in x.items()}
+    del x
+    err = compare(o, lse, xc)
+    print(f"decode full size: every row, max|dO|={err:.3g}", flush=True)
 
 
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])

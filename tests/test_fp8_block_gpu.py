@@ -3,7 +3,8 @@
 * fa_fp8_quantize (64-row block scales, optional random-sign Hadamard rotation)
   against the oracle's quantiser: codes and scales bit-exact;
 * fa_fwd on fp8 codes with block descales against the float64 oracle fed the
-  same dequantised values (O within 8e-2, LSE within 1e-3);
+  same dequantised values (O within 8e-2, LSE within 1e-3), with the
+  probabilities rounded to e4m3 or (fp8_p_bf16) to bf16 for P V;
 * the variants' error against exact attention of the unquantised bf16 inputs
   on the long-context workload's outlier distribution (1 % of key rows x 8),
   per-tensor scales versus block scales versus block scales with rotation.
@@ -22,6 +23,29 @@ pytestmark = pytest.mark.gpu
 
 TOL_O = 8e-2
 TOL_LSE = 1e-3
+# The fp8 matrix instructions sum their products to about 2^-11.4 of the
+# largest product (measured by test_fp8_score_accumulation_precision through
+# the LSE of a single-key problem); a score of d = 128 takes two 64-deep
+# instructions, so its error is at most 2^-10 of its largest product.
+FP8_ACC_REL = 2.0 ** -10
+
+
+def fp8_lse_bound(qd, kd, causal, G, tau):
+    """Per-row bound on the fp8 path's LSE error from the score accumulation:
+    the LSE moves by at most the largest score error among the visible keys,
+    FP8_ACC_REL * tau * max over visible keys j and channels c of
+    |q_ic k_jc| (dequantised values); at least the 1e-3 bar.  [B, Hq, Sq]."""
+    B, Hq, Sq, d = qd.shape
+    Sk = kd.shape[2]
+    out = np.empty((B, Hq, Sq))
+    for b in range(B):
+        for kh in range(kd.shape[1]):
+            ak = np.abs(kd[b, kh])
+            vis = np.maximum.accumulate(ak, axis=0) if causal else np.broadcast_to(ak.max(axis=0), ak.shape)
+            rows = np.minimum(np.arange(Sq) + Sk - Sq, Sk - 1).clip(0)
+            for h in range(kh * G, kh * G + G):
+                out[b, h] = np.max(np.abs(qd[b, h]) * vis[rows], axis=1)
+    return np.maximum(TOL_LSE, FP8_ACC_REL * tau * out)
 
 
 def _signs(seed, d=128):
@@ -88,18 +112,19 @@ def _fp8_inputs(cfg, seed, signs=None, block=True):
     return x, out, deq
 
 
-def run_fp8(fa, out, causal, block=True):
+def run_fp8(fa, out, causal, block=True, p_bf16=False):
     q, k, v = (out[n].cuda().view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
     B, Hq, Sq, d = q.shape
     o = torch.full((B, Hq, Sq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, Hq, Sq), float("nan"), device="cuda")
-    print(f"fa_fwd fp8 q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} block={block}", flush=True)
+    print(f"fa_fwd fp8 q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} block={block} p_bf16={p_bf16}",
+          flush=True)
     if block:
         bds = tuple(out[n + "_bs"].cuda().contiguous() for n in ("q", "k", "v"))
-        fa.fa_fwd(q, k, v, o, lse, causal=causal, block_descales=bds)
+        fa.fa_fwd(q, k, v, o, lse, causal=causal, block_descales=bds, p_bf16=p_bf16)
     else:
         fa.fa_fwd(q, k, v, o, lse, causal=causal, q_descale=out["q_ts"], k_descale=out["k_ts"],
-                  v_descale=out["v_ts"])
+                  v_descale=out["v_ts"], p_bf16=p_bf16)
     torch.cuda.synchronize()
     return o, lse
 
@@ -114,12 +139,13 @@ FWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("p_bf16", [False, True], ids=["p_e4m3", "p_bf16"])
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", FWD_CASES)
-def test_block_descale_forward(gpu, B, Hq, Hkv, Sq, Sk, causal):
+def test_block_descale_forward(gpu, B, Hq, Hkv, Sq, Sk, causal, p_bf16):
     # the fp8 workload's distribution (N(0,1) draws, no outlier rows)
     cfg = fa_inputs.FwdConfig("t", "fp8", B, Hq, Hkv, Sq, Sk, 128, causal)
     _, out, deq = _fp8_inputs(cfg, seed=Sq + Sk)
-    o, lse = run_fp8(gpu, out, causal)
+    o, lse = run_fp8(gpu, out, causal, p_bf16=p_bf16)
     ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], causal)
     og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
     assert not np.isnan(og).any()
@@ -198,41 +224,119 @@ def test_quantise_then_forward_full_size_sampled(gpu):
         assert float(np.max(np.abs(lse[b, h, rows].double().cpu().numpy() - rl[0, 0]))) <= TOL_LSE
 
 
-@pytest.mark.timeout(600)
+def test_block_descales_of_any_ratio(gpu):
+    """Block descales that are not powers of two (plain absmax / 448 per
+    64-row block, and V blocks whose absmax differs by factors up to ~40 so the
+    descale ratios are arbitrary): the V ratio is folded into the
+    probabilities before their rounding, which with bf16 probabilities adds no
+    error beyond that rounding.  Every element within the 8e-2 bar with bf16
+    probabilities; the e4m3 mode is held to its documented envelope,
+    2^-4 max|V| (+1e-2), since the V blocks here reach |V| of about 16."""
+    B, Hq, Hkv, S = 1, 4, 2, 700
+    g = torch.Generator().manual_seed(41)
+    raw = {n: torch.randn(B, Hq if n == "q" else Hkv, S, 128, generator=g) for n in ("q", "k", "v")}
+    raw["v"] *= torch.exp(torch.randn(B, Hkv, S // 64 + 1, 1, generator=g)).repeat_interleave(64, 2)[:, :, :S]
+    out, deq = {}, {}
+    for n, t in raw.items():
+        t = t.to(torch.bfloat16).float()
+        nb = (S + 63) // 64
+        pad = torch.zeros(B, t.shape[1], nb * 64, 128)
+        pad[:, :, :S] = t
+        amax = pad.view(B, t.shape[1], nb, 64 * 128).abs().amax(-1)
+        sc = (amax / 448.0).to(torch.float32)
+        y = (pad / sc.repeat_interleave(64, 2)[..., None]).clamp(-448, 448)[:, :, :S]
+        out[n] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        out[n + "_bs"] = sc.contiguous()
+        deq[n] = oracle.dequant_fp8_blocks_fp64(out[n].numpy(), sc.numpy())
+    assert not bool(torch.frexp(out["v_bs"]).mantissa.eq(0.5).all())  # not powers of two
+    ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], True)
+    vmax = float(np.max(np.abs(deq["v"])))
+    for p_bf16 in (True, False):
+        o, lse = run_fp8(gpu, out, True, p_bf16=p_bf16)
+        err = float(np.max(np.abs(o.double().cpu().numpy() - ro)))
+        print(f"non-power-of-two block descales, p_bf16={p_bf16}: max|dO|={err:.3g} (max|V| {vmax:.3g})")
+        assert err <= (TOL_O if p_bf16 else 2.0 ** -4 * vmax + 1e-2)
+        assert float(np.max(np.abs(lse.double().cpu().numpy() - rl))) <= TOL_LSE
+
+
+def test_fp8_score_accumulation_precision(gpu):
+    """The fp8 path's score precision, measured through the public call: with a
+    single key, LSE = softmax_scale * (q . k) exactly, so LSE against the exact
+    float64 dot product of the codes shows how precisely the fp8 matrix core
+    sums its 128 products.  bf16 inputs (exactly the same values, the same
+    call) sum to fp32 precision; fp8 inputs to about 2^-11.4 of the largest
+    product per 64-deep instruction.  The test pins that ratio below the
+    2^-10 the fp8 LSE bound above relies on, and prints it."""
+    S = 4096
+    g = torch.Generator().manual_seed(3)
+    c = torch.randint(0, 256, (2, S, 128), generator=g, dtype=torch.int32).to(torch.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    q8 = c[0].view(1, 1, S, 128).contiguous()
+    k8 = c[1, :1].view(1, 1, 1, 128).contiguous()
+    qf, kf = oracle.e4m3_decode(q8.numpy()), oracle.e4m3_decode(k8.numpy())
+    exact = (qf[0, 0] @ kf[0, 0, 0])                         # [S]
+    pmax = np.max(np.abs(qf[0, 0] * kf[0, 0, 0]), axis=1)   # largest product per row
+    res = {}
+    for name in ("fp8", "bf16"):
+        if name == "fp8":
+            q, k = q8.cuda().view(torch.float8_e4m3fn), k8.cuda().view(torch.float8_e4m3fn)
+            o = torch.empty(1, 1, S, 128, dtype=torch.bfloat16, device="cuda")
+        else:  # the same values in bf16 (every e4m3 value is a bf16 value)
+            q = torch.from_numpy(qf).to(torch.bfloat16).cuda()
+            k = torch.from_numpy(kf).to(torch.bfloat16).cuda()
+            o = torch.empty_like(q)
+        lse = torch.empty(1, 1, S, device="cuda")
+        print(f"fa_fwd {name} single key, {S} rows", flush=True)
+        gpu.fa_fwd(q, k, k, o, lse, causal=False, softmax_scale=1.0)
+        torch.cuda.synchronize()
+        err = np.abs(lse[0, 0].double().cpu().numpy() - exact) / np.maximum(pmax, 1e-30)
+        res[name] = float(err.max())
+    print("max |LSE - q.k| / max|product|: fp8 2^%.1f, bf16 2^%.1f"
+          % (np.log2(max(res["fp8"], 1e-30)), np.log2(max(res["bf16"], 1e-30))))
+    assert res["fp8"] <= FP8_ACC_REL
+    assert res["bf16"] <= 2.0 ** -18
+
+
+@pytest.mark.timeout(900)
 def test_variants_on_the_long_context_outlier_workload(gpu):
     """The fp8 variants at the long-context workload's full shape and outlier
     distribution (Q [1, 32, 16384, 128], K/V [1, 8, 16384, 128], 164 key rows
     per kv head x 8, causal), quantised on the GPU: per-tensor scales, 64-row
-    block scales, block scales with rotation.  Sampled heads and rows: each
-    variant against the oracle fed its own codes (parity), and its error
-    against exact attention of the bf16 inputs printed for the record.
+    block scales, block scales with rotation; every element of O and LSE
+    against the oracle fed the variant's own codes.
 
-    Parity here cannot use the 8e-2 bar of the fp8 workload.  The outlier keys
-    concentrate the softmax on a few keys, and the kernel rounds P to e4m3
-    (relative error up to 2^-4 per probability in e4m3's normal range) before
-    P V, while the row sum uses the unrounded P; the weights of one output
-    element then err by up to 2^-4 of themselves, so the element by up to
-    2^-4 * max |V| (plus the far smaller absolute rounding of probabilities in
-    the subnormal range).  Measured tails reach 0.097, with every variant's
-    mean error near 0.007.  The checks are 2^-4 * max |V| + 1e-2 on the
-    maximum, 1e-2 on the mean (a wrong block scale would move many elements by
-    far more), and the 1e-3 bar on LSE, which the P rounding does not touch."""
+    With bf16 probabilities (fp8_p_bf16) every variant meets the fp8 bar,
+    8e-2.  With e4m3 probabilities it cannot be promised here: the outlier
+    keys concentrate the softmax on a few keys, and e4m3 keeps 3 mantissa
+    bits, so a probability carries up to 2^-4 of itself as rounding and one
+    output element moves by up to about 2^-4 * max |V| (plus the far smaller
+    absolute rounding of probabilities in the subnormal range).  That mode is
+    held to this documented envelope (+1e-2), a mean error of 1e-2, and the
+    1e-3 LSE bar, which the rounding of P does not touch.  The error of each
+    variant against exact attention of the bf16 inputs is printed on sampled
+    heads and rows, for the record.
+
+    LSE: the 1e-3 bar where the fp8 score accumulation allows it, else the
+    per-row bound fp8_lse_bound derives from it.  Outlier keys make scores of
+    30-50, and the fp8 matrix instructions sum products to about 2^-11.4 of
+    the largest one (test_fp8_score_accumulation_precision), so the LSE of
+    rows dominated by outlier keys moves by up to ~2e-3 (measured 1.6e-3);
+    every row is held to its bound."""
     cfg = fa_inputs.CONFIGS["bf16_gqa32x8_s16384_causal_outlier"]
     x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cuda")
     signs = fa_inputs.make_rotation_signs(128, seed=0, device="cuda")
-    heads = [(0, 0), (0, 13), (0, 31)]
+    heads = [0, 13, 31]
     rows = [0, 1, 4095, 8192, 16383]
-    sl = lambda t, h, G=1: t[0:1, h // G:h // G + 1].cpu()
-    exact = {h: oracle.attention_fp64(sl(x["q"], h), sl(x["k"], h, 4), sl(x["v"], h, 4), True, rows=rows)
-             for _, h in heads}
+    exact = oracle.attention_fp64(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), True, rows=rows,
+                                  heads=[(0, h) for h in heads])
     report = {}
     for name in ("per-tensor", "block", "block+rotation"):
-        out, deq_fn = {}, None
+        out = {}
         if name == "per-tensor":
             for n in ("q", "k", "v"):
                 c8, ts = fa_inputs.quantize_fp8_per_tensor(x[n])
                 out[n], out[n + "_ts"] = c8.view(torch.uint8), ts
-            deq_fn = lambda n, h, G=1: oracle.e4m3_decode(sl(out[n], h, G).numpy()) * out[n + "_ts"]
+            deq = {n: oracle.e4m3_decode(out[n].cpu().numpy()) * out[n + "_ts"] for n in ("q", "k", "v")}
         else:
             for n in ("q", "k", "v"):
                 t = x[n]
@@ -241,25 +345,31 @@ def test_variants_on_the_long_context_outlier_workload(gpu):
                 rot = signs if (name == "block+rotation" and n != "v") else None
                 gpu.fa_fp8_quantize(t, codes, sc, rot)
                 out[n], out[n + "_bs"] = codes, sc
-            deq_fn = lambda n, h, G=1: oracle.dequant_fp8_blocks_fp64(sl(out[n], h, G).numpy(),
-                                                                      sl(out[n + "_bs"], h, G).numpy())
-        o, lse = run_fp8(gpu, out, True, block=name != "per-tensor")
-        par = [0.0, 0.0, 0.0]  # max |O - oracle|, mean |O - oracle|, max |LSE - oracle|
-        ex = [0.0, 0.0]
-        for _, h in heads:
-            vd = deq_fn("v", h, 4)
-            ro, rl = oracle.attention_fp64(deq_fn("q", h), deq_fn("k", h, 4), vd, True, rows=rows)
-            og = o[0:1, h:h + 1, rows].double().cpu().numpy()
-            lg = lse[0:1, h:h + 1, rows].double().cpu().numpy()
-            err = float(np.max(np.abs(og - ro)))
-            assert err <= 2.0 ** -4 * float(np.max(np.abs(vd))) + 1e-2, (name, h, err)
-            par[0] = max(par[0], err)
-            par[1] = max(par[1], float(np.mean(np.abs(og - ro))))
-            par[2] = max(par[2], float(np.max(np.abs(lg - rl))))
-            eo, el = exact[h]
-            ex[0] = max(ex[0], float(np.max(np.abs(og - eo))))
-            ex[1] = max(ex[1], float(np.max(np.abs(lg - el))))
-        report[name] = {"parity": par, "vs_exact": ex}
-        del out, o, lse
-    print("long-context outliers, full shape:", report)
-    assert all(r["parity"][1] <= 1e-2 and r["parity"][2] <= TOL_LSE for r in report.values())
+            deq = {n: oracle.dequant_fp8_blocks_fp64(out[n].cpu().numpy(), out[n + "_bs"].cpu().numpy())
+                   for n in ("q", "k", "v")}
+        ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], True)
+        vmax = float(np.max(np.abs(deq["v"])))
+        lse_bar = fp8_lse_bound(deq["q"], deq["k"], True, 4, cfg.scale)
+        del deq
+        for p_bf16 in (True, False):
+            o, lse = run_fp8(gpu, out, True, block=name != "per-tensor", p_bf16=p_bf16)
+            og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+            d = np.abs(og - ro)
+            dl = np.abs(lg - rl)
+            par = (float(d.max()), float(d.mean()), float(dl.max()))
+            over = int((dl > TOL_LSE).sum())
+            ex = (float(np.max(np.abs(og[:, heads][:, :, rows] - exact[0][:, heads]))),
+                  float(np.max(np.abs(lg[:, heads][:, :, rows] - exact[1][:, heads]))))
+            mode = "p_bf16" if p_bf16 else "p_e4m3"
+            report[f"{name}/{mode}"] = {"parity_max_mean_lse": par, "vs_exact_sampled": ex}
+            print(f"{name} {mode}: every element, max|dO|={par[0]:.3g} mean|dO|={par[1]:.3g} "
+                  f"max|dLSE|={par[2]:.3g} ({over} rows above 1e-3, largest bound {lse_bar.max():.3g}); "
+                  f"vs exact (sampled) {ex[0]:.3g}, {ex[1]:.3g}", flush=True)
+            assert bool(np.all(dl <= lse_bar)), (name, mode, par)
+            if p_bf16:
+                assert par[0] <= TOL_O, (name, mode, par)
+            else:
+                assert par[0] <= 2.0 ** -4 * vmax + 1e-2 and par[1] <= 1e-2, (name, mode, par)
+            del o, lse
+        del out
+    print("long-context outliers, full shape, every element:", report)

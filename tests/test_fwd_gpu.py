@@ -187,26 +187,27 @@ def fp8_oracle_inputs(x):
             e4m3_decode(x["v"].cpu()) * x["v_scale"])
 
 
-def run_fp8(fa, x, causal):
+def run_fp8(fa, x, causal, p_bf16=False):
     q, k, v = x["q"], x["k"], x["v"]
     B, Hq, Sq, d = q.shape
     obuf, o = guarded((B, Hq, Sq, d), torch.bfloat16)
     lbuf, lse = guarded((B, Hq, Sq), torch.float32)
-    print(f"fa_fwd fp8 q={tuple(q.shape)} k={tuple(k.shape)} causal={causal}", flush=True)
+    print(f"fa_fwd fp8 q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} p_bf16={p_bf16}", flush=True)
     fa.fa_fwd(q, k, v, o, lse, causal=causal, q_descale=x["q_scale"], k_descale=x["k_scale"],
-              v_descale=x["v_scale"])
+              v_descale=x["v_scale"], p_bf16=p_bf16)
     torch.cuda.synchronize()
     assert guards_intact(obuf) and guards_intact(lbuf)
     return o, lse
 
 
+@pytest.mark.parametrize("p_bf16", [False, True], ids=["p_e4m3", "p_bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_fwd_fp8_small(gpu, causal, shape):
+def test_fwd_fp8_small(gpu, causal, shape, p_bf16):
     B, Hq, Hkv, Sq, Sk = shape
     cfg = fa_inputs.FwdConfig("t", "fp8", B, Hq, Hkv, Sq, Sk, 128, causal)
     x = {n: (t.cuda() if torch.is_tensor(t) else t) for n, t in fa_inputs.make_fwd_inputs(cfg, seed=Sq).items()}
-    o, lse = run_fp8(gpu, x, causal)
+    o, lse = run_fp8(gpu, x, causal, p_bf16)
     qf, kf, vf = fp8_oracle_inputs(x)
     ro, rl = oracle.attention_fp64(qf, kf, vf, causal)
     og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
@@ -219,17 +220,19 @@ def test_fwd_fp8_small(gpu, causal, shape):
     print("fp8 max |dO|", err)
 
 
-# ---- full-size workloads, outputs checked on sampled heads and rows ---------
+# ---- full-size workloads, every output element checked --------------------
 
-FULL = [
-    ("bf16_b4_h16_s2048_causal", [(0, 0), (1, 7), (3, 15)]),
-    ("bf16_gqa32x8_s16384_causal_outlier", [(0, 0), (0, 13), (0, 31)]),
-    ("fp8_b8_h16_s4096", [(0, 0), (5, 9), (7, 15)]),
-]
+FULL = [("bf16_b4_h16_s2048_causal", False), ("bf16_gqa32x8_s16384_causal_outlier", False),
+        ("fp8_b8_h16_s4096", False), ("fp8_b8_h16_s4096", True)]
 
 
-@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
-def test_fwd_full_size_sampled(gpu, name, heads):
+@pytest.mark.parametrize("name,p_bf16", FULL, ids=["bf16_s2048", "bf16_gqa_s16384", "fp8_p_e4m3", "fp8_p_bf16"])
+def test_fwd_full_size(gpu, name, p_bf16):
+    """The three prefill workloads at full size, in the launch configuration
+    the benchmark times, compared with the float64 oracle element by element:
+    every O and every LSE value.  The long-context workload is the only one
+    whose heads have more than 8 query blocks (one longest-first issue order
+    over 256 key tiles), so this is its only parity case."""
     cfg = fa_inputs.CONFIGS[name]
     x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cuda")
     odt = torch.float32 if cfg.dtype == "f32" else (torch.float16 if cfg.dtype == "f16" else torch.bfloat16)
@@ -238,26 +241,18 @@ def test_fwd_full_size_sampled(gpu, name, heads):
     print(f"fa_fwd full-size {name}", flush=True)
     gpu.fa_fwd(x["q"], x["k"], x["v"], o, lse, causal=cfg.causal, softmax_scale=cfg.scale,
                q_descale=x.get("q_scale", 1.0), k_descale=x.get("k_scale", 1.0),
-               v_descale=x.get("v_scale", 1.0))
+               v_descale=x.get("v_scale", 1.0), p_bf16=p_bf16)
     torch.cuda.synchronize()
     assert not bool(torch.isnan(o).any()) and not bool(torch.isnan(lse).any())
-    G = cfg.Hq // cfg.Hkv
-    rows = sorted(set([0, 1, 127, 128, cfg.Sq // 2 + 3, cfg.Sq - 129, cfg.Sq - 2, cfg.Sq - 1]))
-    tol_o = FP8_TOL_O if cfg.dtype == "fp8" else 2e-2
-    for b, h in heads:
-        sl = lambda t, hh: t[b:b + 1, hh:hh + 1].cpu()  # noqa: E731
-        if cfg.dtype == "fp8":
-            from oracle.e4m3 import e4m3_decode
-
-            qf = e4m3_decode(sl(x["q"], h)) * x["q_scale"]
-            kf = e4m3_decode(sl(x["k"], h // G)) * x["k_scale"]
-            vf = e4m3_decode(sl(x["v"], h // G)) * x["v_scale"]
-        else:
-            qf, kf, vf = sl(x["q"], h), sl(x["k"], h // G), sl(x["v"], h // G)
-        ro, rl = oracle.attention_fp64(qf, kf, vf, cfg.causal, cfg.scale, rows=rows)
-        og = o[b, h, rows].double().cpu().numpy()
-        lg = lse[b, h, rows].double().cpu().numpy()
-        err_o = float(np.max(np.abs(og - ro[0, 0])))
-        err_l = float(np.max(np.abs(lg - rl[0, 0])))
-        print(f"{name} b={b} h={h}: max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}", flush=True)
-        assert err_o <= tol_o and err_l <= 1e-3
+    if cfg.dtype == "fp8":
+        qf, kf, vf = fp8_oracle_inputs(x)
+    else:
+        qf, kf, vf = (x[n].cpu() for n in ("q", "k", "v"))
+    del x
+    ro, rl = oracle.attention_fp64(qf, kf, vf, cfg.causal, cfg.scale)
+    og = o.double().cpu().numpy()
+    lg = lse.double().cpu().numpy()
+    err_o = float(np.max(np.abs(og - ro)))
+    err_l = float(np.max(np.abs(lg - rl)))
+    print(f"{name} p_bf16={p_bf16}: every element, max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}", flush=True)
+    assert err_o <= (FP8_TOL_O if cfg.dtype == "fp8" else 2e-2) and err_l <= 1e-3

@@ -18,6 +18,16 @@
 //     that small probabilities stay normal numbers; the factor is removed with
 //     the row sum in the epilogue.  The row sum itself uses the unrounded fp32
 //     probabilities.
+//   * bf16-probability mode (PB16): e4m3 keeps 3 mantissa bits, so each
+//     probability fed to P V carries up to 2^-4 relative rounding, and a row
+//     whose softmax rests on a few keys moves by up to about 2^-4 max|V|.  In
+//     this mode P is rounded to bf16 instead, the V codes are converted
+//     exactly to bf16 on their way into LDS (every E4M3FN value is a bf16
+//     value), and P V runs on the 32x32x16 bf16 MFMA: 16 products per tile
+//     and wavefront instead of 4, with the score side unchanged.  The K tile
+//     then uses the 16-bit kernel's row order (bits 2 and 3 of the key index
+//     swapped), which puts the score accumulators in the order of the bf16
+//     P^T operand.
 //   * V is transposed in registers (4 keys x 4 columns per thread, byte
 //     permutes) on its way into a double-buffered LDS stage.
 //   * At twice the bf16 matrix rate the softmax is as long as the products, so
@@ -40,6 +50,7 @@
 #include "fa_internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace fa {
 
@@ -64,12 +75,27 @@ constexpr int LDS_BYTES = STAGES_BYTES > SLAB_BYTES ? STAGES_BYTES : SLAB_BYTES;
 constexpr float kSlack8 = 4.0f;
 constexpr float kLog2PScale = 4.f;  // kPScale = 16
 
+// bf16-probability mode: V^T rows of BC bf16 plus 16 bytes of padding (the
+// 16-bit kernel's layout, conflict-free 16-byte reads)
+constexpr int VROW16 = BC + 8;
+constexpr int V_TILE16 = D * VROW16 * 2;  // bytes
+static_assert(2 * (K_TILE + V_TILE16) <= LDS_BYTES, "bf16-P stages must fit the LDS");
+
 // LDS row of key kr of a tile: block mb = (kr >> 4) & 1, half h = kr >> 5,
 // register i = kr & 15 of that block's accumulator, whose C row is
 // 8 * (i >> 2) + 4 * h + (i & 3).
 __device__ __forceinline__ int k_lds_row(int kr) {
   const int h = kr >> 5, mb = (kr >> 4) & 1, i = kr & 15;
   return 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
+}
+
+// bf16-probability mode: bits 2 and 3 of the key index swapped, so that the
+// S^T accumulator (block mb, register i, lane half h) holds key
+// 32 mb + 16 (i >> 3) + 8 h + (i & 7), the order of the bf16 P^T operand
+__device__ __forceinline__ int k_lds_row16(int kr) { return (kr & ~12) | ((kr & 4) << 1) | ((kr & 8) >> 1); }
+
+__device__ __forceinline__ f32x16 mma16(u32x4 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c) {
@@ -89,10 +115,21 @@ struct Fp8BlockScales {
   int nbq, nbk, Hkv;
 };
 
-template <bool CAUSAL, bool BLK>
+// V operand fragments held between LDS reads and their MFMAs: two 32-byte
+// fp8 fragments, or (bf16-probability mode) four 16-byte bf16 fragments
+struct VFrag8 { u32x4 f[2][2]; };
+struct VFrag16 { u32x4 f[4]; };
+
+template <bool CAUSAL, bool BLK, bool PB16>
 __global__ __attribute__((amdgpu_flat_work_group_size(f8::NT, f8::NT), amdgpu_waves_per_eu(2)))
 void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   using namespace f8;
+  // lazy-max slack and log2 of the probability scale: e4m3 P is scaled by 16
+  // (<= 256 under a slack of 4); bf16 P needs neither
+  constexpr float kSlack = PB16 ? kRescaleSlack : kSlack8;
+  constexpr float kLog2PS = PB16 ? 0.f : kLog2PScale;
+  constexpr int VT = PB16 ? V_TILE16 : V_TILE;  // bytes per V stage
+  using VF = std::conditional_t<PB16, VFrag16, VFrag8>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   unsigned char *kbuf = lds;                 // [2][BC][KROW]
   unsigned char *vbuf = lds + 2 * K_TILE;    // [2][D][VROW]
@@ -188,7 +225,8 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     for (int p = 0; p < 4; ++p) vreg[set][p] = buf_load4(r, voff[p]);
   };
   auto store_k_from = [&](const u32x4 &src, int buf) {
-    *reinterpret_cast<u32x4 *>(kbuf + buf * K_TILE + k_lds_row(k_r) * KROW + 16 * k_c) = src;
+    const int r = PB16 ? k_lds_row16(k_r) : k_lds_row(k_r);
+    *reinterpret_cast<u32x4 *>(kbuf + buf * K_TILE + r * KROW + 16 * k_c) = src;
   };
   // 4 keys x 4 columns -> 4 columns x 4 keys
   auto store_v = [&](int set, int buf) {
@@ -197,14 +235,31 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     const unsigned x23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
     const unsigned y01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // k0c2 k1c2 k0c3 k1c3
     const unsigned y23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-    unsigned col[4];
-    col[0] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
-    col[1] = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
-    col[2] = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
-    col[3] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
-    unsigned char *vt = vbuf + buf * V_TILE;
+    if constexpr (PB16) {
+      // each word of key pairs -> two bf16 (exact); column 4 v_c + e gets keys
+      // 4 v_g .. 4 v_g + 3 as one 8-byte store
+      auto lo = [](unsigned w) {
+        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      };
+      auto hi = [](unsigned w) {
+        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+      };
+      unsigned char *vt = vbuf + buf * VT;
+      const u32x2 col[4] = {u32x2{lo(x01), lo(x23)}, u32x2{hi(x01), hi(x23)}, u32x2{lo(y01), lo(y23)},
+                            u32x2{hi(y01), hi(y23)}};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned *>(vt + (4 * v_c + e) * VROW + 4 * v_g) = col[e];
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<u32x2 *>(vt + ((4 * v_c + e) * VROW16 + 4 * v_g) * 2) = col[e];
+    } else {
+      unsigned col[4];
+      col[0] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+      col[1] = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+      col[2] = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
+      col[3] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
+      unsigned char *vt = vbuf + buf * VT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned *>(vt + (4 * v_c + e) * VROW + 4 * v_g) = col[e];
+    }
   };
 
   f32x16 oacc[4];
@@ -225,7 +280,12 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   };
   // MFMA i of O^T: head-dim block i
   auto vfrag = [&](int buf, int i, int half) {
-    return *reinterpret_cast<const u32x4 *>(v_lane + buf * V_TILE + i * 32 * VROW + 16 * half);
+    return *reinterpret_cast<const u32x4 *>(v_lane + buf * VT + i * 32 * VROW + 16 * half);
+  };
+  // bf16-probability mode, MFMA i of O^T: head-dim block i >> 2, key step i & 3
+  const unsigned char *v_lane16 = vbuf + (l32 * VROW16 + 8 * h) * 2;
+  auto vfrag16 = [&](int buf, int i) {
+    return *reinterpret_cast<const u32x4 *>(v_lane16 + buf * VT + ((i >> 2) * 32 * VROW16 + 16 * (i & 3)) * 2);
   };
 
   // ---- online softmax state ----
@@ -235,7 +295,8 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   bool move_p = false;
   float m_use = 0.f;  // running max minus log2 kPScale (minus the tile's V-descale log ratio)
 
-  // accumulator (block mb, register i, half h) is key 32h + 16mb + i
+  // accumulator (block mb, register i, half h) is key 32h + 16mb + i, or in
+  // bf16-probability mode 32mb + 16(i >> 3) + 8h + (i & 7)
   auto mask = [&](f32x16 s[2], int j) {
     const int j0 = j * BC;
     const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
@@ -244,8 +305,10 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * h + 16 * mb + i > lim) s[mb][i] = neg_inf();
+        for (int i = 0; i < 16; ++i) {
+          const int key = PB16 ? 32 * mb + 16 * (i >> 3) + 8 * h + (i & 7) : 32 * h + 16 * mb + i;
+          if (key > lim) s[mb][i] = neg_inf();
+        }
     }
   };
   // first half: tile max, lazy running-max update, exponents of s[0]
@@ -276,13 +339,13 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
       pin(mxa);
     } else if constexpr (st == 5) {
       mxa *= cscale;
-      move_p = mxa > m_run + kSlack8;
+      move_p = mxa > m_run + kSlack;
     } else if constexpr (st == 6) {
       const float m_new = move_p ? mxa : m_run;
       alpha_p = move_p ? fast_exp2(m_run - m_new) : 1.f;  // 0 when m_run = -inf
       m_run = m_new;
       // p' = kPScale * p: the scale enters the exponent as log2(kPScale)
-      m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PScale - lr_t;
+      m_use = ((m_run == neg_inf()) ? 0.f : m_run) - kLog2PS - lr_t;
       pin(alpha_p);
       pin(m_use);
     } else if constexpr (st < 15) {
@@ -298,7 +361,11 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   // second half: exponents of s[1]; P^T packed to e4m3, four keys per word;
   // row sum of the unrounded probabilities as a balanced tree; l update
   float ps[16], qa[8];
-  int pw[8];
+  int pw[16];  // P^T packed: 8 words of e4m3, or 16 of bf16 pairs
+  auto pack_bf16 = [](float x0, float x1) {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(int, v2{static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
+  };
   auto soft_b_step = [&](auto step_tag, f32x16 s[2]) {
     constexpr int st = decltype(step_tag)::value;
     if constexpr (st < 8) {
@@ -308,17 +375,26 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
       pin(p1);
       s[1][2 * st] = p0;
       s[1][2 * st + 1] = p1;
-      if constexpr (st < 4) {
+      if constexpr (PB16) {
+        pw[st] = pack_bf16(s[0][2 * st], s[0][2 * st + 1]);
+        pin(pw[st]);
+      } else if constexpr (st < 4) {
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st], s[0][4 * st + 1], 0, false);
         pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st + 2], s[0][4 * st + 3], w, true);
         pin(pw[st]);
       }
     } else {
+      if constexpr (PB16) {
+        pw[st] = pack_bf16(s[1][2 * (st - 8)], s[1][2 * (st - 8) + 1]);
+        pin(pw[st]);
+      }
       if constexpr (st < 12) {
         constexpr int q = st - 8;
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], 0, false);
-        pw[4 + q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q + 2], s[1][4 * q + 3], w, true);
-        pin(pw[4 + q]);
+        if constexpr (!PB16) {
+          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], 0, false);
+          pw[4 + q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q + 2], s[1][4 * q + 3], w, true);
+          pin(pw[4 + q]);
+        }
 #pragma unroll
         for (int i = 4 * q; i < 4 * q + 4; ++i) {
           ps[i] = s[0][i] + s[1][i];
@@ -344,8 +420,12 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     }
   };
   auto p_pack = [&](f32x16 s[2]) {
-    s[0] = __builtin_bit_cast(f32x16, i32x16{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7],
-                                             0, 0, 0, 0, 0, 0, 0, 0});
+    if constexpr (PB16)
+      s[0] = __builtin_bit_cast(f32x16, i32x16{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7], pw[8],
+                                               pw[9], pw[10], pw[11], pw[12], pw[13], pw[14], pw[15]});
+    else
+      s[0] = __builtin_bit_cast(f32x16, i32x16{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7],
+                                               0, 0, 0, 0, 0, 0, 0, 0});
   };
   auto rescale_o = [&]() {
     if (wave_any(move_p)) {
@@ -362,11 +442,16 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
       kf[i][1] = kfrag(buf, i, 1);
     }
   };
-  auto v_init = [&](int buf, u32x4 (&vf)[RA][2]) {
+  auto v_init = [&](int buf, VF &vf) {
+    if constexpr (PB16) {
 #pragma unroll
-    for (int i = 0; i < RA; ++i) {
-      vf[i][0] = vfrag(buf, i, 0);
-      vf[i][1] = vfrag(buf, i, 1);
+      for (int i = 0; i < 4; ++i) vf.f[i] = vfrag16(buf, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        vf.f[i][0] = vfrag(buf, i, 0);
+        vf.f[i][1] = vfrag(buf, i, 1);
+      }
     }
   };
   // S^T of K buffer `buf` into s, starting from the fragments kf; softmax
@@ -406,26 +491,48 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   // starting from the fragments vf; the first softmax half of `sn` rides
   // along, and the slots past the last V read fetch the first fragments kn
   // of the next S^T block (K buffer kbn)
-  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra, u32x4 (&vf)[RA][2], int kbn,
+  auto block_pv = [&](int buf, const f32x16 &p, f32x16 sn[2], auto &&extra, VF &vf, int kbn,
                       u32x4 (&kn)[RA][2]) {
-    const i32x16 pi = __builtin_bit_cast(i32x16, p);
-    const i32x8 pf = __builtin_shufflevector(pi, pi, 0, 1, 2, 3, 4, 5, 6, 7);
-    static_for<NM>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      oacc[i] = mma(join(vf[i % RA][0], vf[i % RA][1]), pf, oacc[i]);
-      if constexpr (i + RA < NM) {
-        vf[i % RA][0] = vfrag(buf, i + RA, 0);
-        vf[i % RA][1] = vfrag(buf, i + RA, 1);
-      } else {
-        kn[i + RA - NM][0] = kfrag(kbn, i + RA - NM, 0);
-        kn[i + RA - NM][1] = kfrag(kbn, i + RA - NM, 1);
-      }
-      static_for<STEPS / NM>([&](auto K) {
-        soft_a_step(std::integral_constant<int, i * (STEPS / NM) + decltype(K)::value>{}, sn);
+    if constexpr (PB16) {
+      // 16 bf16 MFMAs: head-dim block i >> 2, key step i & 3; V^T read four
+      // MFMAs ahead, the next S^T block's first K fragments in the last two slots
+      constexpr int NPV = 16;
+      const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, __builtin_shufflevector(p, p, 0, 1, 2, 3)),
+                            __builtin_bit_cast(bf16x8, __builtin_shufflevector(p, p, 4, 5, 6, 7)),
+                            __builtin_bit_cast(bf16x8, __builtin_shufflevector(p, p, 8, 9, 10, 11)),
+                            __builtin_bit_cast(bf16x8, __builtin_shufflevector(p, p, 12, 13, 14, 15))};
+      static_for<NPV>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        oacc[i >> 2] = mma16(vf.f[i % 4], pf[i & 3], oacc[i >> 2]);
+        if constexpr (i + 4 < NPV) vf.f[i % 4] = vfrag16(buf, i + 4);
+        if constexpr (i >= NPV - RA) {
+          kn[i + RA - NPV][0] = kfrag(kbn, i + RA - NPV, 0);
+          kn[i + RA - NPV][1] = kfrag(kbn, i + RA - NPV, 1);
+        }
+        soft_a_step(std::integral_constant<int, i * (STEPS / NPV)>{}, sn);
+        extra(std::integral_constant<int, i / 4>{});
+        __builtin_amdgcn_sched_barrier(0);
       });
-      extra(I);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    } else {
+      const i32x16 pi = __builtin_bit_cast(i32x16, p);
+      const i32x8 pf = __builtin_shufflevector(pi, pi, 0, 1, 2, 3, 4, 5, 6, 7);
+      static_for<NM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        oacc[i] = mma(join(vf.f[i % RA][0], vf.f[i % RA][1]), pf, oacc[i]);
+        if constexpr (i + RA < NM) {
+          vf.f[i % RA][0] = vfrag(buf, i + RA, 0);
+          vf.f[i % RA][1] = vfrag(buf, i + RA, 1);
+        } else {
+          kn[i + RA - NM][0] = kfrag(kbn, i + RA - NM, 0);
+          kn[i + RA - NM][1] = kfrag(kbn, i + RA - NM, 1);
+        }
+        static_for<STEPS / NM>([&](auto K) {
+          soft_a_step(std::integral_constant<int, i * (STEPS / NM) + decltype(K)::value>{}, sn);
+        });
+        extra(I);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
   };
 
   // Two score register sets: sc[j & 1] holds S^T of tile j from its QK^T
@@ -488,7 +595,8 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     constexpr int cur = decltype(set_tag)::value;  // t & 1
     constexpr int nxt = cur ^ 1;
     // V of tile t and K of tile t+2 both sit in buffer cur
-    u32x4 vf[RA][2], kf[RA][2];
+    VF vf;
+    u32x4 kf[RA][2];
     v_init(cur, vf);  // first, so the reads overlap the rescale and mask
     tile_consts(skr[cur], svr[cur]);  // of tile t+1, loaded with unit t-1 (or in the prologue)
     rescale_o();
@@ -557,15 +665,17 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     }
   }
   if (row < a.Sq && a.lse != nullptr && h == 0)
-    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PScale) * kLn2 : neg_inf();
+    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PS) * kLn2 : neg_inf();
 }
 
-template <bool CAUSAL, bool BLK> int launch_fp8(const FwdArgs &args, const Fp8BlockScales &bs, hipStream_t stream) {
+template <bool CAUSAL, bool BLK, bool PB16>
+int launch_fp8(const FwdArgs &args, const Fp8BlockScales &bs, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
   fa_log_launch("fwd_fp8_kernel", grid, f8::NT, f8::LDS_BYTES,
-                "causal=%d block_descales=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d", CAUSAL ? 1 : 0,
-                BLK ? 1 : 0, args.B, args.Hq, args.G, args.Sq, args.Sk, f8::BR);
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, BLK>), dim3(grid), dim3(f8::NT), 0, stream, args, bs);
+                "p=%s causal=%d block_descales=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d",
+                PB16 ? "bf16" : "e4m3", CAUSAL ? 1 : 0, BLK ? 1 : 0, args.B, args.Hq, args.G, args.Sq, args.Sk,
+                f8::BR);
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, BLK, PB16>), dim3(grid), dim3(f8::NT), 0, stream, args, bs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "fp8 launch: %s", hipGetErrorString(e));
   return FA_OK;
@@ -584,8 +694,12 @@ int fa_launch_fwd_fp8(const fa_fwd_params *p, void *stream) {
     args.o_mul = 1.f;
     const Fp8BlockScales bs{p->q_block_descale, p->k_block_descale, p->v_block_descale,
                             (p->Sq + f8::BC - 1) / f8::BC, (p->Sk + f8::BC - 1) / f8::BC, p->Hkv};
-    return p->causal ? launch_fp8<true, true>(args, bs, s) : launch_fp8<false, true>(args, bs, s);
+    if (p->fp8_p_bf16)
+      return p->causal ? launch_fp8<true, true, true>(args, bs, s) : launch_fp8<false, true, true>(args, bs, s);
+    return p->causal ? launch_fp8<true, true, false>(args, bs, s) : launch_fp8<false, true, false>(args, bs, s);
   }
   const Fp8BlockScales none{};
-  return p->causal ? launch_fp8<true, false>(args, none, s) : launch_fp8<false, false>(args, none, s);
+  if (p->fp8_p_bf16)
+    return p->causal ? launch_fp8<true, false, true>(args, none, s) : launch_fp8<false, false, true>(args, none, s);
+  return p->causal ? launch_fp8<true, false, false>(args, none, s) : launch_fp8<false, false, false>(args, none, s);
 }
