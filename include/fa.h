@@ -280,6 +280,25 @@ size_t fa_decode_workspace_size(int32_t B, int32_t Hq, int32_t d, int32_t num_sp
 int fa_decode_kvq(const fa_decode_params *p, fa_stream_t stream);
 
 /*
+ * fa_decode_kvq for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the split partials kept in a
+ * fixed array of FA_DECODE_NOALLOC_MAX_BYTES in the library's own device
+ * memory (one per GPU, held until the process ends) instead of a workspace.
+ * p->workspace and p->workspace_bytes are ignored.  Sizes whose partials
+ * need more than FA_DECODE_NOALLOC_MAX_BYTES (fa_decode_workspace_size(B,
+ * Hq, d, num_splits + (W > 0)) bytes) return FA_ERR_WORKSPACE before
+ * anything runs.  The call uses the array of the current device, so call it
+ * with the stream's device current.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * on it; calls ordered on one stream do not.  Nothing in the array needs to
+ * be cleared: each call writes every partial it reads.  The array's address
+ * is looked up on the first call on each device.  No memory is allocated.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES (32 * 1024 * 1024)
+int fa_decode_kvq_noalloc(const fa_decode_params *p, fa_stream_t stream);
+
+/*
  * Quantise-on-append: the write side of the cache (KV-cache quantisation
  * overview, section 3, "before writing the cache": K/V go from FP16/BF16 to a
  * low-bit form that needs a scale).

@@ -525,3 +525,14 @@ def test_binding_bwd_append_quant_reject_mismatches():
             fa.fp8_quant_params(**x)
     with pytest.raises(ValueError, match="not on a GPU"):
         fa.fp8_quant_params(**qp)
+
+
+def test_decode_noalloc_refuses_before_any_hip_call(lib):
+    # partials of 64 splits x 64 x 32 heads exceed the fixed scratch: the size
+    # is checked on the host before the scratch is looked up or anything runs
+    p = good_decode()
+    p.B, p.Hq, p.Hkv, p.num_splits = 64, 32, 8, 64
+    p.workspace, p.workspace_bytes = 0, 0
+    assert fa.fa_decode_workspace_size(64, 32, 128, 64) > fa.FA_DECODE_NOALLOC_MAX_BYTES
+    assert lib.fa_decode_kvq_noalloc(ctypes.byref(p), None) == fa.FA_ERR_WORKSPACE
+    assert "scratch" in fa.fa_last_error()

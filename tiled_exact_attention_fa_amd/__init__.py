@@ -9,6 +9,7 @@ been built, load() raises.
 
     fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None, ...)
     fa_decode_kvq(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, ...)
+    fa_decode_kvq_noalloc(...)  (no workspace: the library's fixed per-GPU scratch)
     fa_decode_workspace_size(B, Hq, d, num_splits)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=False, ...)
     fa_bwd_workspace_size(B, Hq, Sq)
@@ -121,7 +122,10 @@ class FaKvAppendParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_kvq", "fa_decode_workspace_size",
+FA_DECODE_NOALLOC_MAX_BYTES = 32 * 1024 * 1024
+
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_kvq", "fa_decode_kvq_noalloc",
+           "fa_decode_workspace_size",
            "fa_kv_append", "fa_fp8_quantize", "fa_check_fwd_params", "fa_check_bwd_params",
            "fa_check_decode_params", "fa_check_kv_append_params", "fa_check_fp8_quant_params",
            "fa_status_string", "fa_last_error"]
@@ -149,6 +153,8 @@ def load(path: str | None = None):
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_decode_kvq.argtypes = [ctypes.POINTER(FaDecodeParams), ctypes.c_void_p]
     lib.fa_decode_kvq.restype = ctypes.c_int
+    lib.fa_decode_kvq_noalloc.argtypes = [ctypes.POINTER(FaDecodeParams), ctypes.c_void_p]
+    lib.fa_decode_kvq_noalloc.restype = ctypes.c_int
     lib.fa_decode_workspace_size.argtypes = [ctypes.c_int32] * 4
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_check_fwd_params.argtypes = [ctypes.POINTER(FaFwdParams)]
@@ -595,3 +601,16 @@ def fa_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions=Non
     st = load().fa_kv_append(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_kv_append", fa_last_error())
+
+
+def fa_decode_kvq_noalloc(q, k_cache, v_cache, k_scale, v_scale, o, lse=None, seq_lens=None,
+                          num_splits=16, softmax_scale=None, stream=None, kv_format=None,
+                          k_recent=None, v_recent=None, recent_lens=None) -> None:
+    """fa_decode_kvq without a workspace: the split partials go to the
+    library's fixed per-GPU scratch (FA_DECODE_NOALLOC_MAX_BYTES), so nothing
+    is allocated; concurrent calls on one GPU race on it."""
+    p = decode_params(q, k_cache, v_cache, k_scale, v_scale, o, lse, seq_lens, num_splits,
+                      softmax_scale, None, kv_format, k_recent, v_recent, recent_lens)
+    st = load().fa_decode_kvq_noalloc(ctypes.byref(p), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_kvq_noalloc", fa_last_error())

@@ -159,7 +159,8 @@ extern "C" size_t fa_decode_workspace_size(int32_t B, int32_t Hq, int32_t d, int
   return ((o_bytes + 255) & ~size_t(255)) + ((l_bytes + 255) & ~size_t(255));
 }
 
-extern "C" int fa_check_decode_params(const fa_decode_params *p) {
+// Everything fa_check_decode_params checks except the workspace.
+int fa_check_decode_inputs(const fa_decode_params *p) {
   fa_clear_error();
   if (p == nullptr) return fa_set_error(FA_ERR_INVALID_ARG, "params is NULL");
   if (p->kv_format != FA_KV_INT8_TOKHEAD_F16SCALE && p->kv_format != FA_KV_FP8_E4M3_TOKHEAD_F16SCALE)
@@ -203,6 +204,12 @@ extern "C" int fa_check_decode_params(const fa_decode_params *p) {
     if ((st = check_tensor("k_recent", p->k_recent, p->recent_strides, 3, p->W, p->d, 2)) != FA_OK) return st;
     if ((st = check_tensor("v_recent", p->v_recent, p->recent_strides, 3, p->W, p->d, 2)) != FA_OK) return st;
   }
+  return FA_OK;
+}
+
+extern "C" int fa_check_decode_params(const fa_decode_params *p) {
+  const int st = fa_check_decode_inputs(p);
+  if (st != FA_OK || p->B == 0) return st;
   // the window's partial takes one more slot of the workspace
   const size_t need = fa_decode_workspace_size(p->B, p->Hq, p->d, p->num_splits + (p->W > 0 ? 1 : 0));
   if (p->workspace == nullptr || p->workspace_bytes < need)

@@ -52,6 +52,36 @@
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
+#include <mutex>
+
+// Partial results of fa_decode_kvq_noalloc: a file-scope device array, so that
+// entry point allocates nothing.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code this name is only a stand-in:
+// kernels get the device address from fa_decode_scratch(), never the name.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[FA_DECODE_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};  // device address of `scratch`, per device
+}  // namespace
+
+int fa_decode_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fa_set_error(FA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch[dev] = addr;
+  }
+  *ptr = g_scratch[dev];
+  return FA_OK;
+}
+
 namespace fa {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));

@@ -18,6 +18,13 @@ bool fa_log_enabled();
 void fa_log_launch(const char *kernel, unsigned grid, unsigned block, unsigned lds_bytes, const char *fmt, ...)
     __attribute__((format(printf, 5, 6)));
 
+// Everything fa_check_decode_params checks except the workspace.
+int fa_check_decode_inputs(const fa_decode_params *p);
+
+// Device address of fa_decode_kvq_noalloc's scratch array on the current
+// device (FA_DECODE_NOALLOC_MAX_BYTES bytes), looked up once per device.
+int fa_decode_scratch(void **ptr);
+
 // Kernel launchers, one per kernel family (defined in the .hip files).  They
 // assume validated parameters and return FA_OK or FA_ERR_HIP.
 int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream);
