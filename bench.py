@@ -143,7 +143,8 @@ def launches_per_call(cfg) -> int:
 
 
 def workload(name):
-    for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS):
+    for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS,
+                  fa_inputs.SOFT_EXP2_CONFIGS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -295,7 +296,7 @@ def _decode_oracle_check(cfg, x, o, lse, budget_s):
     return cpu, err
 
 
-def _fwd_runner(cfg, seed=0, p_bf16=False):
+def _fwd_runner(cfg, seed=0, p_bf16=False, soft_exp2=False):
     import torch
 
     import tiled_exact_attention_fa_amd as fa
@@ -309,7 +310,7 @@ def _fwd_runner(cfg, seed=0, p_bf16=False):
 
     def run():
         fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale,
-                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], p_bf16=p_bf16)
+                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], p_bf16=p_bf16, soft_exp2=soft_exp2)
 
     return Runner(run, lambda budget: _fwd_oracle_check(cfg, x, o, lse, budget))
 
@@ -481,7 +482,8 @@ def measure(name, steps, warmup, check_budget=0.0):
     elif isinstance(cfg, fa_inputs.Fp8BlockConfig):
         r = _fp8_block_runner(cfg)
     else:
-        r = _fwd_runner(cfg, p_bf16=isinstance(cfg, fa_inputs.Fp8PBf16Config))
+        r = _fwd_runner(cfg, p_bf16=isinstance(cfg, fa_inputs.Fp8PBf16Config),
+                        soft_exp2=isinstance(cfg, fa_inputs.SoftExp2Config))
     ms, wall = _time_region(r.run, steps, warmup)
     each = _time_each(r.run, steps)
     med, mn = each[len(each) // 2], each[0]
@@ -611,7 +613,7 @@ def main():
 
     extras = {}
     names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.BWD_CONFIGS) + list(fa_inputs.KV_CONFIGS)
-             + list(fa_inputs.FP8_VARIANT_CONFIGS) if n != a.workload]
+             + list(fa_inputs.FP8_VARIANT_CONFIGS) + list(fa_inputs.SOFT_EXP2_CONFIGS) if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":

@@ -159,6 +159,18 @@ class Fp8PBf16Config(FwdConfig):
     P V (fa_fwd_params.fp8_p_bf16 = 1); same inputs as FwdConfig."""
 
 
+@dataclass(frozen=True)
+class SoftExp2Config(FwdConfig):
+    """A bf16/fp16 prefill workload run with a quarter of the exponentials in
+    software (fa_fwd_params.soft_exp2 = 1); same inputs as FwdConfig."""
+
+
+# The long-context workload with the software-exponential split.
+SOFT_EXP2_CONFIGS = {
+    "softexp2_bf16_gqa32x8_s16384_causal_outlier": SoftExp2Config(
+        "softexp2_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
+}
+
 # The fp8 accuracy variants at the fp8 workload's shape: the forward on
 # block-scaled codes, the quantiser that makes them, and the per-tensor fp8
 # workload with bf16 probabilities.

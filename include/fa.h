@@ -141,6 +141,14 @@ typedef struct {
    * 2^-6 also lose relative precision in e4m3's subnormal range. */
   const float *q_block_descale, *k_block_descale, *v_block_descale;
   int32_t fp8_p_bf16; /* FP8 only: 0 = P in e4m3, 1 = P in bf16 (see above) */
+  /* BF16/F16 with d = 128 only, 0 or 1: 1 computes a quarter of the
+   * probabilities' exponentials with a polynomial on the FMA pipe instead of
+   * the hardware exp2 (the FlashAttention interview canvas, v4 card: software
+   * exponentials beside the exponential unit).  Relative error of those
+   * exponentials 2^-18.5 (the hardware's is about 2^-22); both are far below
+   * the bf16/fp16 rounding of P.  On gfx950 the transcendental instruction
+   * shares the vector issue with the FMAs, so this is slower, not faster. */
+  int32_t soft_exp2;
 } fa_fwd_params;
 
 int fa_fwd(const fa_fwd_params *p, fa_stream_t stream);

@@ -536,3 +536,17 @@ def test_decode_noalloc_refuses_before_any_hip_call(lib):
     assert fa.fa_decode_workspace_size(64, 32, 128, 64) > fa.FA_DECODE_NOALLOC_MAX_BYTES
     assert lib.fa_decode_kvq_noalloc(ctypes.byref(p), None) == fa.FA_ERR_WORKSPACE
     assert "scratch" in fa.fa_last_error()
+
+
+def test_fwd_soft_exp2_validation(lib):
+    p = good_fwd()
+    p.soft_exp2 = 1
+    assert fa.fa_check_fwd_params(p) == fa.FA_OK
+    p.soft_exp2 = 3
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_INVALID_ARG
+    p.soft_exp2 = 1
+    p.d = 64
+    for n in ("q_strides", "k_strides", "v_strides", "o_strides"):
+        setattr(p, n, fa.I64x3(8 * 100 * 64, 100 * 64, 64))
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_UNSUPPORTED
+

@@ -256,3 +256,43 @@ def test_fwd_full_size(gpu, name, p_bf16):
     err_l = float(np.max(np.abs(lg - rl)))
     print(f"{name} p_bf16={p_bf16}: every element, max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}", flush=True)
     assert err_o <= (FP8_TOL_O if cfg.dtype == "fp8" else 2e-2) and err_l <= 1e-3
+
+
+# ---- software exponentials (a quarter of them on the FMA pipe) --------------
+
+SOFT_SHAPES = [(1, 2, 2, 64, 64), (1, 8, 2, 300, 300), (2, 2, 2, 100, 260), (1, 2, 2, 260, 100)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SOFT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_soft_exp2(gpu, dt, causal, shape):
+    """soft_exp2 = 1: same bars as the hardware exponentials, including rows
+    that see no key (Sq > Sk, causal), whose probabilities must stay 0."""
+    B, Hq, Hkv, Sq, Sk = shape
+    q, k, v = make(B, Hq, Hkv, Sq, Sk, 128, dt, seed=Sq + 5)
+    obuf, o = guarded((B, Hq, Sq, 128), TDT[dt])
+    lbuf, lse = guarded((B, Hq, Sq), torch.float32)
+    print(f"fa_fwd soft_exp2 q={tuple(q.shape)} k={tuple(k.shape)} {dt} causal={causal}", flush=True)
+    gpu.fa_fwd(q, k, v, o, lse, causal=causal, soft_exp2=True)
+    torch.cuda.synchronize()
+    assert guards_intact(obuf) and guards_intact(lbuf)
+    check(o, lse, q, k, v, causal, dt)
+
+
+def test_fwd_soft_exp2_full_size(gpu):
+    """The long-context workload with soft_exp2 = 1, every element."""
+    cfg = fa_inputs.CONFIGS["bf16_gqa32x8_s16384_causal_outlier"]
+    x = fa_inputs.make_fwd_inputs(cfg, seed=0, device="cuda")
+    o = torch.full((cfg.B, cfg.Hq, cfg.Sq, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((cfg.B, cfg.Hq, cfg.Sq), float("nan"), device="cuda")
+    print("fa_fwd full-size soft_exp2", flush=True)
+    gpu.fa_fwd(x["q"], x["k"], x["v"], o, lse, causal=True, soft_exp2=True)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(o).any()) and not bool(torch.isnan(lse).any())
+    ro, rl = oracle.attention_fp64(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), True)
+    err_o = float(np.max(np.abs(o.double().cpu().numpy() - ro)))
+    err_l = float(np.max(np.abs(lse.double().cpu().numpy() - rl)))
+    print(f"soft_exp2 long-context, every element: max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}", flush=True)
+    assert err_o <= 2e-2 and err_l <= 1e-3
+

@@ -55,7 +55,7 @@ class FaFwdParams(ctypes.Structure):
         ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
         ("q_block_descale", ctypes.c_void_p), ("k_block_descale", ctypes.c_void_p),
         ("v_block_descale", ctypes.c_void_p),
-        ("fp8_p_bf16", ctypes.c_int32),
+        ("fp8_p_bf16", ctypes.c_int32), ("soft_exp2", ctypes.c_int32),
     ]
 
 
@@ -300,11 +300,12 @@ def _same_gpu(**tensors):
 
 def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
                q_descale=1.0, k_descale=1.0, v_descale=1.0, block_descales=None,
-               p_bf16=False) -> FaFwdParams:
+               p_bf16=False, soft_exp2=False) -> FaFwdParams:
     """fa_fwd_params for BHSD-indexed tensors q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d]
     (q's dtype), o [B,Hq,Sq,d] (q's dtype, bf16 for fp8 inputs), lse [B,Hq,Sq]
     float32 (any strides with a unit last stride), all on one GPU.  p_bf16
-    sets fp8_p_bf16 (fp8 inputs only)."""
+    sets fp8_p_bf16 (fp8 inputs only), soft_exp2 the software-exponential
+    split (bf16/fp16, d = 128)."""
     import torch
 
     _dims("q", q, 4)
@@ -347,18 +348,19 @@ def fwd_params(q, k, v, o, lse=None, causal=False, softmax_scale=None,
     if block_descales is not None:  # (q, k, v) float32 tensors [B, H, ceil(S / 64)], contiguous
         p.q_block_descale, p.k_block_descale, p.v_block_descale = (_ptr(t) for t in block_descales)
     p.fp8_p_bf16 = 1 if p_bf16 else 0
+    p.soft_exp2 = 1 if soft_exp2 else 0
     return p
 
 
 def fa_fwd(q, k, v, o, lse=None, causal=False, softmax_scale=None,
            q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None, block_descales=None,
-           p_bf16=False) -> None:
+           p_bf16=False, soft_exp2=False) -> None:
     """Enqueue the prefill forward on torch's current stream (or ``stream``).
     ``block_descales``: optional (q, k, v) per-64-row descales for fp8 inputs;
     ``p_bf16``: fp8 inputs only, probabilities rounded to bf16 for P V instead
     of e4m3."""
     p = fwd_params(q, k, v, o, lse, causal, softmax_scale, q_descale, k_descale, v_descale, block_descales,
-                   p_bf16)
+                   p_bf16, soft_exp2)
     st = load().fa_fwd(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd", fa_last_error())

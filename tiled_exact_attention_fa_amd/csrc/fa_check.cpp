@@ -116,6 +116,10 @@ extern "C" int fa_check_fwd_params(const fa_fwd_params *p) {
     return fa_set_error(FA_ERR_INVALID_ARG, "fp8_p_bf16 must be 0 or 1");
   if (p->fp8_p_bf16 != 0 && in != FA_FP8_E4M3)
     return fa_set_error(FA_ERR_INVALID_ARG, "fp8_p_bf16 applies to fp8 inputs only");
+  if (p->soft_exp2 != 0 && p->soft_exp2 != 1)
+    return fa_set_error(FA_ERR_INVALID_ARG, "soft_exp2 must be 0 or 1");
+  if (p->soft_exp2 != 0 && !((in == FA_BF16 || in == FA_F16) && p->d == 128))
+    return fa_set_error(FA_ERR_UNSUPPORTED, "soft_exp2 is built for bf16/fp16 inputs with d = 128");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
     return fa_set_error(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   const int nblk = (p->q_block_descale != nullptr) + (p->k_block_descale != nullptr) + (p->v_block_descale != nullptr);

@@ -70,6 +70,30 @@ __device__ __forceinline__ float swap_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the FMA pipe instead of the transcendental unit (the FlashAttention
+// interview canvas's v4 card moves part of the exponentials there).  Range
+// reduction in the manner of Cody and Waite: x = n + f with n = rint(x) taken
+// by the 1.5 * 2^23 rounding constant and f in [-1/2, 1/2]; 2^f by a degree-4
+// polynomial whose coefficients were fitted here to the relative error of
+// 2^f at Chebyshev nodes (maximum 2^-18.5 when evaluated in float32); n is
+// added to the exponent field.  Valid for x <= 8 (the softmax's arguments stay
+// below the lazy-max slack); arguments at or below -125 (masked scores are
+// -inf) give exactly 0.
+__device__ __forceinline__ float soft_exp2(float x) {
+  constexpr float kRound = 0x1.8p23f;
+  const float xc = fmaxf(x, -125.f);
+  const float t = xc + kRound;  // 1.5 * 2^23 + rint(xc): rint(xc) in the low bits
+  const float n = t - kRound;
+  const float f = xc - n;
+  float p = __builtin_fmaf(0x1.3997cap-7f, f, 0x1.ca1440p-5f);
+  p = __builtin_fmaf(p, f, 0x1.ec06dap-3f);
+  p = __builtin_fmaf(p, f, 0x1.62e0dcp-1f);
+  p = __builtin_fmaf(p, f, 0x1.ffffe8p-1f);
+  // (bits(t) << 23) = n << 23 modulo 2^32, since 1.5 * 2^23 has no bits below 2^9
+  const unsigned bits = __builtin_bit_cast(unsigned, p) + (__builtin_bit_cast(unsigned, t) << 23);
+  return x > -125.f ? __builtin_bit_cast(float, bits) : 0.f;
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).  Used after

@@ -402,7 +402,11 @@ void fwd_mfma_kernel(const FwdArgs a) {
 #endif
 
 
-template <typename T, int D, bool CAUSAL, int NT>
+// SEXP: a quarter of the exponentials (the second of every other pair) by
+// soft_exp2 on the FMA pipe, the FlashAttention-4 card's split between the
+// exponential unit and the FMA units; off by default (on this part the
+// transcendental shares the vector issue with the FMAs).
+template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
 void fwd_mfma16_kernel(const FwdArgs a) {
   using C = Cfg16<T, D, NT>;
@@ -576,7 +580,8 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     } else if constexpr (st < 15) {
       constexpr int e = 2 * (st - 7);
       float p0 = fast_exp2(__builtin_fmaf(s[0][e], cscale, -m_use));
-      float p1 = fast_exp2(__builtin_fmaf(s[0][e + 1], cscale, -m_use));
+      const float x1 = __builtin_fmaf(s[0][e + 1], cscale, -m_use);
+      float p1 = (SEXP && (st & 1)) ? soft_exp2(x1) : fast_exp2(x1);
       pin(p0);
       pin(p1);
       s[0][e] = p0;
@@ -605,7 +610,8 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     constexpr int st = decltype(step_tag)::value;
     if constexpr (st < 8) {
       float p0 = fast_exp2(__builtin_fmaf(s[1][2 * st], cscale, -m_use));
-      float p1 = fast_exp2(__builtin_fmaf(s[1][2 * st + 1], cscale, -m_use));
+      const float x1 = __builtin_fmaf(s[1][2 * st + 1], cscale, -m_use);
+      float p1 = (SEXP && (st & 1)) ? soft_exp2(x1) : fast_exp2(x1);
       pin(p0);
       pin(p1);
       s[1][2 * st] = p0;
@@ -856,12 +862,12 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
 }
 
-template <typename T, int D, bool CAUSAL, int NT>
+template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false>
 int launch_one(const FwdArgs &args, hipStream_t stream) {
   void (*kern)(FwdArgs);
   int lds_bytes;
   if constexpr (sizeof(T) == 2) {
-    kern = fwd_mfma16_kernel<T, D, CAUSAL, NT>;
+    kern = fwd_mfma16_kernel<T, D, CAUSAL, NT, SEXP>;
     lds_bytes = Cfg16<T, D, NT>::LDS_BYTES;
   } else {
     kern = fwd_mfma_kernel<T, D, CAUSAL>;
@@ -869,9 +875,9 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
   }
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
   fa_log_launch(sizeof(T) == 2 ? "fwd_mfma16_kernel" : "fwd_mfma_kernel", grid, NT, lds_bytes,
-                "dtype=%s d=%d causal=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d",
+                "dtype=%s d=%d causal=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d soft_exp2=%d",
                 sizeof(T) == 4 ? "f32" : (std::is_same<T, __bf16>::value ? "bf16" : "f16"), D, CAUSAL ? 1 : 0,
-                args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR);
+                args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR, SEXP ? 1 : 0);
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -890,7 +896,9 @@ template <typename T, int D, int NT> int launch_causal(const FwdArgs &args, bool
   return causal ? launch_one<T, D, true, NT>(args, s) : launch_one<T, D, false, NT>(args, s);
 }
 
-template <typename T, int NT> int launch_dtype(const FwdArgs &args, int d, bool causal, hipStream_t s) {
+template <typename T, int NT> int launch_dtype(const FwdArgs &args, int d, bool causal, bool sexp, hipStream_t s) {
+  if (sexp)  // validated: 16-bit inputs with d = 128
+    return causal ? launch_one<T, 128, true, NT, true>(args, s) : launch_one<T, 128, false, NT, true>(args, s);
   return d == 64 ? launch_causal<T, 64, NT>(args, causal, s) : launch_causal<T, 128, NT>(args, causal, s);
 }
 
@@ -900,12 +908,12 @@ int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream) {
   using namespace fa;
   const int es = fa_dtype_size(p->in_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (es == 4) return launch_dtype<float, 256>(make_fwd_args(p, 128, es), p->d, p->causal != 0, s);
+  if (es == 4) return launch_dtype<float, 256>(make_fwd_args(p, 128, es), p->d, p->causal != 0, false, s);
   constexpr int NT = 512;
   const FwdArgs args = make_fwd_args(p, NT / 2, es);  // 32 query rows per wavefront
   switch (p->in_dtype) {
-    case FA_BF16: return launch_dtype<__bf16, NT>(args, p->d, p->causal != 0, s);
-    case FA_F16: return launch_dtype<_Float16, NT>(args, p->d, p->causal != 0, s);
+    case FA_BF16: return launch_dtype<__bf16, NT>(args, p->d, p->causal != 0, p->soft_exp2 != 0, s);
+    case FA_F16: return launch_dtype<_Float16, NT>(args, p->d, p->causal != 0, p->soft_exp2 != 0, s);
     default: return fa_set_error(FA_ERR_UNSUPPORTED, "dtype %d has no MFMA forward kernel", p->in_dtype);
   }
 }
