@@ -568,6 +568,124 @@ def summarize_pmc(a):
           f"{fetch / 1e6:.1f} | {write / 1e6:.1f} | {algo / 1e6:.1f} | {(fetch + write) / algo:.3f} |")
 
 
+# ---- kernel trace against the bench's own per-call times ---------------------
+
+def _kernel_label(name: str) -> str:
+    """Readable kernel name: the trace gives the demangled form, or the
+    mangled one when the demangler does not know a template argument
+    (bf16: DF16b); template arguments are spelled out either way."""
+    import re
+
+    if name.startswith("_ZN2fa"):
+        m = re.match(r"_ZN2fa\d+(\w+?)I(.*)EEvN", name)
+        if not m:
+            return name
+        args = re.findall(r"DF16b|DF16_|Li(-?\d+)E|Lb(\d)E", m.group(2))
+        toks = re.finditer(r"DF16b|DF16_|Li(-?\d+)E|Lb(\d)E", m.group(2))
+        out = []
+        for t in toks:
+            g = t.group(0)
+            out.append("bf16" if g == "DF16b" else "f16" if g == "DF16_" else (t.group(1) or t.group(2)))
+        del args
+        return f"{m.group(1)}<{', '.join(out)}>"
+    return name.replace("void ", "").split("(")[0].replace("fa::", "")
+
+
+def summarize_trace(trace_csv: str, bench_json: str):
+    """Markdown table of a rocprofv3 --kernel-trace run of this script: the
+    library's dispatches come in one contiguous block per workload (other
+    kernels, the input generators', separate them; setup blocks of fewer than
+    five dispatches, like the quantiser run before the block-scaled prefill,
+    are skipped), taken in the order the script ran the workloads; for each
+    kernel of a block its dispatch count and duration, and the bench's own
+    mean and median time per call from the same run."""
+    import csv
+    import statistics
+
+    with open(bench_json) as f:
+        line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
+    out = json.loads(line)
+    order = [out["config"]["workload"]] + list(out["workloads"])
+    per_call = {out["config"]["workload"]: (out["ms_per_step"], out.get("ms_median"))}
+    for n, w in out["workloads"].items():
+        per_call[n] = (w.get("ms_per_call"), w.get("ms_median"))
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                         int(r["Grid_Size_X"])))
+    rows.sort()
+    blocks, cur = [], []
+    for t0, t1, name, grid in rows:
+        if "fa::" in name or name.startswith("_ZN2fa"):
+            cur.append((_kernel_label(name), grid, t1 - t0))
+        elif cur:
+            blocks.append(cur)
+            cur = []
+    if cur:
+        blocks.append(cur)
+    blocks = [b for b in blocks if len(b) >= 5]
+    print("| workload | kernel | grid threads | dispatches | avg us | median us | min us | bench ms/call (mean, median) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for wl, b in zip(order, blocks):
+        kinds = {}
+        for short, grid, ns in b:
+            kinds.setdefault((short, grid), []).append(ns)
+        for (short, grid), ns in kinds.items():
+            ms = per_call.get(wl, (None, None))
+            bt = f"{ms[0]:.4f}, {ms[1]:.4f}" if ms[0] is not None else "-"
+            print(f"| {wl} | {short} | {grid} | {len(ns)} | {statistics.mean(ns) / 1e3:.1f} | "
+                  f"{statistics.median(ns) / 1e3:.1f} | {min(ns) / 1e3:.1f} | {bt} |")
+
+
+# ---- instruction counters ----------------------------------------------------
+
+def summarize_counters(dirs: str, kernel: str, workload_name: str):
+    """One markdown row of rocprofv3 --pmc runs (comma-separated output
+    directories) of one workload: each counter's mean per dispatch of the
+    kernels whose name contains `kernel`, and the figures derived from them
+    when present.  Kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8
+    XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x kernel cycles);
+    co-exec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; per-MFMA
+    counts divide by SQ_INSTS_MFMA (VALU excluding the MFMAs themselves)."""
+    means, n_disp = {}, 0
+    for d in dirs.split(","):
+        import glob
+
+        counters = set()
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            import csv
+
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    counters.add(r["Counter_Name"])
+        for c in sorted(counters):
+            try:
+                means[c], n = _pmc_per_dispatch(d, c, kernel)
+                n_disp = max(n_disp, n)
+            except SystemExit:
+                pass
+    cyc = means.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    mf = means.get("SQ_INSTS_MFMA", 0.0)
+    parts = [workload_name, str(n_disp), f"{cyc:.3g}" if cyc else "-"]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in means and cyc:
+        parts.append(f"{100 * means['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cyc):.1f} %")
+    else:
+        parts.append("-")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in means and means.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        parts.append(f"{100 * means['SQ_VALU_MFMA_COEXEC_CYCLES'] / means['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} %")
+    else:
+        parts.append("-")
+    for key, sub in (("SQ_INSTS_VALU", mf), ("SQ_INSTS_VALU_TRANS_F32", 0.0), ("SQ_INSTS_LDS", 0.0)):
+        parts.append(f"{(means[key] - sub) / mf:.2f}" if key in means and mf else "-")
+    if "SQ_LDS_BANK_CONFLICT" in means and means.get("SQ_LDS_IDX_ACTIVE"):
+        parts.append(f"{100 * means['SQ_LDS_BANK_CONFLICT'] / means['SQ_LDS_IDX_ACTIVE']:.2f} %")
+    else:
+        parts.append("-")
+    print("| " + " | ".join(parts) + " |")
+    print("raw means per dispatch: " + ", ".join(f"{k}={v:.4g}" for k, v in sorted(means.items())))
+
+
 # ---- main ---------------------------------------------------------------------
 
 def main():
@@ -589,7 +707,18 @@ def main():
     ap.add_argument("--calib-bytes", type=int, default=1 << 30)
     ap.add_argument("--calib-kernel", default="MulFunctor")
     ap.add_argument("--kernel", default="fwd_mfma16_kernel")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="summarise a rocprofv3 kernel trace of this script against --bench-json")
+    ap.add_argument("--bench-json")
+    ap.add_argument("--summarize-counters", metavar="DIRS",
+                    help="summarise rocprofv3 --pmc runs (comma-separated dirs) of --workload for --kernel")
     a = ap.parse_args()
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters, a.kernel, a.workload)
+        return
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace, a.bench_json)
+        return
     if a.summarize_pmc:
         summarize_pmc(a)
         return
