@@ -465,25 +465,38 @@ def stored_traffic(name: str):
     return ent.get("bytes_per_launch")
 
 
+def _runner(cfg):
+    """The Runner of any workload configuration."""
+    if isinstance(cfg, fa_inputs.DecodeConfig):
+        return _decode_runner(cfg)
+    if isinstance(cfg, fa_inputs.AppendConfig):
+        return _append_runner(cfg)
+    if isinstance(cfg, fa_inputs.QuantConfig):
+        return _quant_runner(cfg)
+    if isinstance(cfg, fa_inputs.BwdConfig):
+        return _bwd_runner(cfg)
+    if isinstance(cfg, fa_inputs.Fp8BlockConfig):
+        return _fp8_block_runner(cfg)
+    return _fwd_runner(cfg, p_bf16=isinstance(cfg, fa_inputs.Fp8PBf16Config),
+                       soft_exp2=isinstance(cfg, fa_inputs.SoftExp2Config))
+
+
+def work_and_unit(cfg):
+    """Algorithmic work of one call and the unit its rate is given in."""
+    if isinstance(cfg, (fa_inputs.DecodeConfig, fa_inputs.AppendConfig, fa_inputs.QuantConfig)):
+        return algorithmic_bytes(cfg), "GB/s"
+    if isinstance(cfg, fa_inputs.BwdConfig):
+        return bwd_flops(cfg), "TFLOP/s"
+    return fwd_flops(cfg), "TFLOP/s"
+
+
 def measure(name, steps, warmup, check_budget=0.0):
     """Times one workload; with check_budget > 0 and an oracle check for it,
     also the CPU baseline and the max error on the oracle's sample."""
     cfg = workload(name)
     import torch
 
-    if isinstance(cfg, fa_inputs.DecodeConfig):
-        r = _decode_runner(cfg)
-    elif isinstance(cfg, fa_inputs.AppendConfig):
-        r = _append_runner(cfg)
-    elif isinstance(cfg, fa_inputs.QuantConfig):
-        r = _quant_runner(cfg)
-    elif isinstance(cfg, fa_inputs.BwdConfig):
-        r = _bwd_runner(cfg)
-    elif isinstance(cfg, fa_inputs.Fp8BlockConfig):
-        r = _fp8_block_runner(cfg)
-    else:
-        r = _fwd_runner(cfg, p_bf16=isinstance(cfg, fa_inputs.Fp8PBf16Config),
-                        soft_exp2=isinstance(cfg, fa_inputs.SoftExp2Config))
+    r = _runner(cfg)
     ms, wall = _time_region(r.run, steps, warmup)
     each = _time_each(r.run, steps)
     med, mn = each[len(each) // 2], each[0]
@@ -686,6 +699,71 @@ def summarize_counters(dirs: str, kernel: str, workload_name: str):
     print("raw means per dispatch: " + ", ".join(f"{k}={v:.4g}" for k, v in sorted(means.items())))
 
 
+# ---- power and clock while a workload runs -----------------------------------
+
+def _smi_sample():
+    """Socket power (W) and the mean of the 8 XCDs' gfx clocks (MHz), from one
+    `amd-smi metric -p -c` reading of GPU 0; (None, None) if unavailable."""
+    import re
+    import subprocess
+
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.TimeoutExpired):
+        return None, None
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+    clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", out)]
+    return (float(pw.group(1)) if pw else None), (sum(clks) / len(clks) if clks else None)
+
+
+def power_study(names, seconds=4.0):
+    """For each workload (and the vendor bf16 GEMM, torch.matmul of 8192^3,
+    as a reference for a plain contraction on this part): run it back to back
+    for `seconds` while sampling socket power and gfx clocks; prints one
+    markdown row each: achieved rate, mean and peak power, mean clock."""
+    import threading
+
+    import torch
+
+    print("| workload | rate | mean socket power W | peak W | mean gfx clock MHz | samples |")
+    print("|---|---|---|---|---|---|")
+    # the GEMM first: it also brings the board to its steady power and temperature
+    jobs = [("vendor bf16 GEMM 8192^3 (torch.matmul)", "gemm")] + [(n, None) for n in names]
+    for name, kind in jobs:
+        if kind == "gemm":
+            a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+            b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+            c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+            run = lambda: torch.matmul(a, b, out=c)  # noqa: E731
+            work, unit = 2 * 8192 ** 3, "TFLOP/s"
+        else:
+            cfg = workload(name)
+            run = _runner(cfg).run
+            work, unit = work_and_unit(cfg)
+        ms, _ = _time_region(run, 10, 5)  # warm, and per-call time for the loop length
+        calls = max(1, int(seconds * 1e3 / ms))
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                samples.append(_smi_sample())
+                stop.wait(0.2)
+
+        th = threading.Thread(target=sampler)
+        th.start()
+        ms, _ = _time_region(run, calls, 0)
+        stop.set()
+        th.join()
+        pw = [p for p, _ in samples if p is not None]
+        ck = [c for _, c in samples if c is not None]
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        print(f"| {name} | {rate:.1f} {unit} | {sum(pw) / max(1, len(pw)):.0f} | {max(pw, default=0):.0f} | "
+              f"{sum(ck) / max(1, len(ck)):.0f} | {len(samples)} |", flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+
 # ---- main ---------------------------------------------------------------------
 
 def main():
@@ -712,7 +790,19 @@ def main():
     ap.add_argument("--bench-json")
     ap.add_argument("--summarize-counters", metavar="DIRS",
                     help="summarise rocprofv3 --pmc runs (comma-separated dirs) of --workload for --kernel")
+    ap.add_argument("--power-study", metavar="NAMES",
+                    help="sample socket power and clocks while each listed workload (comma list) runs, "
+                         "and the vendor bf16 GEMM")
     a = ap.parse_args()
+    if a.power_study:
+        import torch
+
+        import tiled_exact_attention_fa_amd as fa
+
+        fa.load()
+        torch.cuda.set_device(0)
+        power_study([n for n in a.power_study.split(",") if n])
+        return
     if a.summarize_counters:
         summarize_counters(a.summarize_counters, a.kernel, a.workload)
         return
