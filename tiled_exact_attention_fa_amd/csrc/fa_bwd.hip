@@ -13,21 +13,26 @@
 // MI355X design.  Three kernels, no atomics, so every result is deterministic:
 //   * bwd_rowdot_kernel: Dr per query row, one 16-lane group per row.
 //   * bwd_dkdv_kernel: a workgroup owns 256 keys of one (batch, kv head), a
-//     wavefront 32 of them (8 wavefronts, two per SIMD); it walks every query head of the group and every
-//     query tile that can see its keys, and keeps dK^T and dV^T of its keys in
-//     registers until the end.  Per tile: S = Q K^T and dP = dO V^T with the
-//     keys' K rows in registers and V rows in LDS as the B operands, then
-//     dV^T += dO^T P and dK^T += Q^T dS with the probabilities fed from the
-//     S accumulators straight into the B operand (the query tile is written
-//     to LDS with bits 2 and 3 of the row index swapped, which puts the
-//     accumulator registers in the operand's order).  The query tile is staged
-//     twice, row-major for the first products and transposed for the second.
+//     wavefront 32 of them (8 wavefronts, two per SIMD); it walks every query
+//     head of the group and every query tile that can see its keys, and keeps
+//     dK^T and dV^T of its keys in registers until the end.  Per 32-row query
+//     tile: S = Q K^T and dP = dO V^T with the keys' K rows in registers and V
+//     rows in LDS as the B operands, then dV^T += dO^T P and dK^T += Q^T dS
+//     with P and dS fed from the S and dP accumulators straight into the B
+//     operand.
 //   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch, head), a
-//     wavefront 32 (two wavefronts per SIMD); per 32-key tile S^T = K Q^T and dP^T = V dO^T with the rows'
-//     Q and dO in registers, then dQ^T += K^T dS^T, K staged both row-major
-//     (permuted rows) and transposed.
-//   * Both tile loops stage through two LDS buffers with register prefetch two
-//     tiles ahead: one barrier per tile.
+//     wavefront 32 (two wavefronts per SIMD); per 32-key tile S^T = K Q^T and
+//     dP^T = V dO^T with the rows' Q and dO in registers, then dQ^T += K^T dS^T.
+//   * Each staged tile (query rows of Q and dO; keys of K and V) is written to
+//     LDS once, row-major.  Row operands are read 16 bytes per lane in the
+//     order of rows that puts the accumulators in operand order (below); the
+//     transposed operands dO^T, Q^T and K^T come from the same rows through
+//     gfx950's transposing LDS reads (ds_read_b64_tr_b16), so no tile is
+//     stored twice.  Two LDS stages with register prefetch two tiles ahead:
+//     one barrier per tile.
+//   * The causal and ragged-edge masks are applied only on the tiles that
+//     need them (a wave-uniform branch); every other tile runs the plain
+//     exponential.  dP's accumulator starts at -Dr, so dS is one multiply.
 // All products are 32x32x16 MFMAs on the input type with fp32 accumulation; P
 // and dS are rounded to the input type only as MFMA operands.  Scores stay in
 // the log2 domain (tau * log2 e folded into one multiply, hardware exp2).
@@ -69,65 +74,77 @@ template <> struct BwdMfma<_Float16> {
 constexpr int kBD = 128;      // head dim
 constexpr int kEPC = 8;       // elements per 16-byte chunk
 constexpr int kCH = kBD / kEPC;
-constexpr int kRow = kBD + kEPC;  // row-major tile row in LDS, +16 bytes
+constexpr int kTR = 32;       // rows of a staged tile
 
-// LDS row holding tile row r: bits 2 and 3 swapped, so that accumulator
-// register i of lane half h of 32-row block mb holds tile row
-// 32 mb + 16 (i / 8) + 8 h + i % 8 — the order the B operand needs.
+// Accumulator row order.  An operand row read from tile row perm_row(m) (bits
+// 2 and 3 of m swapped) puts tile row 32 mb + 16 (i / 8) + 8 h + i % 8 in
+// accumulator register i of lane half h — the order in which eight
+// consecutive registers form the B operand of the next product.
 __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 __device__ __forceinline__ int acc_row(int mb, int i, int h) { return 32 * mb + 16 * (i >> 3) + 8 * h + (i & 7); }
 
-// A tile of R rows x 128 elements, loaded by NT threads: thread (g, c) holds
-// rows g * RPT .. g * RPT + RPT - 1 of chunk c, which it can write both
-// row-major (one 16-byte store per row) and transposed (RPT elements of each of
-// its 8 columns).
-template <typename T, int R, int NT = 256> struct Tile {
-  static constexpr int RPT = R * kCH / NT;   // rows per thread
-  static constexpr int NG = R / RPT;         // row groups
-  static constexpr int TROW = R + kEPC;      // transposed row in LDS (+16 bytes)
-  u32x4 r[RPT];
+// LDS layout of a staged 32-row tile (256-byte rows, no padding inside a
+// row): row r starts at byte 16 * (80 (r >> 2) + 20 (r & 3) + ((r >> 2) & 3)).
+// In 16-byte units modulo 16 (the 64 four-byte banks), row r begins at
+// 4 (r & 3) + ((r >> 2) & 3), so
+//   * 16 lanes reading the same 16 bytes of 16 rows of one aligned group of
+//     16 (the row operands) hit 16 different bank quads;
+//   * 32 lanes of a transposing read, four consecutive rows times 64 bytes,
+//     hit 16 different quads;
+//   * 16 lanes storing one row's 16 chunks hit 16 different quads.
+__host__ __device__ constexpr int row_off(int r) { return 16 * (80 * (r >> 2) + 20 * (r & 3) + ((r >> 2) & 3)); }
+constexpr int kTileBytes = (row_off(kTR - 1) + 256 + 255) / 256 * 256;
+
+// A 32-row x 128-element tile loaded by NT threads, one 16-byte chunk per
+// thread and pass; 16 consecutive threads take one row (coalesced loads,
+// conflict-free stores).
+template <int NT> struct Tile {
+  static constexpr int CPT = kTR * kCH / NT;  // chunks per thread
+  u32x4 r[CPT];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, unsigned ss, int row0, int nrows) {
-    const int g = threadIdx.x % NG, c = threadIdx.x / NG;
 #pragma unroll
-    for (int p = 0; p < RPT; ++p) {
-      const int rr = row0 + g * RPT + p;
-      r[p] = buf_load16(rs, rr < nrows ? static_cast<unsigned>(rr) * ss + c * 16u : kOOB);
+    for (int p = 0; p < CPT; ++p) {
+      const int q = threadIdx.x + NT * p;
+      const int rr = row0 + (q >> 4);
+      r[p] = buf_load16(rs, rr < nrows ? static_cast<unsigned>(rr) * ss + (q & 15) * 16u : kOOB);
     }
   }
-  __device__ __forceinline__ void store_rows(T *dst) const {
-    const int g = threadIdx.x % NG, c = threadIdx.x / NG;
+  __device__ __forceinline__ void store(char *dst) const {
 #pragma unroll
-    for (int p = 0; p < RPT; ++p)
-      *reinterpret_cast<u32x4 *>(dst + perm_row(g * RPT + p) * kRow + c * kEPC) = r[p];
-  }
-  __device__ __forceinline__ void store_transposed(T *dst) const {
-    const int g = threadIdx.x % NG, c = threadIdx.x / NG;
-#pragma unroll
-    for (int e = 0; e < kEPC; ++e) {
-      unsigned short col[RPT];
-#pragma unroll
-      for (int p = 0; p < RPT; ++p) {
-        const u32x4 w = r[p];
-        const unsigned word = w[e >> 1];
-        col[p] = static_cast<unsigned short>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-      }
-      unsigned short *d = reinterpret_cast<unsigned short *>(dst + (c * kEPC + e) * TROW + g * RPT);
-      if constexpr (RPT == 4) {
-        *reinterpret_cast<u32x2 *>(d) = u32x2{col[0] | (static_cast<unsigned>(col[1]) << 16),
-                                              col[2] | (static_cast<unsigned>(col[3]) << 16)};
-      } else if constexpr (RPT == 2) {
-        *reinterpret_cast<unsigned *>(d) = col[0] | (static_cast<unsigned>(col[1]) << 16);
-      } else {
-        static_assert(RPT == 1, "tile rows per thread");
-        *d = col[0];
-      }
+    for (int p = 0; p < CPT; ++p) {
+      const int q = threadIdx.x + NT * p;
+      *reinterpret_cast<u32x4 *>(dst + row_off(q >> 4) + (q & 15) * 16) = r[p];
     }
   }
 };
 
-// Row r of a 32x32 accumulator block as a 16-byte MFMA fragment from LDS.
-template <typename T> __device__ __forceinline__ typename BwdMfma<T>::frag lds_frag(const T *p) {
+// Row operand: 16 bytes of this lane's tile row at byte `off` of it.
+template <typename T> __device__ __forceinline__ typename BwdMfma<T>::frag lds_frag(const char *p) {
   return __builtin_bit_cast(typename BwdMfma<T>::frag, *reinterpret_cast<const u32x4 *>(p));
+}
+
+// Transposed operand from a staged tile: A[m][k] = tile[16 t + k][32 db + m]
+// for the 32x32x16 product, lane (m, kh) holding k = 8 kh .. 8 kh + 7.  A
+// ds_read_b64_tr_b16 gives lane i of each 16-lane group element i % 4 of the
+// 8 bytes addressed by lane 4 j + i / 4, as its element j; so lane s of group
+// g addresses row 16 t + 8 (g >> 1) + 4 rd + (s >> 2), columns
+// 32 db + 16 (g & 1) + 4 (s & 3) .. + 3, and reads rd = 0, 1 give k = 8 kh +
+// 0..3 and 4..7.  tr_lane() is the lane's part of that address; t and db
+// move it by whole 4-row groups (5120 and 64 bytes), rd by 1296.
+__device__ __forceinline__ int tr_lane(int lane) {
+  const int g = (lane >> 4) & 3, s = lane & 15;
+  return 2592 * (g >> 1) + 320 * (s >> 2) + 32 * (g & 1) + 8 * (s & 3);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p)));
+}
+template <typename T>
+__device__ __forceinline__ typename BwdMfma<T>::frag tr_frag(const char *tile_lane, int t, int db) {
+  const char *p = tile_lane + 5120 * t + 64 * db;
+  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 1296);
+  return __builtin_bit_cast(typename BwdMfma<T>::frag, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 template <typename T> __device__ __forceinline__ unsigned pack2(float a, float b) {
@@ -176,32 +193,32 @@ __device__ __forceinline__ float lse2_of(float lse) {
 // one 16-byte chunk each, double-buffered.
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvKeys = 32 * kDkdvWaves;
+constexpr int kVRow = kBD + kEPC;  // V row in LDS, +16 bytes: 68 dwords, so 16 rows start on 16 bank quads
 
-template <typename T, bool CAUSAL, int BR>
+template <typename T, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   using M = BwdMfma<T>;
   typedef typename M::frag frag;
-  using Tl = Tile<T, BR, 512>;
-  constexpr int MB = BR / 32;
+  using Tl = Tile<512>;
   // two LDS stages: tile w is read from stage w & 1 while tile w + 1 is
   // written to the other one, so one barrier per tile suffices
-  __shared__ __attribute__((aligned(16))) T sQ[2][BR * kRow];
-  __shared__ __attribute__((aligned(16))) T sDO[2][BR * kRow];
-  __shared__ __attribute__((aligned(16))) T sQt[2][kBD * Tl::TROW];
-  __shared__ __attribute__((aligned(16))) T sDOt[2][kBD * Tl::TROW];
-  __shared__ __attribute__((aligned(16))) float sL[2][BR];
-  __shared__ __attribute__((aligned(16))) float sD[2][BR];
-  __shared__ __attribute__((aligned(16))) T sV[kDkdvKeys * kRow];
+  __shared__ __attribute__((aligned(256))) char sQ[2][kTileBytes];
+  __shared__ __attribute__((aligned(256))) char sDO[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float sL[2][kTR];   // log2-domain LSE of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sND[2][kTR];  // -Dr of the tile's rows
+  __shared__ __attribute__((aligned(16))) T sV[kDkdvKeys * kVRow];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int kt = blockIdx.x / (a.B * a.Hkv);  // heaviest (earliest) key tiles first
   const int bh = blockIdx.x % (a.B * a.Hkv);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int j0 = kt * kDkdvKeys;
-  const int key = j0 + 32 * wave + l32;  // this lane's key (column of S, dP, dK^T, dV^T)
-  const int coff = a.Sk - a.Sq;          // key j visible from row i iff j <= i + coff
+  const int kw0 = j0 + 32 * wave;  // the wavefront's first key
+  const int key = kw0 + l32;       // this lane's key (column of S, dP, dK^T, dV^T)
+  const int coff = a.Sk - a.Sq;    // key j visible from row i iff j <= i + coff
 
   // K rows of this lane's key in registers (lane half h: elements 64 h .. 64 h + 63);
   // the workgroup's V rows into LDS, one 16-byte chunk per thread and pass
@@ -218,7 +235,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int idx = tid + 512 * p;
       const int r = idx / kCH, c = idx % kCH;
       const int kj = j0 + r;
-      *reinterpret_cast<u32x4 *>(sV + r * kRow + c * kEPC) = buf_load16(rv, kj < a.Sk ? kj * a.v_ss + c * 16 : kOOB);
+      *reinterpret_cast<u32x4 *>(sV + r * kVRow + c * kEPC) = buf_load16(rv, kj < a.Sk ? kj * a.v_ss + c * 16 : kOOB);
     }
   }
   f32x16 dk[4], dv[4];
@@ -227,37 +244,37 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   // first query row that sees any key of this workgroup
   const int i_first = CAUSAL ? max(0, j0 - coff) : 0;
-  const int t_first = i_first / BR;
-  const int n_qt = (a.Sq + BR - 1) / BR;
+  const int t_first = i_first / kTR;
+  const int n_qt = (a.Sq + kTR - 1) / kTR;
 
   // the work is the sequence of (query head of the group, query tile) items;
   // the staging pipeline runs straight through the head changes
   const int ntl = max(n_qt - t_first, 0);
   const int n_items = a.G * ntl;
   Tl tq, tdo;
-  float l_st = 0.f, d_st = 0.f;  // lse2 / row term of row tid of the staged tile (tid < BR)
+  float l_st = 0.f, nd_st = 0.f;  // lse2 / -Dr of row tid of the staged tile (tid < kTR)
   auto load_item = [&](int w) {
     const int hq = hk * a.G + w / ntl;
-    const int i0 = (t_first + w % ntl) * BR;
+    const int i0 = (t_first + w % ntl) * kTR;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
     const __amdgpu_buffer_rsrc_t rdo =
         make_rsrc(static_cast<const T *>(a.dout) + b * a.do_sb + hq * a.do_sh, a.do_ext);
     tq.load(rq, a.q_ss, i0, a.Sq);
     tdo.load(rdo, a.do_ss, i0, a.Sq);
-    if (tid < BR) {
+    if (tid < kTR) {
+      // rows past Sq: +inf LSE makes their probabilities exactly 0, so they
+      // need no mask; their dO (and so dP and dS) is 0 as well
       const int i = i0 + tid;
       l_st = i < a.Sq ? lse2_of(a.lse[b * a.lse_sb + hq * a.lse_sh + i]) : __builtin_inff();
-      d_st = i < a.Sq ? a.rowdot[(static_cast<long long>(b) * a.Hq + hq) * a.Sq + i] : 0.f;
+      nd_st = i < a.Sq ? -a.rowdot[(static_cast<long long>(b) * a.Hq + hq) * a.Sq + i] : 0.f;
     }
   };
   auto store_item = [&](int st) {
-    tq.store_rows(sQ[st]);
-    tq.store_transposed(sQt[st]);
-    tdo.store_rows(sDO[st]);
-    tdo.store_transposed(sDOt[st]);
-    if (tid < BR) {
+    tq.store(sQ[st]);
+    tdo.store(sDO[st]);
+    if (tid < kTR) {
       sL[st][tid] = l_st;
-      sD[st][tid] = d_st;
+      sND[st][tid] = nd_st;
     }
   };
   if (n_items > 0) {
@@ -267,35 +284,40 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   if (n_items > 1) load_item(1);
   __syncthreads();
 
-  const T *vrow = sV + (32 * wave + l32) * kRow + 64 * h;  // B operand of dP: this lane's key
+  const T *vrow = sV + (32 * wave + l32) * kVRow + 64 * h;  // B operand of dP: this lane's key
+  const int arow = row_off(perm_row(l32)) + 128 * h;        // row operands: tile row perm_row(l32)
+  const int trl = tr_lane(lane);
+  const bool key_ok = kw0 + 32 <= a.Sk;  // wave-uniform
   for (int w = 0; w < n_items; ++w) {
     const int st = w & 1;
-    const int i0 = (t_first + w % ntl) * BR;
+    const int i0 = (t_first + w % ntl) * kTR;
     {
-      // S = Q K^T and dP = dO V^T, rows = queries (permuted), columns = keys
-      f32x16 s[MB], dp[MB];
+      // S = Q K^T and dP - Dr = dO V^T - Dr, rows = queries (accumulator
+      // order), columns = keys
+      f32x16 s, dp;
+      {
+        const float *nd = sND[st] + 8 * h;
+        const f32x4 n0 = *reinterpret_cast<const f32x4 *>(nd), n1 = *reinterpret_cast<const f32x4 *>(nd + 4);
+        const f32x4 n2 = *reinterpret_cast<const f32x4 *>(nd + 16), n3 = *reinterpret_cast<const f32x4 *>(nd + 20);
+        dp = f32x16{n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                    n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+      }
+      s = f32x16{};
+      const char *qr = sQ[st] + arow;
+      const char *dr = sDO[st] + arow;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        s[mb] = dp[mb] = f32x16{};
-        const T *qr = sQ[st] + (32 * mb + l32) * kRow + 64 * h;
-        const T *dr = sDO[st] + (32 * mb + l32) * kRow + 64 * h;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          s[mb] = M::mma(lds_frag<T>(qr + 8 * c), kf[c], s[mb]);
-          dp[mb] = M::mma(lds_frag<T>(dr + 8 * c), lds_frag<T>(vrow + 8 * c), dp[mb]);
-        }
+      for (int c = 0; c < 8; ++c) {
+        s = M::mma(lds_frag<T>(qr + 16 * c), kf[c], s);
+        dp = M::mma(lds_frag<T>(dr + 16 * c), lds_frag<T>(reinterpret_cast<const char *>(vrow + 8 * c)), dp);
       }
       // P and dS, as B operands over query steps of 16
-      frag pf[BR / 16], dsf[BR / 16];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+      frag pf[2], dsf[2];
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int r0 = 32 * mb + 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
+          const int r0 = 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
           const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL[st] + r0);
           const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL[st] + r0 + 4);
-          const f32x4 d0 = *reinterpret_cast<const f32x4 *>(sD[st] + r0);
-          const f32x4 d1 = *reinterpret_cast<const f32x4 *>(sD[st] + r0 + 4);
           unsigned pw[4], dw[4];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
@@ -304,31 +326,37 @@ void bwd_dkdv_kernel(const BwdArgs a) {
             for (int u = 0; u < 2; ++u) {
               const int e = 2 * e2 + u;
               const int ireg = 8 * half + e;
-              const int qi = i0 + r0 + e;
               const float l2 = e < 4 ? l0[e] : l1[e - 4];
-              const float dd = e < 4 ? d0[e] : d1[e - 4];
-              bool vis = qi < a.Sq && key < a.Sk;
-              if (CAUSAL) vis = vis && key <= qi + coff;
-              const float p = vis ? fast_exp2(s[mb][ireg] * a.c - l2) : 0.f;
+              float p = fast_exp2(s[ireg] * a.c - l2);
+              if constexpr (decltype(masked)::value) {
+                bool vis = key < a.Sk;
+                if (CAUSAL) vis = vis && key <= i0 + r0 + e + coff;
+                p = vis ? p : 0.f;
+              }
               pv[u] = p;
-              dsv[u] = p * (dp[mb][ireg] - dd);
+              dsv[u] = p * dp[ireg];
             }
             pw[e2] = pack2<T>(pv[0], pv[1]);
             dw[e2] = pack2<T>(dsv[0], dsv[1]);
           }
-          pf[2 * mb + half] = __builtin_bit_cast(frag, u32x4{pw[0], pw[1], pw[2], pw[3]});
-          dsf[2 * mb + half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
+          pf[half] = __builtin_bit_cast(frag, u32x4{pw[0], pw[1], pw[2], pw[3]});
+          dsf[half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
         }
-      }
+      };
+      // the mask matters only on tiles that reach past the diagonal or Sk
+      if (key_ok && (!CAUSAL || kw0 + 31 <= i0 + coff))
+        softmax_grad(std::false_type{});
+      else
+        softmax_grad(std::true_type{});
       // dV^T += dO^T P, dK^T += Q^T dS: rows = head dims, columns = keys
+      const char *dot = sDO[st] + trl;
+      const char *qt = sQ[st] + trl;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const T *dot = sDOt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
-        const T *qtp = sQt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
 #pragma unroll
-        for (int t = 0; t < BR / 16; ++t) {
-          dv[db] = M::mma(lds_frag<T>(dot + 16 * t), pf[t], dv[db]);
-          dk[db] = M::mma(lds_frag<T>(qtp + 16 * t), dsf[t], dk[db]);
+        for (int t = 0; t < 2; ++t) {
+          dv[db] = M::mma(tr_frag<T>(dot, t, db), pf[t], dv[db]);
+          dk[db] = M::mma(tr_frag<T>(qt, t, db), dsf[t], dk[db]);
         }
       }
     }
@@ -355,29 +383,30 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
 }
 
-// ---- dQ: a workgroup owns 128 query rows, a wavefront 32; key tiles of 64 ----
-template <typename T, bool CAUSAL, int BC>
+// ---- dQ: a workgroup owns 128 query rows, a wavefront 32; key tiles of 32 ----
+template <typename T, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const BwdArgs a) {
   using M = BwdMfma<T>;
   typedef typename M::frag frag;
-  using Tl = Tile<T, BC>;
-  __shared__ __attribute__((aligned(16))) T sK[2][BC * kRow];
-  __shared__ __attribute__((aligned(16))) T sV[2][BC * kRow];
-  __shared__ __attribute__((aligned(16))) T sKt[2][kBD * Tl::TROW];
+  using Tl = Tile<256>;
+  __shared__ __attribute__((aligned(256))) char sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(256))) char sV[2][kTileBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int nq = (a.Sq + 127) / 128;
   const int qt = nq - 1 - static_cast<int>(blockIdx.x) / (a.B * a.Hq);  // heaviest (last) rows first
   const int bh = blockIdx.x % (a.B * a.Hq);
   const int b = bh / a.Hq, hq = bh % a.Hq, hk = hq / a.G;
   const int i0 = qt * 128;
-  const int row = i0 + 32 * wave + l32;  // this lane's query row
+  const int rw0 = i0 + 32 * wave;  // the wavefront's first query row
+  const int row = rw0 + l32;       // this lane's query row
   const int coff = a.Sk - a.Sq;
 
   frag qf[8], df[8];
-  float l2 = __builtin_inff(), dd = 0.f;
+  float l2 = __builtin_inff(), dd = 0.f;  // rows past Sq: +inf LSE, so P = 0 without a mask
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
     const __amdgpu_buffer_rsrc_t rdo =
@@ -393,53 +422,51 @@ void bwd_dq_kernel(const BwdArgs a) {
       dd = a.rowdot[(static_cast<long long>(b) * a.Hq + hq) * a.Sq + row];
     }
   }
+  // dP^T's accumulator starts at -Dr of the lane's row (its column), kept in
+  // registers of its own for the whole loop
+  f32x16 ndd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndd[i] = -dd;
   f32x16 dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
 
-  int n_kt = (a.Sk + BC - 1) / BC;
+  int n_kt = (a.Sk + kTR - 1) / kTR;
   if (CAUSAL) {
     const int last = min(i0 + 127, a.Sq - 1) + coff;  // last key any row of the workgroup sees
-    n_kt = min(n_kt, last < 0 ? 0 : last / BC + 1);
+    n_kt = min(n_kt, last < 0 ? 0 : last / kTR + 1);
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const T *>(a.k) + b * a.k_sb + hk * a.k_sh, a.k_ext);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const T *>(a.v) + b * a.v_sb + hk * a.v_sh, a.v_ext);
   Tl tk, tv;
-  auto store_tile = [&](int st) {
-    tk.store_rows(sK[st]);
-    tk.store_transposed(sKt[st]);
-    tv.store_rows(sV[st]);
-  };
   if (n_kt > 0) {
     tk.load(rk, a.k_ss, 0, a.Sk);
     tv.load(rv, a.v_ss, 0, a.Sk);
-    store_tile(0);
+    tk.store(sK[0]);
+    tv.store(sV[0]);
   }
   if (n_kt > 1) {
-    tk.load(rk, a.k_ss, BC, a.Sk);
-    tv.load(rv, a.v_ss, BC, a.Sk);
+    tk.load(rk, a.k_ss, kTR, a.Sk);
+    tv.load(rv, a.v_ss, kTR, a.Sk);
   }
   __syncthreads();
+  const int arow = row_off(perm_row(l32)) + 128 * h;  // row operands: tile row perm_row(l32)
+  const int trl = tr_lane(lane);
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int j0 = kt * BC;
+    const int j0 = kt * kTR;
     const int st = kt & 1;
-    // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), columns = query rows
-    constexpr int MB = BC / 32;
-    f32x16 s[MB], dp[MB];
+    // S^T = K Q^T and dP^T - Dr = V dO^T - Dr: rows = keys (accumulator
+    // order), columns = query rows
+    f32x16 s = f32x16{}, dp = ndd;
+    const char *kr = sK[st] + arow;
+    const char *vr = sV[st] + arow;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      s[mb] = dp[mb] = f32x16{};
-      const T *kr = sK[st] + (32 * mb + l32) * kRow + 64 * h;
-      const T *vr = sV[st] + (32 * mb + l32) * kRow + 64 * h;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        s[mb] = M::mma(lds_frag<T>(kr + 8 * c), qf[c], s[mb]);
-        dp[mb] = M::mma(lds_frag<T>(vr + 8 * c), df[c], dp[mb]);
-      }
+    for (int c = 0; c < 8; ++c) {
+      s = M::mma(lds_frag<T>(kr + 16 * c), qf[c], s);
+      dp = M::mma(lds_frag<T>(vr + 16 * c), df[c], dp);
     }
-    frag dsf[BC / 16];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    frag dsf[2];
+    auto softmax_grad = [&](auto masked) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         unsigned dw[4];
@@ -448,28 +475,39 @@ void bwd_dq_kernel(const BwdArgs a) {
           float dsv[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int e = 2 * e2 + u, ireg = 8 * half + e;
-            const int kj = j0 + acc_row(mb, ireg, h);
-            bool vis = row < a.Sq && kj < a.Sk;
-            if (CAUSAL) vis = vis && kj <= row + coff;
-            const float p = vis ? fast_exp2(s[mb][ireg] * a.c - l2) : 0.f;
-            dsv[u] = p * (dp[mb][ireg] - dd);
+            const int ireg = 8 * half + 2 * e2 + u;
+            float p = fast_exp2(s[ireg] * a.c - l2);
+            if constexpr (decltype(masked)::value) {
+              const int kj = j0 + acc_row(0, ireg, h);
+              bool vis = kj < a.Sk;
+              if (CAUSAL) vis = vis && kj <= row + coff;
+              p = vis ? p : 0.f;
+            }
+            dsv[u] = p * dp[ireg];
           }
           dw[e2] = pack2<T>(dsv[0], dsv[1]);
         }
-        dsf[2 * mb + half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
+        dsf[half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
       }
+    };
+    // the mask matters only on tiles that reach past the diagonal or Sk
+    if (j0 + kTR <= a.Sk && (!CAUSAL || j0 + kTR - 1 <= rw0 + coff))
+      softmax_grad(std::false_type{});
+    else
+      softmax_grad(std::true_type{});
     // dQ^T += K^T dS^T: rows = head dims, columns = query rows
+    const char *ktp = sK[st] + trl;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const T *ktp = sKt[st] + (32 * db + l32) * Tl::TROW + 8 * h;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int t = 0; t < BC / 16; ++t) dq[db] = M::mma(lds_frag<T>(ktp + 16 * t), dsf[t], dq[db]);
+      for (int t = 0; t < 2; ++t) dq[db] = M::mma(tr_frag<T>(ktp, t, db), dsf[t], dq[db]);
+    if (kt + 1 < n_kt) {  // that stage was last read by tile kt - 1
+      tk.store(sK[st ^ 1]);
+      tv.store(sV[st ^ 1]);
     }
-    if (kt + 1 < n_kt) store_tile(st ^ 1);  // that stage was last read by tile kt - 1
     if (kt + 2 < n_kt) {
-      tk.load(rk, a.k_ss, j0 + 2 * BC, a.Sk);
-      tv.load(rv, a.v_ss, j0 + 2 * BC, a.Sk);
+      tk.load(rk, a.k_ss, j0 + 2 * kTR, a.Sk);
+      tv.load(rv, a.v_ss, j0 + 2 * kTR, a.Sk);
     }
     __syncthreads();
   }
@@ -498,7 +536,6 @@ int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
   }
   const unsigned g_kv = static_cast<unsigned>((a.Sk + kDkdvKeys - 1) / kDkdvKeys) * a.B * a.Hkv;
   const unsigned g_q = static_cast<unsigned>((a.Sq + 127) / 128) * a.B * a.Hq;
-  constexpr int BR = 32, BC = 32;  // query rows per dK/dV tile, keys per dQ tile
   if (g_kv)
     fa_log_launch("bwd_dkdv_kernel", g_kv, 512, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
                   causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
@@ -506,11 +543,11 @@ int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
     fa_log_launch("bwd_dq_kernel", g_q, 256, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
                   causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
   if (causal) {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, BR>), dim3(g_kv), dim3(512), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true, BC>), dim3(g_q), dim3(256), 0, s, a);
+    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true>), dim3(g_kv), dim3(512), 0, s, a);
+    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(g_q), dim3(256), 0, s, a);
   } else {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, false, BR>), dim3(g_kv), dim3(512), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, false, BC>), dim3(g_q), dim3(256), 0, s, a);
+    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, false>), dim3(g_kv), dim3(512), 0, s, a);
+    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, false>), dim3(g_q), dim3(256), 0, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
