@@ -253,20 +253,31 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int n_items = a.G * ntl;
   Tl tq, tdo;
   float l_st = 0.f, nd_st = 0.f;  // lse2 / -Dr of row tid of the staged tile (tid < kTR)
-  auto load_item = [&](int w) {
-    const int hq = hk * a.G + w / ntl;
-    const int i0 = (t_first + w % ntl) * kTR;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const T *>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_ext);
-    const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(static_cast<const T *>(a.dout) + b * a.do_sb + hq * a.do_sh, a.do_ext);
-    tq.load(rq, a.q_ss, i0, a.Sq);
-    tdo.load(rdo, a.do_ss, i0, a.Sq);
+  // Items are loaded in order; the cursor keeps the loading item's head as
+  // pointers (advanced when the head changes) and its tile index, so the
+  // loop does no division or 64-bit address arithmetic per tile.
+  const T *qh = static_cast<const T *>(a.q) + b * a.q_sb + static_cast<long long>(hk * a.G) * a.q_sh;
+  const T *doh = static_cast<const T *>(a.dout) + b * a.do_sb + static_cast<long long>(hk * a.G) * a.do_sh;
+  const float *lseh = a.lse + b * a.lse_sb + static_cast<long long>(hk * a.G) * a.lse_sh;
+  const float *rdh = a.rowdot + (static_cast<long long>(b) * a.Hq + hk * a.G) * a.Sq;
+  int lt = 0;  // tile of the next item to load
+  auto load_next = [&]() {
+    const int i0 = (t_first + lt) * kTR;
+    tq.load(make_rsrc(qh, a.q_ext), a.q_ss, i0, a.Sq);
+    tdo.load(make_rsrc(doh, a.do_ext), a.do_ss, i0, a.Sq);
     if (tid < kTR) {
       // rows past Sq: +inf LSE makes their probabilities exactly 0, so they
       // need no mask; their dO (and so dP and dS) is 0 as well
       const int i = i0 + tid;
-      l_st = i < a.Sq ? lse2_of(a.lse[b * a.lse_sb + hq * a.lse_sh + i]) : __builtin_inff();
-      nd_st = i < a.Sq ? -a.rowdot[(static_cast<long long>(b) * a.Hq + hq) * a.Sq + i] : 0.f;
+      l_st = i < a.Sq ? lse2_of(lseh[i]) : __builtin_inff();
+      nd_st = i < a.Sq ? -rdh[i] : 0.f;
+    }
+    if (++lt == ntl) {
+      lt = 0;
+      qh += a.q_sh;
+      doh += a.do_sh;
+      lseh += a.lse_sh;
+      rdh += a.Sq;
     }
   };
   auto store_item = [&](int st) {
@@ -278,19 +289,24 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   };
   if (n_items > 0) {
-    load_item(0);
+    load_next();
     store_item(0);
   }
-  if (n_items > 1) load_item(1);
+  // K's fragments, V and tile 0 have landed: the loop's MFMAs then wait on
+  // nothing but LDS, and the prefetch below stays in flight across a tile
+  wait_vmem_all();
+  if (n_items > 1) load_next();
   __syncthreads();
 
   const T *vrow = sV + (32 * wave + l32) * kVRow + 64 * h;  // B operand of dP: this lane's key
   const int arow = row_off(perm_row(l32)) + 128 * h;        // row operands: tile row perm_row(l32)
   const int trl = tr_lane(lane);
   const bool key_ok = kw0 + 32 <= a.Sk;  // wave-uniform
+  int ct = 0;  // tile of the current item
   for (int w = 0; w < n_items; ++w) {
     const int st = w & 1;
-    const int i0 = (t_first + w % ntl) * kTR;
+    const int i0 = (t_first + ct) * kTR;
+    ct = ct + 1 == ntl ? 0 : ct + 1;
     {
       // S = Q K^T and dP - Dr = dO V^T - Dr, rows = queries (accumulator
       // order), columns = keys
@@ -361,7 +377,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       }
     }
     if (w + 1 < n_items) store_item(st ^ 1);  // that stage was last read by tile w - 1
-    if (w + 2 < n_items) load_item(w + 2);
+    if (w + 2 < n_items) load_next();
     __syncthreads();
   }
 
