@@ -28,8 +28,13 @@
 //     then uses the 16-bit kernel's row order (bits 2 and 3 of the key index
 //     swapped), which puts the score accumulators in the order of the bf16
 //     P^T operand.
-//   * V is transposed in registers (4 keys x 4 columns per thread, byte
-//     permutes) on its way into a double-buffered LDS stage.
+//   * V: with e4m3 probabilities the tile goes to LDS row-major, one 16-byte
+//     load and store per thread like K, and the V^T operand comes from
+//     gfx950's byte-transposing LDS read (ds_read_b64_tr_b8: four of them give
+//     a lane the 32 keys of one head dimension), so no vector instruction
+//     touches V.  With bf16 probabilities V is converted to bf16 and
+//     transposed in registers (4 keys x 4 columns per thread, byte permutes)
+//     on its way into LDS.
 //   * At twice the bf16 matrix rate the softmax is as long as the products, so
 //     the loop is software-pipelined like the 16-bit kernel: 8 wavefronts over
 //     256 rows; P V of tile t carries the first half of tile t+1's softmax
@@ -61,9 +66,14 @@ constexpr int BR = 256;   // query rows per workgroup (8 wavefronts x 32)
 constexpr int BC = 64;    // keys per tile: one 64-deep MFMA for P V
 constexpr int D = 128;
 constexpr int KROW = D + 16;   // bytes per K row in LDS
-constexpr int VROW = BC + 16;  // bytes per V^T row in LDS
+constexpr int VROW = BC + 16;  // bytes per V^T row in LDS (bf16-probability mode: see VROW16)
+// e4m3 mode: V row-major, 160 bytes per key row, so that the eight rows a
+// transposing read covers per 32 lanes start 40 dwords apart and fill the 64
+// banks exactly
+constexpr int VROWR = D + 32;
 constexpr int K_TILE = BC * KROW;
 constexpr int V_TILE = D * VROW;
+static_assert(BC * VROWR == V_TILE, "row-major and transposed V tiles take the same bytes");
 constexpr int ORow = D + 8;    // bf16 elements per row of the epilogue slab
 constexpr int STAGES_BYTES = 2 * (K_TILE + V_TILE);
 constexpr int SLAB_BYTES = NT / 64 * 32 * ORow * 2;
@@ -105,6 +115,14 @@ __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c) {
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// ds_read_b64_tr_b8: lane i of each 16-lane group gets, as its byte j, byte
+// i % 8 of the 8 bytes addressed by lane 2 j + i / 8 of the group
+__device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char *p) {
+  typedef int v2i32 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(p)));
 }
 
 }  // namespace f8
@@ -157,8 +175,9 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     w_kt = min(n_kt, last_w < 0 ? 0 : last_w / BC + 1);
   }
 
-  // ---- staging: K, thread t loads row t/8, 16-byte chunk t%8; V, thread t
-  // loads columns 4*(t/16) .. +3 of keys 4*(t%16) .. +3 (one word per key).
+  // ---- staging: K (and V with e4m3 probabilities), thread t loads row t/8,
+  // 16-byte chunk t%8; V with bf16 probabilities, thread t loads columns
+  // 4*(t/16) .. +3 of keys 4*(t%16) .. +3 (one word per key).
   // Loads go through a buffer resource placed at the tile's first row, so the
   // lane offsets are loop constants and rows past the keys read as zero. ----
   const int k_c = tid & 7, k_r = tid >> 3;
@@ -178,7 +197,8 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) voff[p] = (4 * v_g + p) * a.v_ss + 4u * v_c;
   u32x4 kreg[2];
-  unsigned vreg[2][4];
+  unsigned vreg[2][4];  // bf16-probability mode
+  u32x4 vrow8[2];       // e4m3 mode
   auto load_k_to = [&](u32x4 &dst, int j) { dst = buf_load16(tile_rsrc(kbase, a.k_ss, a.k_ext, j), koff); };
   // ---- block descales: the lane's query-row descale in the score constant,
   // the largest V descale of the slice, and per-tile descales loaded ahead
@@ -221,21 +241,29 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 
   auto load_v = [&](int set, int j) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
+    if constexpr (PB16) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vreg[set][p] = buf_load4(r, voff[p]);
+      for (int p = 0; p < 4; ++p) vreg[set][p] = buf_load4(r, voff[p]);
+    } else {
+      vrow8[set] = buf_load16(r, k_r * a.v_ss + 16u * k_c);
+    }
   };
   auto store_k_from = [&](const u32x4 &src, int buf) {
     const int r = PB16 ? k_lds_row16(k_r) : k_lds_row(k_r);
     *reinterpret_cast<u32x4 *>(kbuf + buf * K_TILE + r * KROW + 16 * k_c) = src;
   };
-  // 4 keys x 4 columns -> 4 columns x 4 keys
+  // e4m3 mode: the row as loaded; bf16 mode: 4 keys x 4 columns -> 4 columns x 4 keys
   auto store_v = [&](int set, int buf) {
+    if constexpr (!PB16) {
+      *reinterpret_cast<u32x4 *>(vbuf + buf * VT + k_r * VROWR + 16 * k_c) = vrow8[set];
+      return;
+    }
     const unsigned *r = vreg[set];
     const unsigned x01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // k0c0 k1c0 k0c1 k1c1
     const unsigned x23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
     const unsigned y01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // k0c2 k1c2 k0c3 k1c3
     const unsigned y23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-    if constexpr (PB16) {
+    {
       // each word of key pairs -> two bf16 (exact); column 4 v_c + e gets keys
       // 4 v_g .. 4 v_g + 3 as one 8-byte store
       auto lo = [](unsigned w) {
@@ -250,15 +278,6 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         *reinterpret_cast<u32x2 *>(vt + ((4 * v_c + e) * VROW16 + 4 * v_g) * 2) = col[e];
-    } else {
-      unsigned col[4];
-      col[0] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
-      col[1] = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
-      col[2] = __builtin_amdgcn_perm(y23, y01, 0x05040100u);
-      col[3] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
-      unsigned char *vt = vbuf + buf * VT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<unsigned *>(vt + (4 * v_c + e) * VROW + 4 * v_g) = col[e];
     }
   };
 
@@ -273,14 +292,20 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   constexpr int RA = 2;
   constexpr int STEPS = 16;
   const unsigned char *k_lane = kbuf + l32 * KROW + 64 * h;
-  const unsigned char *v_lane = vbuf + l32 * VROW + 32 * h;
+  // e4m3 mode, transposing V reads: lane s of 16-lane group g addresses key row
+  // 32 (g >> 1) + 8 rd + (s >> 1), columns 32 i + 16 (g & 1) + 8 (s & 1) .. + 7,
+  // so that read rd gives lane (m, h) keys 32 h + 8 rd .. + 7 of column 32 i + m
+  const unsigned char *v_lane =
+      vbuf + (32 * h + ((lane & 15) >> 1)) * VROWR + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
   // MFMA i of S^T: key block i & 1, depth step i >> 1
   auto kfrag = [&](int buf, int i, int half) {
     return *reinterpret_cast<const u32x4 *>(k_lane + buf * K_TILE + (i & 1) * 32 * KROW + 32 * (i >> 1) + 16 * half);
   };
-  // MFMA i of O^T: head-dim block i
+  // MFMA i of O^T: head-dim block i; bytes 16 half .. 16 half + 15 of the lane's 32
   auto vfrag = [&](int buf, int i, int half) {
-    return *reinterpret_cast<const u32x4 *>(v_lane + buf * VT + i * 32 * VROW + 16 * half);
+    const unsigned char *p = v_lane + buf * VT + 32 * i + 2 * half * 8 * VROWR;
+    const u32x2 lo = lds_read_tr8(p), hi = lds_read_tr8(p + 8 * VROWR);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
   // bf16-probability mode, MFMA i of O^T: head-dim block i >> 2, key step i & 3
   const unsigned char *v_lane16 = vbuf + (l32 * VROW16 + 8 * h) * 2;
