@@ -539,6 +539,28 @@ def copy_calibration(nbytes: int, reps: int = 3):
     torch.cuda.synchronize()
 
 
+def stream_ceiling(nbytes: int = 4_363_132_928, steps: int = 10):
+    """Practical HBM ceilings from vendor kernels on a buffer the size of the
+    int8 decode workload's algorithmic bytes: a read-only reduction (max over
+    int64 words: every byte read once, nothing written of note) and a copy
+    (read and write).  One markdown row each."""
+    import torch
+
+    n = nbytes // 8
+    x = torch.randint(0, 1 << 30, (n,), dtype=torch.int64, device="cuda")
+    y = torch.empty_like(x)
+    print("| kernel | bytes moved per call | ms per call | GB/s |")
+    print("|---|---|---|---|")
+    rows = [("read: torch.amax over int64 words", lambda: torch.amax(x), 8 * n),
+            ("read: torch.sum over int64 words", lambda: torch.sum(x), 8 * n),
+            ("copy: y.copy_(x)", lambda: y.copy_(x), 16 * n)]
+    for name, fn, moved in rows:
+        ms, _ = _time_region(fn, steps, 3)
+        print(f"| {name} | {moved} | {ms:.4f} | {moved / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+    del x, y
+    torch.cuda.empty_cache()
+
+
 def _pmc_per_dispatch(csv_dir: str, counter: str, kernel_substr: str):
     import csv
     import glob
@@ -699,6 +721,61 @@ def summarize_counters(dirs: str, kernel: str, workload_name: str):
     print("raw means per dispatch: " + ", ".join(f"{k}={v:.4g}" for k, v in sorted(means.items())))
 
 
+def summarize_memory(dirs: str, kernel: str, label: str):
+    """Memory-pipeline figures of rocprofv3 --pmc runs (comma-separated output
+    directories) for the kernels whose name contains `kernel`, means over
+    their dispatches: texture-address (TA) busy share of all CU cycles and the
+    share of that stalled by the L1 (TCP); average L2-to-memory read latency
+    (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ) and reads in flight; DRAM credit
+    stalls and L2 busy per channel-cycle (128 channels); L1 pending-stall share;
+    the wave-state split (waiting on a dependency / ready but not issued /
+    issuing).  Kernel cycles = GRBM_GUI_ACTIVE / 8."""
+    import csv
+    import glob
+
+    per = {}
+    for d in dirs.split(","):
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if kernel not in r["Kernel_Name"]:
+                        continue
+                    key = (d, r["Dispatch_Id"])
+                    per.setdefault(key, {})
+                    per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatches of {kernel!r} under {dirs}")
+    sums, cnt = {}, {}
+    for v in per.values():
+        for c, x in v.items():
+            sums[c] = sums.get(c, 0.0) + x
+            cnt[c] = cnt.get(c, 0) + 1
+    m = {c: sums[c] / cnt[c] for c in sums}
+    cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / 8
+
+    def frac(num, den):
+        return f"{num / den:.3g}" if den else "-"
+
+    parts = [label, f"{cyc:.4g}" if cyc else "-"]
+    parts.append(frac(m.get("TA_TA_BUSY_sum", 0.0), 256 * cyc) if "TA_TA_BUSY_sum" in m else "-")
+    parts.append(frac(m.get("TA_ADDR_STALLED_BY_TC_CYCLES_sum", 0.0), m.get("TA_TA_BUSY_sum", 0.0))
+                 if "TA_ADDR_STALLED_BY_TC_CYCLES_sum" in m else "-")
+    if "TCC_EA0_RDREQ_sum" in m:
+        parts.append(f"{m['TCC_EA0_RDREQ_LEVEL_sum'] / m['TCC_EA0_RDREQ_sum']:.0f}")
+        parts.append(f"{m['TCC_EA0_RDREQ_LEVEL_sum'] / cyc:.3g}" if cyc else "-")
+        parts.append(frac(m.get("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", 0.0), 128 * cyc))
+        parts.append(frac(m.get("TCC_BUSY_sum", 0.0), 128 * cyc))
+    else:
+        parts += ["-"] * 4
+    parts.append(frac(m.get("TCP_PENDING_STALL_CYCLES_sum", 0.0), 256 * cyc) if "TCP_PENDING_STALL_CYCLES_sum" in m else "-")
+    if "SQ_WAVE_CYCLES" in m:
+        w = m["SQ_WAVE_CYCLES"]
+        parts.append(f"{m['SQ_WAIT_ANY'] / w:.2f} / {m['SQ_WAIT_INST_ANY'] / w:.2f} / {m['SQ_ACTIVE_INST_ANY'] / w:.2f}")
+    else:
+        parts.append("-")
+    print("| " + " | ".join(parts) + " |")
+
+
 # ---- power and clock while a workload runs -----------------------------------
 
 def _smi_sample():
@@ -790,10 +867,24 @@ def main():
     ap.add_argument("--bench-json")
     ap.add_argument("--summarize-counters", metavar="DIRS",
                     help="summarise rocprofv3 --pmc runs (comma-separated dirs) of --workload for --kernel")
+    ap.add_argument("--summarize-memory", metavar="DIRS",
+                    help="summarise memory-pipeline rocprofv3 --pmc runs (comma-separated dirs) of --kernel")
+    ap.add_argument("--label", default="")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="time vendor read-only and copy kernels over the decode workload's byte count")
     ap.add_argument("--power-study", metavar="NAMES",
                     help="sample socket power and clocks while each listed workload (comma list) runs, "
                          "and the vendor bf16 GEMM")
     a = ap.parse_args()
+    if a.summarize_memory:
+        summarize_memory(a.summarize_memory, a.kernel, a.label or a.kernel)
+        return
+    if a.stream_ceiling:
+        import torch
+
+        torch.cuda.set_device(0)
+        stream_ceiling()
+        return
     if a.power_study:
         import torch
 
