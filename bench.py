@@ -623,7 +623,13 @@ def _kernel_label(name: str) -> str:
             out.append("bf16" if g == "DF16b" else "f16" if g == "DF16_" else (t.group(1) or t.group(2)))
         del args
         return f"{m.group(1)}<{', '.join(out)}>"
-    return name.replace("void ", "").split("(")[0].replace("fa::", "")
+    label = name.replace("void ", "").split("(")[0].replace("fa::", "")
+    # the tracer's demangler garbles some template argument lists (a bool
+    # pack comes out as "<bool _Accum, bool, E>"): drop those rather than
+    # print them
+    if "_Accum" in label:
+        label = label.split("<")[0]
+    return label
 
 
 def summarize_trace(trace_csv: str, bench_json: str):
