@@ -144,7 +144,7 @@ def launches_per_call(cfg) -> int:
 
 def workload(name):
     for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS,
-                  fa_inputs.SOFT_EXP2_CONFIGS):
+                  fa_inputs.SOFT_EXP2_CONFIGS, fa_inputs.NO_LSE_CONFIGS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -228,7 +228,7 @@ def _fwd_oracle_check(cfg, x, o, lse, budget_s):
     else:
         qf, kf, vf = (x[n].cpu().double().numpy() for n in ("q", "k", "v"))
     og = o.cpu().double().numpy()
-    lg = lse.cpu().double().numpy()
+    lg = lse.cpu().double().numpy() if lse is not None else None
     cores = _cores()
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
     n = min(len(heads), cores)
@@ -243,8 +243,9 @@ def _fwd_oracle_check(cfg, x, o, lse, budget_s):
             bi = [b for b, _ in part]
             hi = [h for _, h in part]
             err_o = max(err_o, float(np.max(np.abs(og[bi, hi] - ro[bi, hi]))))
-            fin = np.isfinite(rl[bi, hi])
-            err_l = max(err_l, float(np.max(np.abs(lg[bi, hi][fin] - rl[bi, hi][fin]), initial=0.0)))
+            if lg is not None:
+                fin = np.isfinite(rl[bi, hi])
+                err_l = max(err_l, float(np.max(np.abs(lg[bi, hi][fin] - rl[bi, hi][fin]), initial=0.0)))
             checked += len(part)
         done += len(part)
         # stop before a chunk that would overrun the budget
@@ -257,7 +258,8 @@ def _fwd_oracle_check(cfg, x, o, lse, budget_s):
         sample = f"{done / len(heads):.1f} passes over all {len(heads)} (batch, head) pairs"
     cpu = {"value": flops / elapsed / 1e9, "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
            "sample": f"{sample} of {cfg.name}, float64 numpy two-pass, {elapsed:.1f} s wall"}
-    err = {"O": err_o, "LSE": err_l, "sample": f"{checked} of {len(heads)} (batch, head) pairs, every row"}
+    err = {"O": err_o, "LSE": err_l if lg is not None else None,
+           "sample": f"{checked} of {len(heads)} (batch, head) pairs, every row"}
     return cpu, err
 
 
@@ -305,7 +307,7 @@ def _fwd_runner(cfg, seed=0, p_bf16=False, soft_exp2=False):
     q, k, v = x["q"], x["k"], x["v"]
     odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.bfloat16}[cfg.dtype]
     o = torch.empty(q.shape, dtype=odt, device="cuda")
-    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda")
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda") if cfg.lse else None
     ds = (x.get("q_scale", 1.0), x.get("k_scale", 1.0), x.get("v_scale", 1.0))
 
     def run():
@@ -929,7 +931,8 @@ def main():
 
     extras = {}
     names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.BWD_CONFIGS) + list(fa_inputs.KV_CONFIGS)
-             + list(fa_inputs.FP8_VARIANT_CONFIGS) + list(fa_inputs.SOFT_EXP2_CONFIGS) if n != a.workload]
+             + list(fa_inputs.FP8_VARIANT_CONFIGS) + list(fa_inputs.SOFT_EXP2_CONFIGS)
+             + list(fa_inputs.NO_LSE_CONFIGS) if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":
@@ -954,7 +957,7 @@ def main():
     conf = {"workload": a.workload}
     if isinstance(cfg, fa_inputs.FwdConfig):
         conf.update({"B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "seq_len": cfg.Sq, "d": cfg.d,
-                     "causal": cfg.causal, "lse": True})
+                     "causal": cfg.causal, "lse": cfg.lse})
     out = {
         "metric": METRIC,
         "value": head["value"],

@@ -60,6 +60,7 @@ class FwdConfig:
     causal: bool
     outlier_frac: float = 0.0
     out_dtype: str = ""
+    lse: bool = True  # whether the call asks for the LSE output
 
     @property
     def scale(self) -> float:
@@ -169,6 +170,14 @@ class SoftExp2Config(FwdConfig):
 SOFT_EXP2_CONFIGS = {
     "softexp2_bf16_gqa32x8_s16384_causal_outlier": SoftExp2Config(
         "softexp2_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
+}
+
+# The long-context workload called without an LSE output (the workload as
+# specified names only O; the kernel then skips the unrounded row sum).
+NO_LSE_CONFIGS = {
+    "nolse_bf16_gqa32x8_s16384_causal_outlier": FwdConfig(
+        "nolse_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01,
+        lse=False),
 }
 
 # The fp8 accuracy variants at the fp8 workload's shape: the forward on

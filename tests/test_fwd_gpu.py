@@ -125,6 +125,26 @@ def test_fwd_no_lse_and_strided_layout(gpu):
     check(o, None, q, k, v, True, "bf16")
 
 
+NO_LSE_SHAPES = [(1, 2, 2, 64, 64), (2, 8, 2, 300, 300), (1, 4, 1, 130, 300), (1, 2, 2, 300, 130),
+                 (1, 2, 2, 1, 1), (1, 4, 4, 1024, 1024)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", NO_LSE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_without_lse_output(gpu, dt, causal, shape):
+    """With no LSE pointer the d = 128 kernel skips the unrounded row sum; O
+    is divided by the rounded sum either way, so O must equal the O of the
+    call with an LSE output bit for bit, and meet the oracle's bar."""
+    B, Hq, Hkv, Sq, Sk = shape
+    q, k, v = make(B, Hq, Hkv, Sq, Sk, 128, dt, seed=Sq + 3 * Sk)
+    o_l, lse = run_fwd(gpu, q, k, v, causal, TDT[dt])
+    o_n, none = run_fwd(gpu, q, k, v, causal, TDT[dt], lse_wanted=False)
+    assert none is None
+    assert torch.equal(o_n, o_l), "O differs between the calls with and without an LSE output"
+    check(o_n, None, q, k, v, causal, dt)
+
+
 def test_fwd_deterministic(gpu):
     q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
     o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
@@ -249,6 +269,14 @@ def test_fwd_full_size(gpu, name, p_bf16):
     else:
         qf, kf, vf = (x[n].cpu() for n in ("q", "k", "v"))
     del x
+    if cfg.dtype in ("bf16", "f16"):
+        # the same call without an LSE output (the kernel then skips the
+        # unrounded row sum) must give the same O, bit for bit
+        o_n = torch.full_like(o, float("nan"))
+        gpu.fa_fwd(qf.cuda(), kf.cuda(), vf.cuda(), o_n, None, causal=cfg.causal, softmax_scale=cfg.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o_n, o), f"{name}: O differs between the calls with and without an LSE output"
+        del o_n
     ro, rl = oracle.attention_fp64(qf, kf, vf, cfg.causal, cfg.scale)
     og = o.double().cpu().numpy()
     lg = lse.double().cpu().numpy()

@@ -406,7 +406,7 @@ void fwd_mfma_kernel(const FwdArgs a) {
 // soft_exp2 on the FMA pipe, the FlashAttention-4 card's split between the
 // exponential unit and the FMA units; off by default (on this part the
 // transcendental shares the vector issue with the FMAs).
-template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false>
+template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false, bool WLSE = true>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(FA16_WAVES_PER_EU)))
 void fwd_mfma16_kernel(const FwdArgs a) {
   using C = Cfg16<T, D, NT>;
@@ -624,7 +624,9 @@ void fwd_mfma16_kernel(const FwdArgs a) {
       pw[st] = pack2(s[1][2 * (st - 8)], s[1][2 * (st - 8) + 1]);
       pin(pw[st]);
       lr_run = add_rounded(pw[st], lr_run);
-      if constexpr (st < 12) {
+      if constexpr (!WLSE) {
+        // no LSE output: O needs only the rounded sum
+      } else if constexpr (st < 12) {
         constexpr int mb = (st - 8) >> 1, base = 4 * ((st - 8) & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -858,16 +860,16 @@ void fwd_mfma16_kernel(const FwdArgs a) {
       if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + c * EPC) = v;
     }
   }
-  if (row < a.Sq && a.lse != nullptr && h == 0)
+  if (WLSE && row < a.Sq && a.lse != nullptr && h == 0)
     a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
 }
 
-template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false>
+template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false, bool WLSE = true>
 int launch_one(const FwdArgs &args, hipStream_t stream) {
   void (*kern)(FwdArgs);
   int lds_bytes;
   if constexpr (sizeof(T) == 2) {
-    kern = fwd_mfma16_kernel<T, D, CAUSAL, NT, SEXP>;
+    kern = fwd_mfma16_kernel<T, D, CAUSAL, NT, SEXP, WLSE>;
     lds_bytes = Cfg16<T, D, NT>::LDS_BYTES;
   } else {
     kern = fwd_mfma_kernel<T, D, CAUSAL>;
@@ -875,9 +877,10 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
   }
   const unsigned grid = static_cast<unsigned>(args.nq) * args.B * args.Hq;
   fa_log_launch(sizeof(T) == 2 ? "fwd_mfma16_kernel" : "fwd_mfma_kernel", grid, NT, lds_bytes,
-                "dtype=%s d=%d causal=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d soft_exp2=%d",
+                "dtype=%s d=%d causal=%d B=%d Hq=%d G=%d Sq=%d Sk=%d rows_per_wg=%d soft_exp2=%d lse_sum=%d",
                 sizeof(T) == 4 ? "f32" : (std::is_same<T, __bf16>::value ? "bf16" : "f16"), D, CAUSAL ? 1 : 0,
-                args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR, SEXP ? 1 : 0);
+                args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR, SEXP ? 1 : 0,
+                WLSE ? 1 : 0);
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -896,10 +899,17 @@ template <typename T, int D, int NT> int launch_causal(const FwdArgs &args, bool
   return causal ? launch_one<T, D, true, NT>(args, s) : launch_one<T, D, false, NT>(args, s);
 }
 
+// Without an LSE output (args.lse null) the d = 128 kernel drops the row sum
+// of the unrounded probabilities: O is divided by the sum of the rounded ones,
+// which it keeps either way.
 template <typename T, int NT> int launch_dtype(const FwdArgs &args, int d, bool causal, bool sexp, hipStream_t s) {
   if (sexp)  // validated: 16-bit inputs with d = 128
     return causal ? launch_one<T, 128, true, NT, true>(args, s) : launch_one<T, 128, false, NT, true>(args, s);
-  return d == 64 ? launch_causal<T, 64, NT>(args, causal, s) : launch_causal<T, 128, NT>(args, causal, s);
+  if (d == 64) return launch_causal<T, 64, NT>(args, causal, s);
+  if (args.lse == nullptr)
+    return causal ? launch_one<T, 128, true, NT, false, false>(args, s)
+                  : launch_one<T, 128, false, NT, false, false>(args, s);
+  return launch_causal<T, 128, NT>(args, causal, s);
 }
 
 }  // namespace fa
