@@ -144,7 +144,7 @@ def launches_per_call(cfg) -> int:
 
 def workload(name):
     for table in (fa_inputs.CONFIGS, fa_inputs.BWD_CONFIGS, fa_inputs.KV_CONFIGS, fa_inputs.FP8_VARIANT_CONFIGS,
-                  fa_inputs.SOFT_EXP2_CONFIGS, fa_inputs.NO_LSE_CONFIGS):
+                  fa_inputs.SOFT_EXP2_CONFIGS, fa_inputs.NO_LSE_CONFIGS, fa_inputs.BWD_VARIANT_CONFIGS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -399,9 +399,11 @@ def _bwd_runner(cfg, seed=0):
     fa.fa_fwd(q, k, v, o, lse, causal=cfg.causal, softmax_scale=cfg.scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.fa_bwd_workspace_size(cfg.B, cfg.Hq, cfg.Sq), dtype=torch.uint8, device="cuda")
+    pingpong = isinstance(cfg, fa_inputs.PingPongBwdConfig)
 
     def run():
-        fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=cfg.causal, softmax_scale=cfg.scale, workspace=ws)
+        fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=cfg.causal, softmax_scale=cfg.scale, workspace=ws,
+                  wave_pingpong=pingpong)
 
     return Runner(run)
 
@@ -932,7 +934,7 @@ def main():
     extras = {}
     names = [n for n in list(fa_inputs.CONFIGS) + list(fa_inputs.BWD_CONFIGS) + list(fa_inputs.KV_CONFIGS)
              + list(fa_inputs.FP8_VARIANT_CONFIGS) + list(fa_inputs.SOFT_EXP2_CONFIGS)
-             + list(fa_inputs.NO_LSE_CONFIGS) if n != a.workload]
+             + list(fa_inputs.NO_LSE_CONFIGS) + list(fa_inputs.BWD_VARIANT_CONFIGS) if n != a.workload]
     if a.extra == "none":
         names = []
     elif a.extra != "all":

@@ -172,6 +172,19 @@ SOFT_EXP2_CONFIGS = {
         "softexp2_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True, outlier_frac=0.01),
 }
 
+@dataclass(frozen=True)
+class PingPongBwdConfig(BwdConfig):
+    """A backward workload run with the dK/dV kernel's two-role wave schedule
+    (fa_bwd_params.wave_pingpong = 1); same inputs as BwdConfig."""
+
+
+# The long-context backward with the two-role schedule.
+BWD_VARIANT_CONFIGS = {
+    "bwd_pingpong_bf16_gqa32x8_s16384_causal_outlier": PingPongBwdConfig(
+        "bwd_pingpong_bf16_gqa32x8_s16384_causal_outlier", "bf16", 1, 32, 8, 16384, 16384, 128, True,
+        outlier_frac=0.01),
+}
+
 # The long-context workload called without an LSE output (the workload as
 # specified names only O; the kernel then skips the unrounded row sum).
 NO_LSE_CONFIGS = {

@@ -183,6 +183,17 @@ typedef struct {
   int32_t causal;
   void *workspace;
   size_t workspace_bytes;
+  /* 0 or 1: the dK/dV kernel's wave-specialised schedule (FlashAttention-3
+   * page, "Hopper asynchrony" section: one group of warps runs its softmax
+   * while another runs its matrix products).  The two wavefronts of each SIMD
+   * take two roles, the second running the same per-tile phases (S and dP
+   * products, softmax gradient, dV and dK products) two phases behind the
+   * first, three barriers per tile, so that in two of every three phases one
+   * of them issues matrix work while the other does vector work.  Same
+   * results, bit for bit; measured slower on this part (the per-tile vector
+   * work is too short to fill the matrix phases, and the extra barriers
+   * cost more than the overlap gains), kept for the comparison. */
+  int32_t wave_pingpong;
 } fa_bwd_params;
 
 /* Bytes of workspace fa_bwd needs (0 on invalid sizes). */

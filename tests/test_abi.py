@@ -292,6 +292,15 @@ def test_bwd_validator_errors(lib, mutate, status):
     assert fa.fa_check_bwd_params(p) == status
 
 
+def test_bwd_wave_pingpong_validation(lib):
+    p = good_bwd()
+    p.wave_pingpong = 1
+    assert fa.fa_check_bwd_params(p) == fa.FA_OK
+    p.wave_pingpong = 2
+    assert fa.fa_check_bwd_params(p) == fa.FA_ERR_INVALID_ARG
+    assert "wave_pingpong" in fa.fa_last_error()
+
+
 def good_quant():
     p = fa.FaFp8QuantParams()
     p.x, p.codes, p.scales, p.signs = 0x10000, 0x20000, 0x30000, 0

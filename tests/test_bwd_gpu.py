@@ -97,6 +97,44 @@ def test_bwd_deterministic_and_gqa_sums(gpu):
         assert float((grouped.float() - summed).abs().max()) <= 2e-2 * float(summed.abs().max())
 
 
+PINGPONG_CASES = [
+    # dtype, B, Hq, Hkv, Sq, Sk, causal
+    ("bf16", 1, 2, 2, 64, 64, True),
+    ("bf16", 2, 4, 2, 200, 200, True),
+    ("bf16", 1, 4, 1, 130, 300, True),
+    ("bf16", 1, 2, 2, 300, 130, True),
+    ("bf16", 2, 2, 1, 257, 129, False),
+    ("fp16", 1, 8, 2, 100, 333, False),
+    ("bf16", 1, 4, 2, 1024, 1024, True),
+    ("bf16", 1, 2, 1, 1000, 1100, False),
+]
+
+
+@pytest.mark.parametrize("dt,B,Hq,Hkv,Sq,Sk,causal", PINGPONG_CASES)
+def test_bwd_wave_pingpong_bitwise(gpu, dt, B, Hq, Hkv, Sq, Sk, causal):
+    # the two-role dK/dV schedule runs the same tiles in the same order in each
+    # wave, so all three gradients equal the default schedule's bit for bit
+    cfg = fa_inputs.FwdConfig("t", dt if dt == "bf16" else "f16", B, Hq, Hkv, Sq, Sk, 128, causal)
+    xc = fa_inputs.make_fwd_inputs(cfg, seed=Sq + 3 * Sk)
+    dout = _dout((B, Hq, Sq, 128), Sq + Sk, xc["q"].dtype).cuda()
+    x = {n: xc[n].cuda() for n in ("q", "k", "v")}
+    ref = run_bwd(gpu, x, dout, causal)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device="cuda")
+    gpu.fa_fwd(x["q"], x["k"], x["v"], o, lse, causal=causal)
+    got = [torch.full_like(t, float("nan")) for t in ref]
+    print(f"fa_bwd wave_pingpong q={(B, Hq, Sq)} k={(Hkv, Sk)} causal={causal} {dt}", flush=True)
+    gpu.fa_bwd(x["q"], x["k"], x["v"], o, dout, lse, *got, causal=causal, wave_pingpong=True)
+    torch.cuda.synchronize()
+    for name, u, w in zip(("dQ", "dK", "dV"), ref, got):
+        assert torch.equal(u.view(torch.int16), w.view(torch.int16)), name
+    if Sq * Sk <= 300 * 300:
+        rq, rk, rv = oracle.attention_bwd_fp64(xc["q"], xc["k"], xc["v"], dout.cpu(), causal)
+        check(got[0], rq, "dQ")
+        check(got[1], rk, "dK")
+        check(got[2], rv, "dV")
+
+
 def test_bwd_strided_bshd(gpu):
     # token-major [B, S, H, d] buffers viewed as BHSD, for inputs and gradients
     B, S, H = 1, 96, 2

@@ -104,6 +104,7 @@ class FaBwdParams(ctypes.Structure):
         ("lse_strides", I64x2),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("wave_pingpong", ctypes.c_int32),
     ]
 
 
@@ -415,9 +416,10 @@ def fa_fp8_quantize(x, codes, scales, signs=None, stream=None) -> None:
 
 
 def bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=None,
-               workspace=None) -> FaBwdParams:
+               workspace=None, wave_pingpong=False) -> FaBwdParams:
     """fa_bwd_params for q/o/dout/dq [B,Hq,Sq,d], k/v/dk/dv [B,Hkv,Sk,d] and
-    lse [B,Hq,Sq] float32 (any strides with a unit head-dim stride)."""
+    lse [B,Hq,Sq] float32 (any strides with a unit head-dim stride);
+    wave_pingpong selects the dK/dV kernel's wave-specialised schedule."""
     import torch
 
     _dims("q", q, 4)
@@ -449,18 +451,19 @@ def bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=No
     p.causal = 1 if causal else 0
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.wave_pingpong = 1 if wave_pingpong else 0
     return p
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal=False, softmax_scale=None, workspace=None,
-           stream=None) -> None:
+           stream=None, wave_pingpong=False) -> None:
     """Enqueue the backward (dq, dk, dv from dout, o and the forward's lse)."""
     import torch
 
     if workspace is None:
         workspace = torch.empty(fa_bwd_workspace_size(q.shape[0], q.shape[1], q.shape[2]),
                                 dtype=torch.uint8, device=q.device)
-    p = bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal, softmax_scale, workspace)
+    p = bwd_params(q, k, v, o, dout, lse, dq, dk, dv, causal, softmax_scale, workspace, wave_pingpong)
     st = load().fa_bwd(ctypes.byref(p), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd", fa_last_error())

@@ -33,6 +33,14 @@
 //   * The causal and ragged-edge masks are applied only on the tiles that
 //     need them (a wave-uniform branch); every other tile runs the plain
 //     exponential.  dP's accumulator starts at -Dr, so dS is one multiply.
+//   * Optional two-role schedule for bwd_dkdv_kernel (the wave specialisation
+//     of the FlashAttention-3 page's asynchrony section, on LDS barriers):
+//     waves 0-3 run a tile's score phase while waves 4-7 run the previous
+//     tile's accumulation phase, three barriers per tile.  Each wave still
+//     takes every tile in the same order, so results equal the default
+//     schedule's bit for bit.  On gfx950 it measured slower (the two roles
+//     share each SIMD's issue slots, and the extra barriers cost more than the
+//     overlap gains); it is kept selectable for that comparison.
 // All products are 32x32x16 MFMAs on the input type with fp32 accumulation; P
 // and dS are rounded to the input type only as MFMA operands.  Scores stay in
 // the log2 domain (tau * log2 e folded into one multiply, hardware exp2).
@@ -195,7 +203,7 @@ constexpr int kDkdvWaves = 8;
 constexpr int kDkdvKeys = 32 * kDkdvWaves;
 constexpr int kVRow = kBD + kEPC;  // V row in LDS, +16 bytes: 68 dwords, so 16 rows start on 16 bank quads
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool PP>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   using M = BwdMfma<T>;
@@ -302,83 +310,143 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int arow = row_off(perm_row(l32)) + 128 * h;        // row operands: tile row perm_row(l32)
   const int trl = tr_lane(lane);
   const bool key_ok = kw0 + 32 <= a.Sk;  // wave-uniform
-  int ct = 0;  // tile of the current item
-  for (int w = 0; w < n_items; ++w) {
+  // The three phases of query tile w: A forms S and dP - Dr (MFMA), B the
+  // probabilities and dS (vector work), C dV^T += dO^T P and dK^T += Q^T dS
+  // (MFMA).  Their results pass between phases in registers.
+  f32x16 s, dp;
+  frag pf[2], dsf[2];
+  auto phase_a = [&](int w) {
+    // S = Q K^T and dP - Dr = dO V^T - Dr, rows = queries (accumulator
+    // order), columns = keys
+    const int st = w & 1;
+    const float *nd = sND[st] + 8 * h;
+    const f32x4 n0 = *reinterpret_cast<const f32x4 *>(nd), n1 = *reinterpret_cast<const f32x4 *>(nd + 4);
+    const f32x4 n2 = *reinterpret_cast<const f32x4 *>(nd + 16), n3 = *reinterpret_cast<const f32x4 *>(nd + 20);
+    dp = f32x16{n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+    s = f32x16{};
+    const char *qr = sQ[st] + arow;
+    const char *dr = sDO[st] + arow;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s = M::mma(lds_frag<T>(qr + 16 * c), kf[c], s);
+      dp = M::mma(lds_frag<T>(dr + 16 * c), lds_frag<T>(reinterpret_cast<const char *>(vrow + 8 * c)), dp);
+    }
+  };
+  int ct = 0;  // tile of the item phase B runs next (every wavefront runs B in item order)
+  auto phase_b = [&](int w) {
+    // P and dS, as B operands over query steps of 16
     const int st = w & 1;
     const int i0 = (t_first + ct) * kTR;
     ct = ct + 1 == ntl ? 0 : ct + 1;
-    {
-      // S = Q K^T and dP - Dr = dO V^T - Dr, rows = queries (accumulator
-      // order), columns = keys
-      f32x16 s, dp;
-      {
-        const float *nd = sND[st] + 8 * h;
-        const f32x4 n0 = *reinterpret_cast<const f32x4 *>(nd), n1 = *reinterpret_cast<const f32x4 *>(nd + 4);
-        const f32x4 n2 = *reinterpret_cast<const f32x4 *>(nd + 16), n3 = *reinterpret_cast<const f32x4 *>(nd + 20);
-        dp = f32x16{n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
-                    n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-      }
-      s = f32x16{};
-      const char *qr = sQ[st] + arow;
-      const char *dr = sDO[st] + arow;
+    auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        s = M::mma(lds_frag<T>(qr + 16 * c), kf[c], s);
-        dp = M::mma(lds_frag<T>(dr + 16 * c), lds_frag<T>(reinterpret_cast<const char *>(vrow + 8 * c)), dp);
-      }
-      // P and dS, as B operands over query steps of 16
-      frag pf[2], dsf[2];
-      auto softmax_grad = [&](auto masked) {
+      for (int half = 0; half < 2; ++half) {
+        const int r0 = 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
+        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL[st] + r0);
+        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL[st] + r0 + 4);
+        unsigned pw[4], dw[4];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r0 = 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
-          const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL[st] + r0);
-          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL[st] + r0 + 4);
-          unsigned pw[4], dw[4];
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float pv[2], dsv[2];
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            float pv[2], dsv[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int e = 2 * e2 + u;
-              const int ireg = 8 * half + e;
-              const float l2 = e < 4 ? l0[e] : l1[e - 4];
-              float p = fast_exp2(s[ireg] * a.c - l2);
-              if constexpr (decltype(masked)::value) {
-                bool vis = key < a.Sk;
-                if (CAUSAL) vis = vis && key <= i0 + r0 + e + coff;
-                p = vis ? p : 0.f;
-              }
-              pv[u] = p;
-              dsv[u] = p * dp[ireg];
+          for (int u = 0; u < 2; ++u) {
+            const int e = 2 * e2 + u;
+            const int ireg = 8 * half + e;
+            const float l2 = e < 4 ? l0[e] : l1[e - 4];
+            float p = fast_exp2(s[ireg] * a.c - l2);
+            if constexpr (decltype(masked)::value) {
+              bool vis = key < a.Sk;
+              if (CAUSAL) vis = vis && key <= i0 + r0 + e + coff;
+              p = vis ? p : 0.f;
             }
-            pw[e2] = pack2<T>(pv[0], pv[1]);
-            dw[e2] = pack2<T>(dsv[0], dsv[1]);
+            pv[u] = p;
+            dsv[u] = p * dp[ireg];
           }
-          pf[half] = __builtin_bit_cast(frag, u32x4{pw[0], pw[1], pw[2], pw[3]});
-          dsf[half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
+          pw[e2] = pack2<T>(pv[0], pv[1]);
+          dw[e2] = pack2<T>(dsv[0], dsv[1]);
         }
-      };
-      // the mask matters only on tiles that reach past the diagonal or Sk
-      if (key_ok && (!CAUSAL || kw0 + 31 <= i0 + coff))
-        softmax_grad(std::false_type{});
-      else
-        softmax_grad(std::true_type{});
-      // dV^T += dO^T P, dK^T += Q^T dS: rows = head dims, columns = keys
-      const char *dot = sDO[st] + trl;
-      const char *qt = sQ[st] + trl;
+        pf[half] = __builtin_bit_cast(frag, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        dsf[half] = __builtin_bit_cast(frag, u32x4{dw[0], dw[1], dw[2], dw[3]});
+      }
+    };
+    // the mask matters only on tiles that reach past the diagonal or Sk
+    if (key_ok && (!CAUSAL || kw0 + 31 <= i0 + coff))
+      softmax_grad(std::false_type{});
+    else
+      softmax_grad(std::true_type{});
+  };
+  auto phase_c = [&](int w) {
+    // dV^T += dO^T P, dK^T += Q^T dS: rows = head dims, columns = keys
+    const int st = w & 1;
+    const char *dot = sDO[st] + trl;
+    const char *qt = sQ[st] + trl;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          dv[db] = M::mma(tr_frag<T>(dot, t, db), pf[t], dv[db]);
-          dk[db] = M::mma(tr_frag<T>(qt, t, db), dsf[t], dk[db]);
-        }
+      for (int t = 0; t < 2; ++t) {
+        dv[db] = M::mma(tr_frag<T>(dot, t, db), pf[t], dv[db]);
+        dk[db] = M::mma(tr_frag<T>(qt, t, db), dsf[t], dk[db]);
       }
     }
-    if (w + 1 < n_items) store_item(st ^ 1);  // that stage was last read by tile w - 1
+  };
+  // tile w + 1 into the stage tile w - 1 left; tile w + 2 into registers
+  auto stage_next = [&](int w) {
+    if (w + 1 < n_items) store_item((w + 1) & 1);
     if (w + 2 < n_items) load_next();
-    __syncthreads();
+  };
+  if constexpr (!PP) {
+    for (int w = 0; w < n_items; ++w) {
+      phase_a(w);
+      phase_b(w);
+      phase_c(w);
+      stage_next(w);
+      __syncthreads();
+    }
+  } else {
+    // Wave-specialised schedule.  Round r has three slots, each ended by a
+    // workgroup barrier.  Wavefronts 0-3 (one per SIMD) run A(r), B(r), C(r)
+    // in them; wavefronts 4-7 run the same phases two slots later (B(r-1),
+    // C(r-1), A(r)), so in the first two slots one wavefront of each SIMD
+    // issues MFMAs while the other does vector work.  In the third slot every
+    // thread stores tile r + 1 into the stage tile r - 1 left (its last
+    // reader, C(r-1) of wavefronts 4-7, ended in slot two) and fetches tile
+    // r + 2.  The roles run separate loops with the same barrier count, so
+    // each keeps only its own phase results live.
+    if (wave < kDkdvWaves / 2) {
+      for (int r = 0; r < n_items; ++r) {
+        phase_a(r);
+        __syncthreads();
+        phase_b(r);
+        __syncthreads();
+        phase_c(r);
+        stage_next(r);
+        __syncthreads();
+      }
+      // the other role's last round
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    } else {
+      __syncthreads();
+      __syncthreads();
+      if (n_items > 0) {
+        phase_a(0);
+        stage_next(0);
+      }
+      __syncthreads();
+      for (int r = 1; r <= n_items; ++r) {
+        phase_b(r - 1);
+        __syncthreads();
+        phase_c(r - 1);
+        __syncthreads();
+        if (r < n_items) {
+          phase_a(r);
+          stage_next(r);
+        }
+        __syncthreads();
+      }
+    }
   }
 
   // ---- write dK = tau dK^T^T and dV: lane's key, dims 32 db + 8 m + 4 h .. +3 ----
@@ -543,7 +611,7 @@ void bwd_dq_kernel(const BwdArgs a) {
 }
 
 template <typename T>
-int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
+int launch_bwd_typed(const BwdArgs &a, bool causal, bool pingpong, hipStream_t s) {
   const long long rows = static_cast<long long>(a.B) * a.Hq * a.Sq;
   const char *dt = std::is_same<T, __bf16>::value ? "bf16" : "f16";
   if (rows > 0) {
@@ -553,17 +621,29 @@ int launch_bwd_typed(const BwdArgs &a, bool causal, hipStream_t s) {
   const unsigned g_kv = static_cast<unsigned>((a.Sk + kDkdvKeys - 1) / kDkdvKeys) * a.B * a.Hkv;
   const unsigned g_q = static_cast<unsigned>((a.Sq + 127) / 128) * a.B * a.Hq;
   if (g_kv)
-    fa_log_launch("bwd_dkdv_kernel", g_kv, 512, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
-                  causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
+    fa_log_launch("bwd_dkdv_kernel", g_kv, 512, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d pingpong=%d",
+                  dt, causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, pingpong ? 1 : 0);
   if (g_q)
     fa_log_launch("bwd_dq_kernel", g_q, 256, 0, "dtype=%s causal=%d B=%d Hq=%d Hkv=%d Sq=%d Sk=%d", dt,
                   causal ? 1 : 0, a.B, a.Hq, a.Hkv, a.Sq, a.Sk);
-  if (causal) {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, true>), dim3(g_kv), dim3(512), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(g_q), dim3(256), 0, s, a);
-  } else {
-    if (g_kv) hipLaunchKernelGGL((bwd_dkdv_kernel<T, false>), dim3(g_kv), dim3(512), 0, s, a);
-    if (g_q) hipLaunchKernelGGL((bwd_dq_kernel<T, false>), dim3(g_q), dim3(256), 0, s, a);
+  if (g_kv) {
+    if (causal) {
+      if (pingpong)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, true>), dim3(g_kv), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, true, false>), dim3(g_kv), dim3(512), 0, s, a);
+    } else {
+      if (pingpong)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, false, true>), dim3(g_kv), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, false, false>), dim3(g_kv), dim3(512), 0, s, a);
+    }
+  }
+  if (g_q) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, true>), dim3(g_q), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, false>), dim3(g_q), dim3(256), 0, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -628,6 +708,6 @@ int fa_launch_bwd(const fa_bwd_params *p, void *stream) {
   a.scale = p->softmax_scale;
   a.c = p->softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->dtype == FA_BF16) return launch_bwd_typed<__bf16>(a, p->causal != 0, s);
-  return launch_bwd_typed<_Float16>(a, p->causal != 0, s);
+  if (p->dtype == FA_BF16) return launch_bwd_typed<__bf16>(a, p->causal != 0, p->wave_pingpong != 0, s);
+  return launch_bwd_typed<_Float16>(a, p->causal != 0, p->wave_pingpong != 0, s);
 }

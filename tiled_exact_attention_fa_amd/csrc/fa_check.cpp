@@ -269,6 +269,8 @@ extern "C" int fa_check_bwd_params(const fa_bwd_params *p) {
     return fa_set_error(FA_ERR_UNSUPPORTED, "backward dtype %d not supported (bf16 or fp16)", p->dtype);
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f))
     return fa_set_error(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->wave_pingpong != 0 && p->wave_pingpong != 1)
+    return fa_set_error(FA_ERR_INVALID_ARG, "wave_pingpong must be 0 or 1");
   if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return FA_OK;
   int st;
   if (p->Sq > 0) {
