@@ -386,7 +386,10 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
   // second half: exponents of s[1]; P^T packed to e4m3, four keys per word;
   // row sum of the unrounded probabilities as a balanced tree; l update
   float ps[16], qa[8];
-  int pw[16];  // P^T packed: 8 words of e4m3, or 16 of bf16 pairs
+  // P^T packed: 8 words of e4m3, or 16 of bf16 pairs.  An e4m3 word is
+  // written a half at a time; its first half goes over the word's previous
+  // tile (dead once that tile's P V has issued), so no zeroing is needed.
+  int pw[16] = {};
   auto pack_bf16 = [](float x0, float x1) {
     typedef __bf16 v2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(int, v2{static_cast<__bf16>(x0), static_cast<__bf16>(x1)});
@@ -404,7 +407,7 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
         pw[st] = pack_bf16(s[0][2 * st], s[0][2 * st + 1]);
         pin(pw[st]);
       } else if constexpr (st < 4) {
-        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st], s[0][4 * st + 1], 0, false);
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st], s[0][4 * st + 1], pw[st], false);
         pw[st] = __builtin_amdgcn_cvt_pk_fp8_f32(s[0][4 * st + 2], s[0][4 * st + 3], w, true);
         pin(pw[st]);
       }
@@ -416,7 +419,7 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
       if constexpr (st < 12) {
         constexpr int q = st - 8;
         if constexpr (!PB16) {
-          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], 0, false);
+          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q], s[1][4 * q + 1], pw[4 + q], false);
           pw[4 + q] = __builtin_amdgcn_cvt_pk_fp8_f32(s[1][4 * q + 2], s[1][4 * q + 3], w, true);
           pin(pw[4 + q]);
         }
