@@ -62,6 +62,8 @@ CASES = [
     ("fp16", 2, 4, 4, 192, 192, True),
     ("fp16", 1, 8, 2, 100, 333, False),
     ("bf16", 1, 2, 2, 1024, 1024, True),   # several 128-row / 128-key blocks
+    ("bf16", 1, 16, 2, 200, 200, True),    # 8 query heads per K/V head
+    ("fp16", 1, 16, 1, 150, 290, False),   # 16 query heads sharing one K/V head
 ]
 
 

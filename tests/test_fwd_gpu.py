@@ -145,6 +145,35 @@ def test_fwd_without_lse_output(gpu, dt, causal, shape):
     check(o_n, None, q, k, v, causal, dt)
 
 
+MORE_CASES = [
+    # name, B, Hq, Hkv, Sq, Sk, factor on Q and K, softmax scale (None: 1/sqrt(d))
+    ("group8", 1, 16, 2, 300, 300, 1.0, None),
+    ("group16", 2, 32, 2, 200, 200, 1.0, None),
+    ("mqa32", 1, 32, 1, 260, 260, 1.0, None),
+    ("short_q_long_k", 1, 4, 2, 64, 4100, 1.0, None),     # 65 key tiles, one partial
+    ("long_q_short_k", 1, 2, 1, 1100, 70, 1.0, None),     # causal: 1030 rows see no key
+    ("peaked", 1, 4, 2, 300, 300, 4.0, None),             # scores span about +-64: one-hot rows, lazy max moves
+    ("flat", 1, 4, 2, 300, 300, 1.0, 0.01),               # nearly uniform rows
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", MORE_CASES, ids=lambda c: c[0])
+def test_fwd_groups_lengths_and_score_ranges(gpu, dt, causal, case):
+    """Wider query groups (8, 16, 32 query heads per K/V head), a short query
+    block against many key tiles and the reverse, and score distributions at
+    both ends: strongly peaked rows (the running max moves by large steps, and
+    O is close to a single V row) and nearly uniform ones."""
+    name, B, Hq, Hkv, Sq, Sk, f, scale = case
+    q, k, v = make(B, Hq, Hkv, Sq, Sk, 128, dt, seed=Sq + Sk + Hq)
+    if f != 1.0:
+        q = (q.float() * f).to(q.dtype)
+        k = (k.float() * f).to(k.dtype)
+    o, lse = run_fwd(gpu, q, k, v, causal, TDT[dt], scale)
+    check(o, lse, q, k, v, causal, dt, scale)
+
+
 def test_fwd_deterministic(gpu):
     q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
     o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
