@@ -86,8 +86,9 @@ SHAPES = [
     (2, 2, 2, 100, 260),   # Sq < Sk
     (1, 2, 2, 260, 100),   # Sq > Sk: causal leaves leading rows empty
     # 136 (batch, head) pairs: 17 per XCD, so the causal issue order of short
-    # heads cuts them into a group of 16 (four whole GQA groups) and a ragged
-    # group of one
+    # heads cuts each XCD's range into a group of 16 heads and a ragged group
+    # of one; 17 is not a multiple of G = 4, so on most XCDs the groups
+    # straddle K/V heads (a locality cost only: the mapping stays one-to-one)
     (2, 68, 17, 300, 300),
 ]
 

@@ -28,8 +28,12 @@ struct FwdArgs {
 // XCD's L2.  Within an XCD:
 //   * causal (tiles of unequal length): longest tiles first, so the short
 //     tiles fill the tail of the launch.  When a head has at most 8 query
-//     tiles, the range is cut into groups of heads (whole GQA groups, so the
-//     query heads of one K/V head stay together) whose tiles together about
+//     tiles, the range is cut into groups of heads (a multiple of G heads;
+//     they are whole GQA groups, the query heads of one K/V head kept
+//     together, when the heads per XCD are a multiple of G, as in every
+//     benchmarked shape; otherwise the XCD's range starts inside a GQA group
+//     and the groups straddle K/V heads, which costs locality, not
+//     correctness) whose tiles together about
 //     fill the XCD's 32 compute units once, and each group is issued longest
 //     first across its heads: a compute unit that drew a long tile then draws
 //     a short one, so the pairs even out as under one order over the whole
