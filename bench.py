@@ -211,6 +211,18 @@ def _cores():
     return len(os.sched_getaffinity(0))
 
 
+def _cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _fwd_oracle_check(cfg, x, o, lse, budget_s):
     """The oracle over whole (batch, head) pairs of a prefill workload, as many
     as fit the budget (whole passes repeated when the workload is smaller).
@@ -257,7 +269,8 @@ def _fwd_oracle_check(cfg, x, o, lse, budget_s):
     else:
         sample = f"{done / len(heads):.1f} passes over all {len(heads)} (batch, head) pairs"
     cpu = {"value": flops / elapsed / 1e9, "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
-           "sample": f"{sample} of {cfg.name}, float64 numpy two-pass, {elapsed:.1f} s wall"}
+           "sample": f"{sample} of {cfg.name}, float64 numpy two-pass, {elapsed:.1f} s wall",
+           "cpu_model": _cpu_model()}
     err = {"O": err_o, "LSE": err_l if lg is not None else None,
            "sample": f"{checked} of {len(heads)} (batch, head) pairs, every row"}
     return cpu, err
@@ -293,7 +306,7 @@ def _decode_oracle_check(cfg, x, o, lse, budget_s):
             break
     cpu = {"value": per_entry * done / elapsed / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
            "sample": f"{done} of {cfg.B} batch entries of {cfg.name} (all {cfg.Hq} heads each), float64 numpy, "
-                     f"{elapsed:.1f} s wall"}
+                     f"{elapsed:.1f} s wall", "cpu_model": _cpu_model()}
     err = {"O": err_o, "LSE": err_l, "sample": f"{done} of {cfg.B} batch entries, every head"}
     return cpu, err
 
@@ -494,9 +507,11 @@ def work_and_unit(cfg):
     return fwd_flops(cfg), "TFLOP/s"
 
 
-def measure(name, steps, warmup, check_budget=0.0):
+def measure(name, steps, warmup, check_budget=0.0, clock=False):
     """Times one workload; with check_budget > 0 and an oracle check for it,
-    also the CPU baseline and the max error on the oracle's sample."""
+    also the CPU baseline and the max error on the oracle's sample; with
+    clock, also the gfx clock and socket power observed while it runs (after
+    the timed region)."""
     cfg = workload(name)
     import torch
 
@@ -522,6 +537,8 @@ def measure(name, steps, warmup, check_budget=0.0):
             # the prefill target is stated against the bf16 peak for every input type
             res["frac_of_bf16_peak"] = tf / PEAK_BF16_TFLOPS
     res.update({"ms_per_call": ms, "ms_median": med, "ms_min": mn, "wall_s": wall})
+    if clock:
+        res["observed"] = observed_clock(r.run, ms)
     if check_budget > 0 and r.check is not None:
         res["cpu_baseline"], res["max_abs_err"] = r.check(check_budget)
     del r
@@ -804,6 +821,35 @@ def _smi_sample():
     return (float(pw.group(1)) if pw else None), (sum(clks) / len(clks) if clks else None)
 
 
+def observed_clock(run, ms_per_call, seconds=2.5, warm_s=0.5):
+    """Mean gfx clock (MHz) and socket power (W) of GPU 0 sampled with
+    amd-smi while `run` goes back to back for about `seconds`, after the timed
+    region and `warm_s` of unsampled calls (the board ramps up again after the
+    idle host work before it); None where amd-smi gives nothing."""
+    import threading
+
+    per = max(ms_per_call, 1e-3)
+    _time_region(run, max(1, int(warm_s * 1e3 / per)), 0)
+    calls = max(1, int(seconds * 1e3 / per))
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append(_smi_sample())
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    _time_region(run, calls, 0)
+    stop.set()
+    th.join()
+    pw = [p for p, _ in samples if p is not None]
+    ck = [c for _, c in samples if c is not None]
+    return {"gfx_clock_mhz": round(sum(ck) / len(ck), 1) if ck else None,
+            "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+            "samples": len(samples), "tool": "amd-smi metric -p -c, after the timed region and 0.5 s of warm calls"}
+
+
 def power_study(names, seconds=4.0):
     """For each workload (and the vendor bf16 GEMM, torch.matmul of 8192^3,
     as a reference for a plain contraction on this part): run it back to back
@@ -928,7 +974,7 @@ def main():
     fa.load()
     torch.cuda.set_device(0)
     cpu_on = not a.no_cpu_baseline
-    head = measure(a.workload, a.steps, a.warmup, check_budget=12.0 if cpu_on else 0.0)
+    head = measure(a.workload, a.steps, a.warmup, check_budget=12.0 if cpu_on else 0.0, clock=True)
     cfg = workload(a.workload)
 
     extras = {}
@@ -979,6 +1025,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "max_abs_err": head.get("max_abs_err"),
+        "observed": head.get("observed"),
         "workloads": extras,
         "device": torch.cuda.get_device_name(0),
     }

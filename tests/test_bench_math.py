@@ -70,3 +70,20 @@ def test_counter_digest_follows_each_kernel_family():
     assert fams["decode_fp8_b64_gqa32x8_L32768"] == "decode" and fams["append_fp8_b64_h8_t4096"] == "append"
     digests = {f: bench.source_digest(f) for f in bench.KERNEL_SOURCES}
     assert len(set(digests.values())) == len(digests)
+
+
+def test_variant_workloads_are_benchmarked_with_their_switch():
+    # the two-role backward runs the same work as the default backward
+    pp = fa_inputs.BWD_VARIANT_CONFIGS["bwd_pingpong_bf16_gqa32x8_s16384_causal_outlier"]
+    base = fa_inputs.BWD_CONFIGS["bwd_bf16_gqa32x8_s16384_causal_outlier"]
+    assert isinstance(pp, fa_inputs.PingPongBwdConfig) and bench.workload(pp.name) is pp
+    assert bench.bwd_flops(pp) == bench.bwd_flops(base) and bench.kernel_family(pp) == "bwd"
+
+
+def test_host_description_fields():
+    # the oracle baseline names the CPU it ran on (None only where /proc/cpuinfo has no model line)
+    m = bench._cpu_model()
+    assert m is None or (isinstance(m, str) and m)
+    # without a readable GPU the amd-smi sample is empty, never an exception
+    p, c = bench._smi_sample()
+    assert (p is None or p > 0) and (c is None or c > 0)

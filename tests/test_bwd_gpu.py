@@ -181,3 +181,44 @@ def test_bwd_full_size(gpu):
     rq, rk, rv = oracle.attention_bwd_fp64(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), dout.cpu(), True)
     errs = [check(dq, rq, "dQ"), check(dk, rk, "dK"), check(dv, rv, "dV")]
     print("full-size backward, every element: relative max errors dQ/dK/dV", errs, flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_bwd_long_context_full_size(gpu):
+    """The long-context GQA backward at full size (Q [1, 32, 16384, 128], K/V
+    [1, 8, 16384, 128], causal, 1 % outlier keys), with the inputs and launch
+    the benchmark times: every element of dQ for the four query heads of one
+    K/V head, and every element of that K/V head's dK and dV (the sum over
+    its four query heads), against the oracle; and the two-role dK/dV
+    schedule bit-identical to the default at this size."""
+    cfg = fa_inputs.BWD_CONFIGS["bwd_bf16_gqa32x8_s16384_causal_outlier"]
+    x = fa_inputs.make_bwd_inputs(cfg, seed=0, device="cuda")
+    q, k, v, dout = x["q"], x["k"], x["v"], x["dout"]
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Sq, dtype=torch.float32, device="cuda")
+    print("fa_fwd + fa_bwd, long-context GQA workload", flush=True)
+    gpu.fa_fwd(q, k, v, o, lse, causal=True)
+    got = [torch.full_like(t, float("nan")) for t in (q, k, v)]
+    gpu.fa_bwd(q, k, v, o, dout, lse, *got, causal=True)
+    pp = [torch.full_like(t, float("nan")) for t in (q, k, v)]
+    gpu.fa_bwd(q, k, v, o, dout, lse, *pp, causal=True, wave_pingpong=True)
+    torch.cuda.synchronize()
+    for name, u, w in zip(("dQ", "dK", "dV"), got, pp):
+        assert torch.equal(u.view(torch.int16), w.view(torch.int16)), f"two-role schedule differs in {name}"
+    G = cfg.Hq // cfg.Hkv
+    kvh = 5
+    heads = [(0, h) for h in range(G * kvh, G * kvh + G)]
+    qc, kc, vc, dc = (t.cpu() for t in (q, k, v, dout))
+    rq = rk = rv = None
+    for bh in heads:  # one head at a time: each holds several S x S float64 arrays
+        print(f"oracle backward, head {bh}", flush=True)
+        hq, hk, hv = oracle.attention_bwd_fp64(qc, kc, vc, dc, True, heads=[bh])
+        rq = hq if rq is None else rq + hq
+        rk = hk if rk is None else rk + hk
+        rv = hv if rv is None else rv + hv
+        del hq, hk, hv
+    h0, h1 = G * kvh, G * kvh + G
+    errs = [check(got[0][:, h0:h1], rq[:, h0:h1], "dQ"),
+            check(got[1][:, kvh:kvh + 1], rk[:, kvh:kvh + 1], "dK"),
+            check(got[2][:, kvh:kvh + 1], rv[:, kvh:kvh + 1], "dV")]
+    print("long-context backward, one K/V group, every element: relative max errors dQ/dK/dV", errs, flush=True)
