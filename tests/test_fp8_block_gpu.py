@@ -199,9 +199,10 @@ def test_variants_against_exact_on_outliers(gpu):
     assert chan["block+rotation"][0] < chan["block"][0]
 
 
-def test_quantise_then_forward_full_size_sampled(gpu):
+def test_quantise_then_forward_full_size(gpu):
     """The fp8 workload's shape (B=8, H=16, S=4096) quantised on the GPU with
-    block scales and rotation, then the block-descale forward; sampled heads
+    block scales and rotation, then the block-descale forward, as the
+    benchmark's block-scaled workload runs it: every element of O and LSE
     against the oracle on the dequantised codes."""
     cfg = fa_inputs.CONFIGS["fp8_b8_h16_s4096"]
     x = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16", out_dtype=""), seed=0, device="cuda")
@@ -214,14 +215,14 @@ def test_quantise_then_forward_full_size_sampled(gpu):
         gpu.fa_fp8_quantize(t, codes, sc, signs if n != "v" else None)
         out[n], out[n + "_bs"] = codes, sc
     o, lse = run_fp8(gpu, out, False)
-    for b, h in [(0, 0), (5, 11), (7, 15)]:
-        deq = {n: oracle.dequant_fp8_blocks_fp64(out[n][b:b + 1, h:h + 1].cpu().numpy(),
-                                                 out[n + "_bs"][b:b + 1, h:h + 1].cpu().numpy())
-               for n in ("q", "k", "v")}
-        rows = [0, 1, 2047, 4095]
-        ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], False, rows=rows)
-        assert float(np.max(np.abs(o[b, h, rows].double().cpu().numpy() - ro[0, 0]))) <= TOL_O
-        assert float(np.max(np.abs(lse[b, h, rows].double().cpu().numpy() - rl[0, 0]))) <= TOL_LSE
+    deq = {n: oracle.dequant_fp8_blocks_fp64(out[n].cpu().numpy(), out[n + "_bs"].cpu().numpy())
+           for n in ("q", "k", "v")}
+    print("oracle forward, every head", flush=True)
+    ro, rl = oracle.attention_fp64(deq["q"], deq["k"], deq["v"], False)
+    err_o = float(np.max(np.abs(o.double().cpu().numpy() - ro)))
+    err_l = float(np.max(np.abs(lse.double().cpu().numpy() - rl)))
+    print(f"block-scaled, rotated fp8 at full size, every element: max|dO|={err_o:.3g} max|dLSE|={err_l:.3g}")
+    assert err_o <= TOL_O and err_l <= TOL_LSE
 
 
 def test_block_descales_of_any_ratio(gpu):
