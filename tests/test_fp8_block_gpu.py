@@ -202,8 +202,10 @@ def test_variants_against_exact_on_outliers(gpu):
 def test_quantise_then_forward_full_size(gpu):
     """The fp8 workload's shape (B=8, H=16, S=4096) quantised on the GPU with
     block scales and rotation, then the block-descale forward, as the
-    benchmark's block-scaled workload runs it: every element of O and LSE
-    against the oracle on the dequantised codes."""
+    benchmark's block-scaled workload runs it: every code and scale of Q, K
+    and V bit-exact against the oracle's quantiser (the quantiser workload's
+    full size), and every element of O and LSE against the oracle on the
+    dequantised codes."""
     cfg = fa_inputs.CONFIGS["fp8_b8_h16_s4096"]
     x = fa_inputs.make_fwd_inputs(dataclasses.replace(cfg, dtype="bf16", out_dtype=""), seed=0, device="cuda")
     signs = _signs(7).cuda()
@@ -215,6 +217,12 @@ def test_quantise_then_forward_full_size(gpu):
         gpu.fa_fp8_quantize(t, codes, sc, signs if n != "v" else None)
         out[n], out[n + "_bs"] = codes, sc
     o, lse = run_fp8(gpu, out, False)
+    for n in ("q", "k", "v"):
+        print(f"oracle quantiser, {n}", flush=True)
+        rc, rs = oracle.quantize_fp8_blocks(x[n].cpu(), signs.cpu().numpy() if n != "v" else None)
+        assert np.array_equal(out[n + "_bs"].cpu().numpy().view(np.uint32), rs.view(np.uint32)), n
+        assert np.array_equal(out[n].cpu().numpy(), rc), n
+        del rc, rs
     deq = {n: oracle.dequant_fp8_blocks_fp64(out[n].cpu().numpy(), out[n + "_bs"].cpu().numpy())
            for n in ("q", "k", "v")}
     print("oracle forward, every head", flush=True)
