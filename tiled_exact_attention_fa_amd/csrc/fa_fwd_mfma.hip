@@ -881,14 +881,21 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
                 sizeof(T) == 4 ? "f32" : (std::is_same<T, __bf16>::value ? "bf16" : "f16"), D, CAUSAL ? 1 : 0,
                 args.B, args.Hq, args.G, args.Sq, args.Sk, sizeof(T) == 2 ? NT / 2 : Cfg<T, D>::BR, SEXP ? 1 : 0,
                 WLSE ? 1 : 0);
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  // the dynamic LDS limit is raised once per kernel and device, before the
+  // kernel's first launch there (a host-side call, no stream work)
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t attr_err[kMaxDevices] = {};
+  int dev = -1;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return fa_set_error(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(de));
+  if (dev < 0 || dev >= kMaxDevices) return fa_set_error(FA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::call_once(once[dev], [&] {
+    attr_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   });
-  if (attr_err != hipSuccess)
-    return fa_set_error(FA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
+  if (attr_err[dev] != hipSuccess)
+    return fa_set_error(FA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err[dev]));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds_bytes, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_error(FA_ERR_HIP, "launch: %s", hipGetErrorString(e));
