@@ -190,9 +190,10 @@ typedef struct {
    * products, softmax gradient, dV and dK products) two phases behind the
    * first, three barriers per tile, so that in two of every three phases one
    * of them issues matrix work while the other does vector work.  Same
-   * results, bit for bit; measured slower on this part (the per-tile vector
-   * work is too short to fill the matrix phases, and the extra barriers
-   * cost more than the overlap gains), kept for the comparison. */
+   * results, bit for bit; measured 3-10 % slower on this part (each phase
+   * slot lasts as long as the longer of its two roles' phases, and the
+   * extra barriers cost more than the overlap gains), kept for the
+   * comparison.  Any other value is refused with FA_ERR_INVALID_ARG. */
   int32_t wave_pingpong;
 } fa_bwd_params;
 
