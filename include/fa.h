@@ -38,9 +38,12 @@
  *
  * Conventions shared by every call.
  *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent).  The
- *     caller owns every buffer and the library allocates nothing.  The only
- *     state it keeps between calls is the per-thread message of fa_last_error(),
- *     so calls from several host threads are safe.
+ *     caller owns every buffer and the library allocates nothing.  Between
+ *     calls it keeps only host-side bookkeeping: the per-thread message of
+ *     fa_last_error(), a once-per-device flag for each kernel whose dynamic LDS
+ *     limit it has raised, and fa_decode_kvq_noalloc's scratch address per
+ *     device (both set up under a lock or once-flag), so calls from several
+ *     host threads are safe and no call's result depends on an earlier one.
  *   - With the environment variable FA_LOG set to a value other than "0", every
  *     kernel launch prints one line to stderr before it is enqueued: the
  *     kernel, its grid, block and LDS bytes, and the sizes it was chosen for.
@@ -85,7 +88,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
   FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head dim, dtype pair, size limit */
   FA_ERR_ALIGNMENT = -3,   /* pointer or stride breaks the 16-byte row alignment */
-  FA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  FA_ERR_WORKSPACE = -4,   /* workspace missing or too small (decode, backward), or a
+                              size beyond fa_decode_kvq_noalloc's fixed scratch */
   FA_ERR_HIP = -5          /* the HIP runtime rejected a launch */
 } fa_status;
 
