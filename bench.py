@@ -805,12 +805,22 @@ def summarize_memory(dirs: str, kernel: str, label: str):
 
 # ---- power and clock while a workload runs -----------------------------------
 
+def _under_profiler() -> bool:
+    """True when this process runs under rocprofv3, which sets these for the
+    program it profiles: amd-smi is not started then (a child process of a
+    profiled program would start with the profiler's library preloaded)."""
+    return "ROCPROFILER_LIBRARY_CTOR" in os.environ or "ROCPROF_OUTPUT_PATH" in os.environ
+
+
 def _smi_sample():
     """Socket power (W) and the mean of the 8 XCDs' gfx clocks (MHz), from one
-    `amd-smi metric -p -c` reading of GPU 0; (None, None) if unavailable."""
+    `amd-smi metric -p -c` reading of GPU 0, run as a child process; (None,
+    None) if unavailable or under a profiler."""
     import re
     import subprocess
 
+    if _under_profiler():
+        return None, None
     try:
         out = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True, text=True,
                              timeout=10).stdout
@@ -828,6 +838,9 @@ def observed_clock(run, ms_per_call, seconds=2.5, warm_s=0.5):
     idle host work before it); None where amd-smi gives nothing."""
     import threading
 
+    if _under_profiler():
+        return {"gfx_clock_mhz": None, "socket_power_w": None, "samples": 0,
+                "tool": "not sampled: running under a profiler"}
     per = max(ms_per_call, 1e-3)
     _time_region(run, max(1, int(warm_s * 1e3 / per)), 0)
     calls = max(1, int(seconds * 1e3 / per))

@@ -87,3 +87,12 @@ def test_host_description_fields():
     # without a readable GPU the amd-smi sample is empty, never an exception
     p, c = bench._smi_sample()
     assert (p is None or p > 0) and (c is None or c > 0)
+
+
+def test_no_amd_smi_under_a_profiler(monkeypatch):
+    # a profiled program must not start amd-smi (its child would carry the profiler's preload)
+    monkeypatch.setenv("ROCPROFILER_LIBRARY_CTOR", "1")
+    assert bench._under_profiler()
+    assert bench._smi_sample() == (None, None)
+    obs = bench.observed_clock(lambda: None, 1.0)
+    assert obs["gfx_clock_mhz"] is None and obs["samples"] == 0
