@@ -863,6 +863,55 @@ def observed_clock(run, ms_per_call, seconds=2.5, warm_s=0.5):
             "samples": len(samples), "tool": "amd-smi metric -p -c, after the timed region and 0.5 s of warm calls"}
 
 
+def sweep(steps=10, warmup=3):
+    """Rates over shapes beyond the named workloads (no oracle check): prefill
+    bf16 at d = 128 over sequence lengths (MHA, B * S = 32768 tokens, causal and
+    not; GQA 32/8 up to S = 65536), d = 64, fp16 and fp8; the backward; int8-KV
+    decode over cache lengths (B = 64, GQA 32/8, 2048-token splits, at most 64).
+    Prints one markdown row per shape."""
+    import torch
+
+    F = fa_inputs.FwdConfig
+    rows = []
+    for causal in (True, False):
+        for S in (512, 1024, 2048, 4096, 8192, 16384, 32768):
+            B = max(1, 32768 // S)
+            rows.append(F(f"bf16 MHA", "bf16", B, 16, 16, S, S, 128, causal))
+    for S in (4096, 16384, 65536):
+        rows.append(F("bf16 GQA 32/8", "bf16", 1, 32, 8, S, S, 128, True))
+    for S in (2048, 8192):
+        rows.append(F("bf16 MHA d=64", "bf16", 32768 // S, 16, 16, S, S, 64, True))
+    rows.append(F("fp16 MHA", "f16", 16, 16, 16, 2048, 2048, 128, True))
+    for S, causal in ((1024, False), (4096, False), (16384, False), (4096, True)):
+        rows.append(F("fp8 MHA", "fp8", max(1, 32768 // S), 16, 16, S, S, 128, causal, out_dtype="bf16"))
+    for S in (2048, 8192, 16384):
+        rows.append(fa_inputs.BwdConfig("backward bf16 GQA 32/8", "bf16", max(1, 16384 // S), 32, 8, S, S, 128,
+                                        True))
+    for L in (4096, 16384, 32768, 131072):
+        rows.append(fa_inputs.DecodeConfig("decode int8 GQA 32/8", 64, 32, 8, L, 128, min(64, max(1, L // 2048))))
+    print("| kind | B | Hq/Hkv | S or L | d | causal | ms per call | rate | fraction of peak |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for cfg in rows:
+        r = _runner(cfg)
+        ms, _ = _time_region(r.run, steps, warmup)
+        work, unit = work_and_unit(cfg)
+        if unit == "GB/s":
+            rate = work / (ms * 1e-3) / 1e9
+            frac = f"{rate / PEAK_HBM_GBS:.1%} HBM"
+            shape = (cfg.B, f"{cfg.Hq}/{cfg.Hkv}", cfg.L, cfg.d, "-")
+        else:
+            rate = work / (ms * 1e-3) / 1e12
+            peak = {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
+            frac = f"{rate / peak:.1%} of its dtype's peak"
+            if cfg.dtype == "fp8":
+                frac += f", {rate / PEAK_BF16_TFLOPS:.1%} of bf16"
+            shape = (cfg.B, f"{cfg.Hq}/{cfg.Hkv}", cfg.Sq, cfg.d, "yes" if cfg.causal else "no")
+        print(f"| {cfg.name} | " + " | ".join(str(x) for x in shape) + f" | {ms:.4f} | {rate:.1f} {unit} | {frac} |",
+              flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+
 def power_study(names, seconds=4.0):
     """For each workload (and the vendor bf16 GEMM, torch.matmul of 8192^3,
     as a reference for a plain contraction on this part): run it back to back
@@ -941,6 +990,8 @@ def main():
     ap.add_argument("--label", default="")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="time vendor read-only and copy kernels over the decode workload's byte count")
+    ap.add_argument("--sweep", action="store_true",
+                    help="rates over sequence lengths, head dims, dtypes and cache lengths (markdown rows)")
     ap.add_argument("--power-study", metavar="NAMES",
                     help="sample socket power and clocks while each listed workload (comma list) runs, "
                          "and the vendor bf16 GEMM")
@@ -953,6 +1004,15 @@ def main():
 
         torch.cuda.set_device(0)
         stream_ceiling()
+        return
+    if a.sweep:
+        import torch
+
+        import tiled_exact_attention_fa_amd as fa
+
+        fa.load()
+        torch.cuda.set_device(0)
+        sweep()
         return
     if a.power_study:
         import torch
