@@ -175,6 +175,17 @@ def test_fwd_groups_lengths_and_score_ranges(gpu, dt, causal, case):
     check(o, lse, q, k, v, causal, dt, scale)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk", [(1024, 1024), (1025, 1025), (700, 1024), (1024, 1025)])
+def test_fwd_d64_launch_choice(gpu, dt, causal, Sq, Sk):
+    """d = 64 runs 128-row workgroups (two per compute unit) up to 1024 keys and
+    256-row ones past that: both sides of the switch, and Sq != Sk across it."""
+    q, k, v = make(2, 4, 2, Sq, Sk, 64, dt, seed=Sq + 2 * Sk)
+    o, lse = run_fwd(gpu, q, k, v, causal, TDT[dt])
+    check(o, lse, q, k, v, causal, dt)
+
+
 def test_fwd_deterministic(gpu):
     q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
     o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
