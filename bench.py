@@ -879,7 +879,7 @@ def sweep(steps=10, warmup=3):
             rows.append(F(f"bf16 MHA", "bf16", B, 16, 16, S, S, 128, causal))
     for S in (4096, 16384, 65536):
         rows.append(F("bf16 GQA 32/8", "bf16", 1, 32, 8, S, S, 128, True))
-    for S in (2048, 8192):
+    for S in (512, 1024, 2048, 8192):
         rows.append(F("bf16 MHA d=64", "bf16", 32768 // S, 16, 16, S, S, 64, True))
     rows.append(F("fp16 MHA", "f16", 16, 16, 16, 2048, 2048, 128, True))
     for S, causal in ((1024, False), (4096, False), (16384, False), (4096, True)):
