@@ -18,8 +18,11 @@
 //     register order of the P^T operand of O^T = V^T P^T: P is rounded in place
 //     and fed back to the matrix core without any data movement.
 //   * V is transposed in registers on its way to LDS, so every V^T operand is a
-//     single 16-byte LDS read; both tiles are padded by 16 bytes per row, which
-//     keeps 8-lane phases of 16-byte reads free of bank conflicts.
+//     single 16-byte LDS read; its rows are padded by 16 bytes, which keeps
+//     16-byte reads free of bank conflicts.  In the 16-bit kernel K goes from
+//     memory straight into LDS (direct-to-LDS buffer loads, no registers), in
+//     unpadded rows whose 16-byte chunks are XOR-swizzled by the row instead;
+//     the fp32 kernel pads its K rows.
 //   * Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
 //     exponentiated with the hardware exp2; the running max moves lazily.
 //   * 16-bit kernel: O is divided by the sum of the probabilities as rounded
@@ -34,8 +37,9 @@
 //   * 16-bit kernel: 8 wavefronts over 256 rows, software-pipelined so that
 //     every wavefront has MFMA, vector and LDS work in flight at once: P V of
 //     tile t carries the first half of tile t+1's softmax between its MFMAs,
-//     and S^T of tile t+2 the second half; K/V staging rides along too, with
-//     one barrier per tile.
+//     and S^T of tile t+2 the second half; K/V staging rides along too (K of
+//     tile t+3 straight into LDS, V of tile t+1 from registers), with one
+//     barrier per tile.
 //   * Causal tiles past a wavefront's last row are skipped; the mask is applied
 //     only on tiles that cross the diagonal or the end of the keys.  Workgroups
 //     are issued heaviest first and grouped so each XCD works on a contiguous
@@ -99,8 +103,36 @@ template <typename T, int D> struct Cfg {
 };
 
 
+// 16 bytes per lane from a buffer resource straight into LDS, bypassing the
+// registers: lane i of the wavefront writes bytes [16 i, 16 i + 16) past
+// lds_base (wave-uniform), whatever offset it reads from.  Words past the
+// resource's end arrive as zeros.  The compiler tracks neither the LDS write
+// nor its completion: wait for it with wait_vmem<N> before the barrier that
+// publishes the bytes.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void *lds_base, unsigned off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0, 0);
+}
+
+// Keeps the compiler from moving memory operations across this point, so
+// that counts of the loads issued after a direct-to-LDS load hold as written.
+// No instruction is emitted.
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wavefront are outstanding.  They complete in the order issued, so this
+// waits for all but the N most recent.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+  mem_order();
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Configuration of the 16-bit kernel: 8 wavefronts (two per SIMD) own 256 query
 // rows, so each K/V tile is fetched and staged once for twice as many rows.
+// K rows sit in LDS unpadded, as whole kilobytes per wavefront load (the
+// direct-to-LDS loads write 1 KiB runs); the 16-byte chunks of each row are
+// XOR-swizzled by the row (ksw), so 16 lanes reading one chunk of 16
+// consecutive rows cover all 64 banks.
 template <typename T, int D, int NT_> struct Cfg16 {
   static constexpr int ES = sizeof(T);
   static constexpr int KW = 8;
@@ -112,13 +144,23 @@ template <typename T, int D, int NT_> struct Cfg16 {
   static constexpr int PASSES = BC * CH / NT;   // 16-byte loads per thread per tile (K or V)
   static constexpr int KPT = PASSES;            // keys per thread in the V transpose
   static constexpr int NG = BC / KPT;           // V key groups
-  static constexpr int KROW = D + EPC;          // K row in LDS, +16 bytes
+  static constexpr int NW = NT / 64;            // wavefronts
+  static constexpr int KROW = D;                // K row in LDS (chunks swizzled, no padding)
+  static constexpr int RPS = 256 / (D * ES);    // K rows per 256 bytes (one pass over the banks)
   static constexpr int VROW = BC + EPC;         // V^T row in LDS, +16 bytes
+  static constexpr int SROW = D + EPC;          // epilogue slab row, +16 bytes
   static constexpr int K_TILE = BC * KROW;
   static constexpr int V_TILE = D * VROW;
   static constexpr int DB = D / 32;
-  static constexpr int LDS_BYTES = 2 * (K_TILE + V_TILE) * ES;
+  static constexpr int STAGE_BYTES = 2 * (K_TILE + V_TILE) * ES;
+  static constexpr int SLAB_BYTES = NW * 32 * SROW * ES;
+  static constexpr int LDS_BYTES = STAGE_BYTES > SLAB_BYTES ? STAGE_BYTES : SLAB_BYTES;
   static_assert(BC * CH % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(K_TILE * ES == NW * PASSES * 1024, "each wavefront's K loads fill whole kilobytes of the tile");
+  static_assert(RPS >= 1 && 256 % (D * ES) == 0 && (32 / RPS) % CH == 0,
+                "rows 32 apart must share their swizzle");
+  // swizzle of LDS row r: stored chunk s holds the row's chunk s ^ ksw(r)
+  static __device__ __forceinline__ int ksw(int r) { return (r / RPS) & (CH - 1); }
 };
 
 // LDS row of key kr within a tile.  For 16-bit types bits 2 and 3 are swapped,
@@ -394,8 +436,10 @@ void fwd_mfma_kernel(const FwdArgs a) {
 // (see the main loop).  Global loads go through a buffer resource placed at
 // the tile's first row, so per-lane offsets are loop constants and rows past
 // the end of the keys (or tiles past the workgroup's range) read as zero
-// without any per-lane address arithmetic.  LDS fragments are read four MFMAs
-// ahead of the MFMAs that consume them.
+// without any per-lane address arithmetic.  K tiles are loaded straight into
+// LDS, so the compiler does not see when they land: each wavefront waits for
+// its own K loads (vmcnt) before the barrier that publishes them.  LDS
+// fragments are read four MFMAs ahead of the MFMAs that consume them.
 // ---------------------------------------------------------------------------
 #ifndef FA16_WAVES_PER_EU
 #define FA16_WAVES_PER_EU 2
@@ -453,40 +497,49 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     const unsigned shift = live ? static_cast<unsigned>(j * BC) * ss : 0u;
     return make_rsrc(base + shift, live ? ext - shift : 0u);
   };
-  const int k_c = tid % CH, k_r = tid / CH;
+  // K: load p of wavefront w fills kilobyte p * NW + w of the tile, lane by
+  // lane; each lane fetches the (key, chunk) that the row order and the
+  // swizzle put at its 16 bytes
   const int v_g = tid % C::NG, v_c = tid / C::NG;
   unsigned koff[C::PASSES], voff[C::PASSES];
 #pragma unroll
   for (int p = 0; p < C::PASSES; ++p) {
-    koff[p] = (k_r + (C::NT / CH) * p) * a.k_ss + k_c * 16;
+    const int pos = (p * C::NW + wave) * 1024 + lane * 16;  // byte within the K tile
+    const int r = pos / (D * ES), sc16 = (pos % (D * ES)) / 16;
+    koff[p] = k_lds_row<8>(r) * a.k_ss + (sc16 ^ C::ksw(r)) * 16;
     voff[p] = (v_g * C::KPT + p) * a.v_ss + v_c * 16;
   }
-  u32x4 kreg[2][C::PASSES], vreg[2][C::PASSES];
+  auto k_dst = [&](int buf, int p) {
+    return reinterpret_cast<unsigned char *>(kbuf + buf * C::K_TILE) + (p * C::NW + wave) * 1024;
+  };
+  auto load_k_lds = [&](int buf, int j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) buf_load16_lds(r, k_dst(buf, p), koff[p]);
+  };
+  // the same placement through registers (the prologue's third K tile)
   auto load_k_to = [&](u32x4 *dst, int j) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, a.k_ss, a.k_ext, j);
 #pragma unroll
     for (int p = 0; p < C::PASSES; ++p) dst[p] = buf_load16(r, koff[p]);
   };
-  auto load_k = [&](int set, int j) { load_k_to(kreg[set], j); };
-  auto load_v = [&](int set, int j) {
+  auto store_k_from = [&](const u32x4 *src, int buf) {
+#pragma unroll
+    for (int p = 0; p < C::PASSES; ++p) *reinterpret_cast<u32x4 *>(k_dst(buf, p) + lane * 16) = src[p];
+  };
+  u32x4 vreg[C::PASSES];
+  auto load_v = [&](int j) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, a.v_ss, a.v_ext, j);
 #pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) vreg[set][p] = buf_load16(r, voff[p]);
+    for (int p = 0; p < C::PASSES; ++p) vreg[p] = buf_load16(r, voff[p]);
   };
-  auto store_k_from = [&](const u32x4 *src, int buf) {
-    T *ks = kbuf + buf * C::K_TILE;
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p)
-      *reinterpret_cast<u32x4 *>(ks + k_lds_row<8>(k_r + (C::NT / CH) * p) * C::KROW + k_c * EPC) = src[p];
-  };
-  auto store_k = [&](int set, int buf) { store_k_from(kreg[set], buf); };
-  auto store_v = [&](int set, int buf) {
+  auto store_v = [&](int buf) {
     T *vt = vbuf + buf * C::V_TILE;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       T col[C::KPT];
 #pragma unroll
-      for (int p = 0; p < C::KPT; ++p) col[p] = reinterpret_cast<const T *>(&vreg[set][p])[e];
+      for (int p = 0; p < C::KPT; ++p) col[p] = reinterpret_cast<const T *>(&vreg[p])[e];
       T *dst = vt + (v_c * EPC + e) * C::VROW + v_g * C::KPT;
       if constexpr (C::KPT * ES == 8) *reinterpret_cast<u32x2 *>(dst) = __builtin_bit_cast(u32x2, col);
       else if constexpr (C::KPT * ES == 4) *reinterpret_cast<unsigned *>(dst) = __builtin_bit_cast(unsigned, col);
@@ -506,11 +559,16 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   constexpr int NPV = 4 * C::DB;  // MFMAs of O^T += V^T P^T per tile
   constexpr int STEPS = 16;       // steps of each softmax half
   static_assert(STEPS % NQK == 0 && STEPS % NPV == 0, "softmax steps must split evenly over the MFMA slots");
-  const T *k_lane = kbuf + l32 * C::KROW + (D / 2) * h;
+  // MFMA i of S^T: key block i & 1, head-dim step i >> 1 (two independent
+  // chains).  Step j takes chunk j of the row in lane half 0 and chunk
+  // CH/2 + j in half 1; the swizzle makes each step's address its own
+  // register (rows l32 and l32 + 32 share it).
+  int k_lane[QS];
+#pragma unroll
+  for (int j = 0; j < QS; ++j) k_lane[j] = l32 * C::KROW + (((CH / 2) * h + j) ^ C::ksw(l32)) * EPC;
   const T *v_lane = vbuf + l32 * C::VROW + 8 * h;
-  // MFMA i of S^T: key block i & 1, head-dim step i >> 1 (two independent chains)
   auto kfrag = [&](int buf, int i) {
-    return *reinterpret_cast<const u32x4 *>(k_lane + buf * C::K_TILE + (i & 1) * 32 * C::KROW + (i >> 1) * EPC);
+    return *reinterpret_cast<const u32x4 *>(kbuf + buf * C::K_TILE + (i & 1) * 32 * C::KROW + k_lane[i >> 1]);
   };
   // MFMA i of O^T: head-dim block i >> 2, key step i & 3
   auto vfrag = [&](int buf, int i) {
@@ -732,19 +790,16 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   f32x16 sc[2][2];
 
   // ---- prologue: K of tiles 0-2 and V of tile 0 staged, tile 0 through its
-  // softmax, S^T of tile 1 formed, staging units 0 and 1 in flight.  The
-  // first tiles and the Q rows are fetched together, so the prologue waits
-  // on one memory round trip.  (K of tile 2 waits in the second V register
-  // set until tile 0's buffer is free.) ----
-  // unit u = (K of tile u+3, V of tile u+1), written to LDS in iteration u
-  auto load_unit = [&](int set, int u) {
-    load_k(set, u + 3);
-    load_v(set, u + 1);
-  };
-  load_k(0, 0);
-  load_k(1, 1);
-  load_v(0, 0);
-  load_k_to(vreg[1], 2);
+  // softmax, S^T of tile 1 formed, V of tile 1 in flight.  The first tiles
+  // and the Q rows are fetched together, so the prologue waits on one memory
+  // round trip.  (K of tile 2 waits in registers until tile 0's buffer is
+  // free.) ----
+  load_k_lds(0, 0);
+  load_k_lds(1, 1);
+  mem_order();  // the loads below are counted as issued after these
+  load_v(0);
+  u32x4 k2[C::PASSES];
+  load_k_to(k2, 2);
   // Q rows into registers
   {
     const __amdgpu_buffer_rsrc_t rq =
@@ -754,10 +809,11 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     for (int c = 0; c < QS; ++c)
       qf[c] = __builtin_bit_cast(frag, buf_load16(rq, ok ? row * a.q_ss + ((D / 2) * h + c * EPC) * ES : kOOB));
   }
-  store_k(0, 0);
-  store_k(1, 1);
-  store_v(0, 0);
-  load_unit(0, 0);
+  store_v(0);
+  load_v(1);
+  // K of tiles 0 and 1 in LDS: everything but V of tile 0, K of tile 2, the
+  // Q rows and V of tile 1 is done
+  wait_vmem<3 * C::PASSES + QS>();
   __syncthreads();
   if (0 < w_kt) {
     u32x4 kf[RA];
@@ -768,8 +824,7 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     block_qk(1, sc[1], sc[0], std::integral_constant<int, 2>{}, [](auto) {}, kf);
   }
   __syncthreads();
-  store_k_from(vreg[1], 0);
-  load_unit(1, 1);
+  store_k_from(k2, 0);
   __syncthreads();
 
   // Main loop.  Iteration t, for a wave whose rows reach tile t:
@@ -777,11 +832,12 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   //   dealt out between its MFMAs;
   //   S^T of tile t+2, with the second half of tile t+1's softmax.
   // Every wave thus keeps matrix, vector and LDS work in flight together, and
-  // the two waves of a SIMD fill each other's gaps.  The wave's share of unit
-  // t rides along too: K of tile t+3 goes into the K buffer of tile t+1 and V
-  // of tile t+1 into the V buffer of tile t-1, buffers no wave reads in this
-  // iteration; then the unit's registers are refilled.  One barrier per
-  // iteration publishes the unit.
+  // the two waves of a SIMD fill each other's gaps.  Staging rides along:
+  // K of tile t+3 goes straight into the K buffer of tile t+1 and V of tile
+  // t+1 (fetched in the previous iteration) into the V buffer of tile t-1,
+  // buffers no wave reads in this iteration; then V of tile t+2 is fetched.
+  // One barrier per iteration publishes both, after the wave's own K loads
+  // have landed.
   auto iter = [&](auto set_tag, int t) {
     constexpr int cur = decltype(set_tag)::value;  // t & 1
     constexpr int nxt = cur ^ 1;
@@ -791,21 +847,26 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     rescale_o();
     mask(sc[nxt], t + 1);
     block_pv(cur, sc[cur][0], sc[nxt], [&](auto I) {
-      if constexpr (decltype(I)::value == 1) store_k(cur, nxt);
-      if constexpr (decltype(I)::value == 3) store_v(cur, nxt);
+      if constexpr (decltype(I)::value == 0) {
+        load_k_lds(nxt, t + 3);
+        mem_order();
+      }
+      if constexpr (decltype(I)::value == 3) store_v(nxt);
     }, vf, cur, kf);
     block_qk(cur, sc[cur], sc[nxt], std::integral_constant<int, 1>{}, [&](auto I) {
-      if constexpr (decltype(I)::value == 2) load_unit(cur, t + 2);
+      if constexpr (decltype(I)::value == 2) load_v(t + 2);
     }, kf);
+    wait_vmem<C::PASSES>();  // this iteration's K loads; V of tile t+2 may be in flight
     __syncthreads();
   };
   // iterations past the wave's last tile (causal): staging only
   auto iter_stage = [&](auto set_tag, int t) {
-    constexpr int cur = decltype(set_tag)::value;
-    constexpr int nxt = cur ^ 1;
-    store_k(cur, nxt);
-    store_v(cur, nxt);
-    load_unit(cur, t + 2);
+    constexpr int nxt = decltype(set_tag)::value ^ 1;
+    load_k_lds(nxt, t + 3);
+    mem_order();
+    store_v(nxt);
+    load_v(t + 2);
+    wait_vmem<C::PASSES>();
     __syncthreads();
   };
   // two loops with a single path each (the register sets alternate, so both
@@ -837,8 +898,7 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   const float lr_tot = lr_run + swap_halves(lr_run);
   {
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-    T *slab = kbuf + wave * 32 * C::KROW;  // 32 rows of KROW elements
-    static_assert(C::NT / 64 * 32 * C::KROW <= 2 * (C::K_TILE + C::V_TILE), "epilogue slabs must fit the LDS");
+    T *slab = kbuf + wave * 32 * C::SROW;  // 32 rows of SROW elements (within LDS_BYTES)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -846,7 +906,7 @@ void fwd_mfma16_kernel(const FwdArgs a) {
         T out[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(slab + l32 * C::KROW + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+        *reinterpret_cast<u32x2 *>(slab + l32 * C::SROW + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
       }
     // the slab is private to the wavefront: LDS operations of one wavefront
     // complete in order, so its reads below see its writes above
@@ -855,7 +915,7 @@ void fwd_mfma16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 32 / RPI; ++k) {
       const int r = k * RPI + lane / CH, c = lane % CH;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * C::KROW + c * EPC);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * C::SROW + c * EPC);
       const int orow_i = wrow0 + r;
       if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + c * EPC) = v;
     }
@@ -930,8 +990,9 @@ int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream) {
     // d = 64 over short key ranges: workgroups of 256 threads (128 rows), two
     // per compute unit, so one workgroup's prologue and epilogue overlap the
     // other's loop.  Measured +13 % (causal) and +5.5 % at S = 512, +3 % at
-    // 1024, neutral at 2048; at d = 128 the 256-thread kernel does not fit its
-    // registers (twice the staging per thread).
+    // 1024, neutral at 2048.  At d = 128 the same launch fits its registers
+    // but measured -4 % at 1024 keys and +1.5 % at 512 (causal only), so
+    // d = 128 keeps 512 threads.
     const FwdArgs args = make_fwd_args(p, 128, es);
     switch (p->in_dtype) {
       case FA_BF16: return launch_causal<__bf16, 64, 256>(args, p->causal != 0, s);
