@@ -127,6 +127,16 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The lane's index within its wavefront, computed where it is called: the
+// opaque zero keeps the compiler from reusing an earlier value, which would
+// then have to stay live (and in a register-bound loop be spilled) until
+// here.
+__device__ __forceinline__ int fresh_lane_id() {
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, static_cast<unsigned>(zero))));
+}
+
 // Configuration of the 16-bit kernel: 8 wavefronts (two per SIMD) own 256 query
 // rows, so each K/V tile is fetched and staged once for twice as many rows.
 // K rows sit in LDS unpadded, as whole kilobytes per wavefront load (the
@@ -585,16 +595,19 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   const float cscale = a.c;
 
   // mask the keys of tile j past the end of the keys or the diagonal
+  // (on edge tiles only; the lane's row and half are taken afresh from the
+  // lane id, so they need not stay live through the loop)
   auto mask = [&](f32x16 s[2], int j) {
     const int j0 = j * BC;
     const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
     if (edge) {
-      const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
+      const int fl = fresh_lane_id();
+      const int lim = min(a.Sk - 1 - j0, CAUSAL ? wrow0 + (fl & 31) + coff - j0 : BC);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (acc_key<8>(mb, i, h) > lim) s[mb][i] = neg_inf();
+          if (acc_key<8>(mb, i, fl >> 5) > lim) s[mb][i] = neg_inf();
     }
   };
   // First half, in 16 steps: tile max (max3 tree, then the other lane half),
@@ -893,9 +906,19 @@ void fwd_mfma16_kernel(const FwdArgs a) {
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l).  The LDS is
   // free after the loop's last barrier: each wavefront transposes its 32 x D
   // block through its own LDS slab, so that global stores write whole rows
-  // (16 lanes x 16 bytes per row) instead of 8-byte pieces of 32 rows. ----
-  const float l_tot = l_run + swap_halves(l_run);
-  const float lr_tot = lr_run + swap_halves(lr_run);
+  // (16 lanes x 16 bytes per row) instead of 8-byte pieces of 32 rows.
+  // The lane's indices are taken afresh from the lane id: kept live across
+  // the loop, which does not use them, they would be spilled to scratch and
+  // read back here, a memory round trip per work item. ----
+  const int elane = fresh_lane_id();
+  const int el32 = elane & 31, eh = elane >> 5, erow = wrow0 + el32;
+  auto other_half = [&](float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, eh == 0 ? r[1] : r[0]);
+  };
+  const float l_tot = l_run + other_half(l_run);
+  const float lr_tot = lr_run + other_half(lr_run);
   {
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     T *slab = kbuf + wave * 32 * C::SROW;  // 32 rows of SROW elements (within LDS_BYTES)
@@ -906,7 +929,7 @@ void fwd_mfma16_kernel(const FwdArgs a) {
         T out[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(slab + l32 * C::SROW + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+        *reinterpret_cast<u32x2 *>(slab + el32 * C::SROW + 32 * db + 8 * g + 4 * eh) = __builtin_bit_cast(u32x2, out);
       }
     // the slab is private to the wavefront: LDS operations of one wavefront
     // complete in order, so its reads below see its writes above
@@ -914,14 +937,14 @@ void fwd_mfma16_kernel(const FwdArgs a) {
     T *obase = static_cast<T *>(a.o) + b * a.o_sb + hq * a.o_sh;
 #pragma unroll
     for (int k = 0; k < 32 / RPI; ++k) {
-      const int r = k * RPI + lane / CH, c = lane % CH;
+      const int r = k * RPI + elane / CH, c = elane % CH;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * C::SROW + c * EPC);
       const int orow_i = wrow0 + r;
       if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + c * EPC) = v;
     }
   }
-  if (WLSE && row < a.Sq && a.lse != nullptr && h == 0)
-    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+  if (WLSE && erow < a.Sq && a.lse != nullptr && eh == 0)
+    a.lse[b * a.lse_sb + hq * a.lse_sh + erow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
 }
 
 template <typename T, int D, bool CAUSAL, int NT, bool SEXP = false, bool WLSE = true>
