@@ -340,6 +340,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const int i0 = (t_first + ct) * kTR;
     ct = ct + 1 == ntl ? 0 : ct + 1;
     auto softmax_grad = [&](auto masked) {
+      // masked tiles only: the lane's key taken afresh (see fresh_lane_id)
+      const int mkey = decltype(masked)::value ? kw0 + (fresh_lane_id() & 31) : 0;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int r0 = 16 * half + 8 * h;  // tile rows r0 .. r0 + 7 in registers 8 half ..
@@ -356,8 +358,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
             const float l2 = e < 4 ? l0[e] : l1[e - 4];
             float p = fast_exp2(s[ireg] * a.c - l2);
             if constexpr (decltype(masked)::value) {
-              bool vis = key < a.Sk;
-              if (CAUSAL) vis = vis && key <= i0 + r0 + e + coff;
+              bool vis = mkey < a.Sk;
+              if (CAUSAL) vis = vis && mkey <= i0 + r0 + e + coff;
               p = vis ? p : 0.f;
             }
             pv[u] = p;
@@ -449,15 +451,18 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
-  // ---- write dK = tau dK^T^T and dV: lane's key, dims 32 db + 8 m + 4 h .. +3 ----
-  if (key < a.Sk) {
-    char *dkrow = static_cast<char *>(a.dk) + (b * a.dk_sb + hk * a.dk_sh) * 2 + static_cast<long long>(key) * a.dk_ss;
-    char *dvrow = static_cast<char *>(a.dv) + (b * a.dv_sb + hk * a.dv_sh) * 2 + static_cast<long long>(key) * a.dv_ss;
+  // ---- write dK = tau dK^T^T and dV: lane's key, dims 32 db + 8 m + 4 h .. +3
+  // (the lane's key and half taken afresh: see fresh_lane_id) ----
+  const int elane = fresh_lane_id();
+  const int ekey = kw0 + (elane & 31), eh = elane >> 5;
+  if (ekey < a.Sk) {
+    char *dkrow = static_cast<char *>(a.dk) + (b * a.dk_sb + hk * a.dk_sh) * 2 + static_cast<long long>(ekey) * a.dk_ss;
+    char *dvrow = static_cast<char *>(a.dv) + (b * a.dv_sb + hk * a.dv_sh) * 2 + static_cast<long long>(ekey) * a.dv_ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int d0 = 32 * db + 8 * m + 4 * h;
+        const int d0 = 32 * db + 8 * m + 4 * eh;
         *reinterpret_cast<u32x2 *>(dkrow + 2 * d0) =
             u32x2{pack2<T>(dk[db][4 * m] * a.scale, dk[db][4 * m + 1] * a.scale),
                   pack2<T>(dk[db][4 * m + 2] * a.scale, dk[db][4 * m + 3] * a.scale)};
@@ -551,6 +556,9 @@ void bwd_dq_kernel(const BwdArgs a) {
     }
     frag dsf[2];
     auto softmax_grad = [&](auto masked) {
+      // masked tiles only: the lane's row and half taken afresh (see fresh_lane_id)
+      const int ml = decltype(masked)::value ? fresh_lane_id() : 0;
+      const int mrow = rw0 + (ml & 31), mh = ml >> 5;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         unsigned dw[4];
@@ -562,9 +570,9 @@ void bwd_dq_kernel(const BwdArgs a) {
             const int ireg = 8 * half + 2 * e2 + u;
             float p = fast_exp2(s[ireg] * a.c - l2);
             if constexpr (decltype(masked)::value) {
-              const int kj = j0 + acc_row(0, ireg, h);
+              const int kj = j0 + acc_row(0, ireg, mh);
               bool vis = kj < a.Sk;
-              if (CAUSAL) vis = vis && kj <= row + coff;
+              if (CAUSAL) vis = vis && kj <= mrow + coff;
               p = vis ? p : 0.f;
             }
             dsv[u] = p * dp[ireg];
@@ -596,13 +604,16 @@ void bwd_dq_kernel(const BwdArgs a) {
     __syncthreads();
   }
 
-  if (row < a.Sq) {
-    char *dqrow = static_cast<char *>(a.dq) + (b * a.dq_sb + hq * a.dq_sh) * 2 + static_cast<long long>(row) * a.dq_ss;
+  // the lane's row and half taken afresh (see fresh_lane_id)
+  const int elane = fresh_lane_id();
+  const int erow = rw0 + (elane & 31), eh = elane >> 5;
+  if (erow < a.Sq) {
+    char *dqrow = static_cast<char *>(a.dq) + (b * a.dq_sb + hq * a.dq_sh) * 2 + static_cast<long long>(erow) * a.dq_ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int d0 = 32 * db + 8 * m + 4 * h;
+        const int d0 = 32 * db + 8 * m + 4 * eh;
         *reinterpret_cast<u32x2 *>(dqrow + 2 * d0) =
             u32x2{pack2<T>(dq[db][4 * m] * a.scale, dq[db][4 * m + 1] * a.scale),
                   pack2<T>(dq[db][4 * m + 2] * a.scale, dq[db][4 * m + 3] * a.scale)};

@@ -102,6 +102,17 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // the loop's own prefetches.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The lane's index within its wavefront, computed where it is called: the
+// opaque zero keeps the compiler from reusing an earlier value, which would
+// then have to stay live through a register-bound loop (and be spilled, or
+// crowd it) until here.  For rarely taken branches such as edge masks, and
+// for epilogues.
+__device__ __forceinline__ int fresh_lane_id() {
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, static_cast<unsigned>(zero))));
+}
+
 // True if pred holds in any lane of the wavefront (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -326,12 +326,14 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
     const int j0 = j * BC;
     const bool edge = (j0 + BC > a.Sk) || (CAUSAL && j0 + BC - 1 > wrow0 + coff);
     if (edge) {
-      const int lim = min(a.Sk - 1 - j0, CAUSAL ? row + coff - j0 : BC);
+      // the lane's row and half taken afresh (see fresh_lane_id)
+      const int fl = fresh_lane_id(), fh = fl >> 5;
+      const int lim = min(a.Sk - 1 - j0, CAUSAL ? wrow0 + (fl & 31) + coff - j0 : BC);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = PB16 ? 32 * mb + 16 * (i >> 3) + 8 * h + (i & 7) : 32 * h + 16 * mb + i;
+          const int key = PB16 ? 32 * mb + 16 * (i >> 3) + 8 * fh + (i & 7) : 32 * fh + 16 * mb + i;
           if (key > lim) s[mb][i] = neg_inf();
         }
     }
@@ -668,8 +670,16 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
 
   // ---- epilogue: O = o_mul * O_acc / l (l carries kPScale, which cancels),
   // transposed through LDS (free after the loop's last barrier) so that each
-  // store writes whole rows ----
-  const float l_tot = l_run + swap_halves(l_run);
+  // store writes whole rows.  The lane's indices are taken afresh (see
+  // fresh_lane_id). ----
+  const int elane = fresh_lane_id();
+  const int el32 = elane & 31, eh = elane >> 5, erow = wrow0 + el32;
+  auto other_half = [&](float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, eh == 0 ? r[1] : r[0]);
+  };
+  const float l_tot = l_run + other_half(l_run);
   {
     const float inv = l_tot > 0.f ? (BLK ? sv_max : a.o_mul) / l_tot : 0.f;
     __bf16 *slab = reinterpret_cast<__bf16 *>(lds) + wave * 32 * ORow;
@@ -680,20 +690,20 @@ void fwd_fp8_kernel(const FwdArgs a, const Fp8BlockScales bs) {
         bf16x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(oacc[db][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(slab + l32 * ORow + 32 * db + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, out);
+        *reinterpret_cast<u32x2 *>(slab + el32 * ORow + 32 * db + 8 * g + 4 * eh) = __builtin_bit_cast(u32x2, out);
       }
     // the slab is private to the wavefront, whose LDS operations complete in order
     __bf16 *obase = static_cast<__bf16 *>(a.o) + b * a.o_sb + hq * a.o_sh;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int r = 4 * k + lane / 16, c = lane % 16;
+      const int r = 4 * k + elane / 16, c = elane % 16;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + r * ORow + 8 * c);
       const int orow_i = wrow0 + r;
       if (orow_i < a.Sq) *reinterpret_cast<u32x4 *>(obase + static_cast<long long>(orow_i) * a.o_ss + 8 * c) = v;
     }
   }
-  if (row < a.Sq && a.lse != nullptr && h == 0)
-    a.lse[b * a.lse_sb + hq * a.lse_sh + row] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PS) * kLn2 : neg_inf();
+  if (erow < a.Sq && a.lse != nullptr && eh == 0)
+    a.lse[b * a.lse_sb + hq * a.lse_sh + erow] = l_tot > 0.f ? (m_run + __log2f(l_tot) - kLog2PS) * kLn2 : neg_inf();
 }
 
 template <bool CAUSAL, bool BLK, bool PB16>

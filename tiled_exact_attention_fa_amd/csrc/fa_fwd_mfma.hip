@@ -127,16 +127,6 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// The lane's index within its wavefront, computed where it is called: the
-// opaque zero keeps the compiler from reusing an earlier value, which would
-// then have to stay live (and in a register-bound loop be spilled) until
-// here.
-__device__ __forceinline__ int fresh_lane_id() {
-  int zero = 0;
-  asm volatile("" : "+v"(zero));
-  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, static_cast<unsigned>(zero))));
-}
-
 // Configuration of the 16-bit kernel: 8 wavefronts (two per SIMD) own 256 query
 // rows, so each K/V tile is fetched and staged once for twice as many rows.
 // K rows sit in LDS unpadded, as whole kilobytes per wavefront load (the
