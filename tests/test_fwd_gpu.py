@@ -186,6 +186,21 @@ def test_fwd_d64_launch_choice(gpu, dt, causal, Sq, Sk):
     check(o, lse, q, k, v, causal, dt)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk", [(512, 512), (513, 513), (300, 512), (512, 513)])
+def test_fwd_d128_launch_choice(gpu, dt, causal, Sq, Sk):
+    """d = 128 with an LSE output runs 128-row workgroups up to 512 keys and
+    256-row ones past that (and without an LSE output, 256-row ones
+    throughout): both sides of the switch, Sq != Sk across it, and the no-LSE
+    call at the same sizes."""
+    q, k, v = make(2, 4, 2, Sq, Sk, 128, dt, seed=Sq + 3 * Sk)
+    o, lse = run_fwd(gpu, q, k, v, causal, TDT[dt])
+    check(o, lse, q, k, v, causal, dt)
+    o2, _ = run_fwd(gpu, q, k, v, causal, TDT[dt], lse_wanted=False)
+    check(o2, None, q, k, v, causal, dt)
+
+
 def test_fwd_deterministic(gpu):
     q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
     o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)

@@ -999,17 +999,21 @@ int fa_launch_fwd_mfma(const fa_fwd_params *p, void *stream) {
   const int es = fa_dtype_size(p->in_dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (es == 4) return launch_dtype<float, 256>(make_fwd_args(p, 128, es), p->d, p->causal != 0, false, s);
-  if (p->d == 64 && p->Sk <= 1024) {
-    // d = 64 over short key ranges: workgroups of 256 threads (128 rows), two
-    // per compute unit, so one workgroup's prologue and epilogue overlap the
-    // other's loop.  Measured +13 % (causal) and +5.5 % at S = 512, +3 % at
-    // 1024, neutral at 2048.  At d = 128 the same launch fits its registers
-    // but measured -4 % at 1024 keys and +1.5 % at 512 (causal only), so
-    // d = 128 keeps 512 threads.
+  // Short key ranges: workgroups of 256 threads (128 rows), two per compute
+  // unit, so one workgroup's prologue and epilogue overlap the other's loop.
+  // d = 64 up to 1024 keys: measured +13 % (causal) and +5.5 % at S = 512, +3 %
+  // at 1024, neutral at 2048.  d = 128 up to 512 keys (with an LSE output and
+  // the hardware exponential, the variants built for this launch): +2 %
+  // causal and not at S = 512, but -4 % at 1024.
+  const bool short64 = p->d == 64 && p->Sk <= 1024;
+  const bool short128 = p->d == 128 && p->Sk <= 512 && p->lse != nullptr && p->soft_exp2 == 0;
+  if (short64 || short128) {
     const FwdArgs args = make_fwd_args(p, 128, es);
+    const bool c = p->causal != 0;
     switch (p->in_dtype) {
-      case FA_BF16: return launch_causal<__bf16, 64, 256>(args, p->causal != 0, s);
-      case FA_F16: return launch_causal<_Float16, 64, 256>(args, p->causal != 0, s);
+      case FA_BF16: return short64 ? launch_causal<__bf16, 64, 256>(args, c, s) : launch_causal<__bf16, 128, 256>(args, c, s);
+      case FA_F16:
+        return short64 ? launch_causal<_Float16, 64, 256>(args, c, s) : launch_causal<_Float16, 128, 256>(args, c, s);
       default: return fa_set_error(FA_ERR_UNSUPPORTED, "dtype %d has no MFMA forward kernel", p->in_dtype);
     }
   }
