@@ -201,6 +201,20 @@ def test_fwd_d128_launch_choice(gpu, dt, causal, Sq, Sk):
     check(o2, None, q, k, v, causal, dt)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 17, 600), (2, 4, 1, 129, 700), (1, 4, 2, 300, 577), (1, 2, 1, 700, 600)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fwd_d128_ragged_past_512_keys(gpu, dt, causal, shape):
+    """Ragged query and key lengths just past 512 keys, so the 256-row
+    workgroups see partial last tiles, short query blocks and (causal, Sq > Sk)
+    leading rows that see no key."""
+    B, Hq, Hkv, Sq, Sk = shape
+    q, k, v = make(B, Hq, Hkv, Sq, Sk, 128, dt, seed=Sq * 7 + Sk)
+    o, lse = run_fwd(gpu, q, k, v, causal, TDT[dt])
+    check(o, lse, q, k, v, causal, dt)
+
+
 def test_fwd_deterministic(gpu):
     q, k, v = make(2, 8, 2, 333, 333, 128, "bf16", seed=11)
     o1, l1 = run_fwd(gpu, q, k, v, True, torch.bfloat16)
