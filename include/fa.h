@@ -59,8 +59,10 @@
  *     axes; the head-dimension stride is always 1.  Base pointers must be 16-byte
  *     aligned and the strides must keep every row 16-byte aligned
  *     (FA_ERR_ALIGNMENT otherwise).  Rows of one sequence must not overlap
- *     (sequence stride >= d), and one (batch, head) slice must span less than
- *     2^31 bytes (FA_ERR_UNSUPPORTED otherwise).
+ *     (sequence stride >= d), one (batch, head) slice must span less than
+ *     2^31 bytes, and the sequence stride must be at most 8 MiB per row (the
+ *     kernels form row offsets in 32 bits for every row of a tile);
+ *     FA_ERR_UNSUPPORTED otherwise.
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H

@@ -97,6 +97,19 @@ def test_fwd_validator_errors(lib, mutate, status):
     assert fa.fa_last_error() != ""
 
 
+def test_fwd_sequence_stride_limit(lib):
+    """Row offsets within a tile are formed in 32 bits for every row of the
+    tile, also past the last key: a one-key K whose sequence stride exceeds
+    8 MiB is refused although its extent is small; 8 MiB itself is accepted."""
+    p = good_fwd()
+    p.Sk = 1
+    p.k_strides = fa.I64x3(0, 0, 1 << 22)  # 8 MiB of bf16 per row
+    assert fa.fa_check_fwd_params(p) == fa.FA_OK
+    p.k_strides = fa.I64x3(0, 0, (1 << 22) + 8)
+    assert fa.fa_check_fwd_params(p) == fa.FA_ERR_UNSUPPORTED
+    assert "8 MiB" in fa.fa_last_error()
+
+
 def test_fwd_fp8_needs_positive_descales(lib):
     p = good_fwd()
     p.in_dtype = fa.FA_FP8_E4M3

@@ -85,6 +85,13 @@ int check_tensor(const char *name, const void *ptr, const int64_t *strides, int 
     if (rows > 1 && strides[2] < d)
       return fa_set_error(FA_ERR_INVALID_ARG, "%s sequence stride %lld < d=%d (rows overlap)", name,
                           static_cast<long long>(strides[2]), d);
+    // The kernels form row * stride in 32 bits for every row of a tile (up to
+    // 256), including rows past the end that the buffer range then reads as
+    // zero; above 8 MiB per row such an offset could wrap back inside the
+    // slice.  Checked whatever `rows` is: a short tensor still has full tiles.
+    if (strides[2] * esize > (int64_t(1) << 23))
+      return fa_set_error(FA_ERR_UNSUPPORTED, "%s sequence stride %lld elements exceeds 8 MiB per row", name,
+                          static_cast<long long>(strides[2]));
     const int64_t extent = (static_cast<int64_t>(rows > 0 ? rows - 1 : 0) * strides[2] + d) * esize;
     if (extent >= (int64_t(1) << 31))
       return fa_set_error(FA_ERR_UNSUPPORTED, "%s: one (batch, head) slice spans %lld bytes (limit 2^31)",
