@@ -44,9 +44,12 @@ struct QuantArgs {
 
 constexpr int kQRows = 64;  // rows per block
 
+// (every pattern used here reads a lane inside the same row, so no lane is
+// out of bounds; bound_ctrl set lets the move need no prior value in its
+// destination)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // the value lane (l ^ X) holds, within each row of 16 lanes (X = 1, 2, 4, 8)
@@ -60,15 +63,17 @@ __device__ __forceinline__ float lane_xor(float v) {
 }
 
 // one transform stage across lanes: the lane whose chunk has bit X clear holds
-// a (takes a + b), the other holds b (takes a - b)
+// a (takes a + b), the other holds b (takes a - b).  Both are other + sgn * y
+// with sgn = +-1 (bit X of the chunk): the product is exact and the sum is the
+// same correctly rounded a + b or a - b, so the stage costs one multiply and
+// one add whose other operand arrives through DPP.
 template <int X>
-__device__ __forceinline__ void xstage(float (&y)[8], int c) {
-  const bool upper = (c & X) != 0;
+__device__ __forceinline__ void xstage(float (&y)[8], float sgn) {
+  // kept as a separate multiply and add (a fused form ties the add's output
+  // to a register the DPP move must fill first)
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float other = lane_xor<X>(y[e]);
-    y[e] = upper ? other - y[e] : y[e] + other;
-  }
+  for (int e = 0; e < 8; ++e) y[e] = lane_xor<X>(y[e]) + sgn * y[e];
 }
 
 template <bool BF16, bool ROT>
@@ -121,10 +126,10 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
             y[r][e + hs] = p - q;
           }
       // stages h = 8, 16, 32, 64 across the group
-      xstage<1>(y[r], c);
-      xstage<2>(y[r], c);
-      xstage<4>(y[r], c);
-      xstage<8>(y[r], c);
+      xstage<1>(y[r], (c & 1) ? -1.f : 1.f);
+      xstage<2>(y[r], (c & 2) ? -1.f : 1.f);
+      xstage<4>(y[r], (c & 4) ? -1.f : 1.f);
+      xstage<8>(y[r], (c & 8) ? -1.f : 1.f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[r][e] *= 0.08838834764831845f;  // fp32(1/sqrt(128))
     }
