@@ -113,6 +113,26 @@ __device__ __forceinline__ int fresh_lane_id() {
   return static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, static_cast<unsigned>(zero))));
 }
 
+// A DPP move within each row of 16 lanes.  Every pattern used here reads a
+// lane inside the same row, so no lane is out of bounds; bound_ctrl set lets
+// the move need no prior value in its destination.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// The value lane (l ^ X) holds, within each row of 16 lanes (X = 1, 2, 4, 8):
+// one or two DPP moves on the vector ALU, where a width-16 shuffle would be
+// an LDS permute.
+template <int X>
+__device__ __forceinline__ float row16_xor(float v) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8, "row16_xor: 1, 2, 4 or 8");
+  if constexpr (X == 1) return dpp_mov<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
+  else if constexpr (X == 2) return dpp_mov<0x4E>(v);             // quad_perm [2, 3, 0, 1]
+  else if constexpr (X == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // l ^ 7, then l ^ 3
+  else return dpp_mov<0x141>(dpp_mov<0x140>(v));                  // l ^ 15, then l ^ 7
+}
+
 // True if pred holds in any lane of the wavefront (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

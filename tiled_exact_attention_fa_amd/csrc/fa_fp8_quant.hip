@@ -44,24 +44,6 @@ struct QuantArgs {
 
 constexpr int kQRows = 64;  // rows per block
 
-// (every pattern used here reads a lane inside the same row, so no lane is
-// out of bounds; bound_ctrl set lets the move need no prior value in its
-// destination)
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// the value lane (l ^ X) holds, within each row of 16 lanes (X = 1, 2, 4, 8)
-template <int X>
-__device__ __forceinline__ float lane_xor(float v) {
-  static_assert(X == 1 || X == 2 || X == 4 || X == 8, "lane_xor: 1, 2, 4 or 8");
-  if constexpr (X == 1) return dpp_mov<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
-  else if constexpr (X == 2) return dpp_mov<0x4E>(v);             // quad_perm [2, 3, 0, 1]
-  else if constexpr (X == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // l ^ 7, then l ^ 3
-  else return dpp_mov<0x141>(dpp_mov<0x140>(v));                  // l ^ 15, then l ^ 7
-}
-
 // one transform stage across lanes: the lane whose chunk has bit X clear holds
 // a (takes a + b), the other holds b (takes a - b).  Both are other + sgn * y
 // with sgn = +-1 (bit X of the chunk): the product is exact and the sum is the
@@ -73,7 +55,7 @@ __device__ __forceinline__ void xstage(float (&y)[8], float sgn) {
   // to a register the DPP move must fill first)
 #pragma clang fp contract(off)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = lane_xor<X>(y[e]) + sgn * y[e];
+  for (int e = 0; e < 8; ++e) y[e] = row16_xor<X>(y[e]) + sgn * y[e];
 }
 
 template <bool BF16, bool ROT>
@@ -136,10 +118,10 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const QuantArgs a)
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[r][e]));
   }
-  amax = fmaxf(amax, lane_xor<8>(amax));
-  amax = fmaxf(amax, lane_xor<4>(amax));
-  amax = fmaxf(amax, lane_xor<2>(amax));
-  amax = fmaxf(amax, lane_xor<1>(amax));
+  amax = fmaxf(amax, row16_xor<8>(amax));
+  amax = fmaxf(amax, row16_xor<4>(amax));
+  amax = fmaxf(amax, row16_xor<2>(amax));
+  amax = fmaxf(amax, row16_xor<1>(amax));
   if (c == 0) s_max[g] = amax;
   __syncthreads();
   float bmax = 0.f;

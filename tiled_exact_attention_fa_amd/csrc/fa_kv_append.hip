@@ -90,8 +90,11 @@ __device__ __forceinline__ u32x2 quantise8(const u32x4 raw, _Float16 &sc16) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  // the group's absmax by DPP exchanges within the 16-lane row
+  amax = fmaxf(amax, row16_xor<8>(amax));
+  amax = fmaxf(amax, row16_xor<4>(amax));
+  amax = fmaxf(amax, row16_xor<2>(amax));
+  amax = fmaxf(amax, row16_xor<1>(amax));
   constexpr float kQmax = FP8 ? 448.f : 127.f;
   sc16 = static_cast<_Float16>(fminf(amax / kQmax, 65504.f));
   const float scf = static_cast<float>(sc16);
