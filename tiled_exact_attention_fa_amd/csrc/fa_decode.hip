@@ -173,10 +173,17 @@ __device__ __forceinline__ int exp_of(float x) {
 // left at zero everywhere in this library).
 template <bool VEC> __device__ __forceinline__ u32x2 load_scales4_at(__amdgpu_buffer_rsrc_t r, unsigned voff) {
   if constexpr (VEC) return buf_load8_nt(r, voff);
-  unsigned short e[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2u * i, 0, kNonTemporal);
-  return u32x2{e[0] | (static_cast<unsigned>(e[1]) << 16), e[2] | (static_cast<unsigned>(e[3]) << 16)};
+  // four 2-byte loads built into two 2-element vectors.  (Packed instead with
+  // shifts and ORs, this compiler kept more of the three tiles' scales live
+  // at once and spilled 16-24 bytes per thread to scratch inside the loop;
+  // built this way the unaligned-scale kernels do not spill.)
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 lo, hi;
+  lo[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, kNonTemporal);
+  lo[1] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2u, 0, kNonTemporal);
+  hi[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4u, 0, kNonTemporal);
+  hi[1] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 6u, 0, kNonTemporal);
+  return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
 // Four fp16 scales of consecutive tokens starting at token t (a multiple of 4).
