@@ -867,7 +867,8 @@ def sweep(steps=10, warmup=3):
     """Rates over shapes beyond the named workloads (no oracle check): prefill
     bf16 at d = 128 over sequence lengths (MHA, B * S = 32768 tokens, causal and
     not; GQA 32/8 up to S = 65536), d = 64, fp16 and fp8; the backward; int8-KV
-    decode over cache lengths (B = 64, GQA 32/8, 2048-token splits, at most 64).
+    decode over cache lengths (B = 64, GQA 32/8, 2048-token splits, at most 64), and once with a
+    cache length that leaves the scale rows unaligned (2-byte scale loads).
     Prints one markdown row per shape."""
     import torch
 
@@ -889,6 +890,8 @@ def sweep(steps=10, warmup=3):
                                         True))
     for L in (4096, 16384, 32768, 131072):
         rows.append(fa_inputs.DecodeConfig("decode int8 GQA 32/8", 64, 32, 8, L, 128, min(64, max(1, L // 2048))))
+    # a cache length that is not a multiple of 8: scale rows not 16-byte aligned, 2-byte scale loads
+    rows.append(fa_inputs.DecodeConfig("decode int8 GQA 32/8, unaligned scale rows", 64, 32, 8, 32764, 128, 16))
     print("| kind | B | Hq/Hkv | S or L | d | causal | ms per call | rate | fraction of peak |")
     print("|---|---|---|---|---|---|---|---|---|")
     for cfg in rows:
