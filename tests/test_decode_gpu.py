@@ -178,17 +178,18 @@ def test_decode_value_scales_spanning_the_chunk(gpu, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
-@pytest.mark.parametrize("path", ["staged", "vec8", "scalar2"])
+@pytest.mark.parametrize("path", ["staged", "staged2", "vec8", "scalar2"])
 def test_decode_poisoned_cache_tail(gpu, fmt, path):
     """Cache slots at or past seq_lens[b] hold +-Inf and NaN fp16 scales
     (0x7C00, 0xFC00, 0x7E00) and, for fp8, the NaN codes 0x7F / 0xFF: only
     the first seq_lens[b] tokens may reach the result.  Lengths are not
-    multiples of 32 or 4.  The three scale paths: scales staged in LDS (chunks
-    of at most 2048 tokens), 8-byte per-tile scale loads (longer chunks), and
-    2-byte loads (scale rows offset by one element)."""
+    multiples of 32 or 4.  The four scale paths: scales staged in LDS (chunks
+    of at most 2048 tokens) with 16-byte loads or, for scale rows offset by
+    one element, 2-byte loads; per-tile 8-byte scale loads (longer chunks);
+    per-tile 2-byte loads (longer chunks, offset rows)."""
     lens = [184, 1, 3001, 2047, 33, 4095]
     B, Hq, Hkv, L = len(lens), 8, 2, 4096
-    splits = 4 if path == "staged" else 1  # chunks of 1024 or 4096 tokens
+    splits = 4 if path.startswith("staged") else 1  # chunks of 1024 or 4096 tokens
     cfg = fa_inputs.DecodeConfig("t", B, Hq, Hkv, L, 128, splits, tuple(lens), fmt)
     xc = fa_inputs.make_decode_inputs(cfg, seed=31)
     x = {k: v.clone() for k, v in xc.items()}
@@ -203,7 +204,7 @@ def test_decode_poisoned_cache_tail(gpu, fmt, path):
             else:
                 x[key][b, :, n:] = 127
     x = {k: v.cuda() for k, v in x.items()}
-    if path == "scalar2":
+    if path in ("scalar2", "staged2"):
         for key in ("k_scale", "v_scale"):
             big = torch.zeros(B, Hkv, L + 1, dtype=torch.float16, device="cuda")
             big[..., 1:] = x[key]

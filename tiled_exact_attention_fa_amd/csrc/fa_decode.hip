@@ -17,10 +17,11 @@
 //     chunk's 32-token tiles are dealt to the four wavefronts in turn, so the
 //     workgroup streams one contiguous stretch at a time; each wavefront keeps
 //     two tiles of register prefetch and no barrier, and the four partial
-//     states are merged through LDS at the end.  When the scale rows allow
-//     16-byte loads and a chunk has at most 2048 tokens, the chunk's key and
-//     value scales are staged in LDS once, with two coalesced loads per
-//     thread, instead of four tiny loads per tile and wavefront.
+//     states are merged through LDS at the end.  When a chunk has at most
+//     2048 tokens, the chunk's key and value scales are staged in LDS once
+//     (two coalesced 16-byte loads per thread when the scale rows are 16-byte
+//     aligned, sixteen 2-byte loads otherwise) instead of four small loads per
+//     tile and wavefront.
 //   * The dequantisation is fused into the tile load and folded into the math:
 //     int8 codes become exact fp16 values with two byte permutes and a packed
 //     subtract (1024 + u in fp16 is 0x6400 | u); E4M3FN codes (every one of
@@ -357,7 +358,6 @@ constexpr int kStageTok = 2048;
 template <bool SCVEC, bool FP8, bool STAGED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const DecodeArgs a) {
-  static_assert(!STAGED || SCVEC, "staged scales use 16-byte loads of aligned scale rows");
   __shared__ float s_o[4][FA_DECODE_MAX_GROUP][kD];
   __shared__ float s_l[4][FA_DECODE_MAX_GROUP];
   __shared__ float s_vmax[4];
@@ -469,14 +469,23 @@ void decode_split_kernel(const DecodeArgs a) {
   // pass below, so the workgroup waits on one memory round trip, not three.
   TileRegs r0, r1, r2;
   // staged scales: 8 tokens per thread and array, the chunk starting at c0 (a
-  // multiple of 32 tokens, so the 16-byte loads are aligned); tokens past L
-  // read as zero, those past c1 are masked where they are used
+  // multiple of 32 tokens, so with aligned scale rows the 16-byte loads are
+  // aligned; otherwise eight 2-byte loads per array); tokens past L read as
+  // zero, those past c1 are masked where they are used
   u32x4 st_k{0u, 0u, 0u, 0u}, st_v{0u, 0u, 0u, 0u};
   if constexpr (STAGED) {
     const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksslice, a.sc_ext);
     const bool in = 8 * tid < a.chunk;
-    st_k = buf_load16_nt(rks, in ? static_cast<unsigned>(c0 + 8 * tid) * 2u : kOOB);
-    st_v = buf_load16_nt(rvs, in ? static_cast<unsigned>(c0 + 8 * tid) * 2u : kOOB);
+    const unsigned off = in ? static_cast<unsigned>(c0 + 8 * tid) * 2u : kOOB;
+    if constexpr (SCVEC) {
+      st_k = buf_load16_nt(rks, off);
+      st_v = buf_load16_nt(rvs, off);
+    } else {
+      const u32x2 k0 = load_scales4_at<false>(rks, off), k1 = load_scales4_at<false>(rks, off + 8u);
+      const u32x2 v0s = load_scales4_at<false>(rvs, off), v1s = load_scales4_at<false>(rvs, off + 8u);
+      st_k = u32x4{k0[0], k0[1], k1[0], k1[1]};
+      st_v = u32x4{v0s[0], v0s[1], v1s[0], v1s[1]};
+    }
   }
   load_tile(r0, tile_t0(0), false);  // staged scales of these two: after the barrier below
   load_tile(r1, tile_t0(1), false);
@@ -800,12 +809,15 @@ int fa_launch_decode(const fa_decode_params *p, void *stream) {
   const unsigned grid1 = static_cast<unsigned>(p->num_splits + (window ? 1 : 0)) * p->Hkv * p->B;
   const dim3 g1(grid1), b1(kDecodeThreads);
   const bool fp8 = p->kv_format == FA_KV_FP8_E4M3_TOKHEAD_F16SCALE;
-  const bool staged = a.sc_vec && a.chunk <= kStageTok;
+  const bool staged = a.chunk <= kStageTok;
   fa_log_launch("decode_split_kernel", grid1, kDecodeThreads, 0,
                 "kv=%s scales=%s B=%d Hq=%d Hkv=%d L=%d splits=%d chunk=%d window=%d", fp8 ? "fp8" : "int8",
-                staged ? "staged" : (a.sc_vec ? "vec8" : "scalar2"), a.B, a.Hq, a.Hkv, a.L, a.nsplit, a.chunk, a.W);
-  if (staged && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true, true>), g1, b1, 0, s, a);
-  else if (staged) hipLaunchKernelGGL((decode_split_kernel<true, false, true>), g1, b1, 0, s, a);
+                staged ? (a.sc_vec ? "staged" : "staged2") : (a.sc_vec ? "vec8" : "scalar2"), a.B, a.Hq, a.Hkv, a.L,
+                a.nsplit, a.chunk, a.W);
+  if (staged && a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true, true>), g1, b1, 0, s, a);
+  else if (staged && a.sc_vec) hipLaunchKernelGGL((decode_split_kernel<true, false, true>), g1, b1, 0, s, a);
+  else if (staged && fp8) hipLaunchKernelGGL((decode_split_kernel<false, true, true>), g1, b1, 0, s, a);
+  else if (staged) hipLaunchKernelGGL((decode_split_kernel<false, false, true>), g1, b1, 0, s, a);
   else if (a.sc_vec && fp8) hipLaunchKernelGGL((decode_split_kernel<true, true>), g1, b1, 0, s, a);
   else if (a.sc_vec) hipLaunchKernelGGL((decode_split_kernel<true, false>), g1, b1, 0, s, a);
   else if (fp8) hipLaunchKernelGGL((decode_split_kernel<false, true>), g1, b1, 0, s, a);
