@@ -169,6 +169,17 @@ __device__ __forceinline__ int exp_of(float x) {
   return x > 0.f ? e : 0;
 }
 
+// The value lane (l ^ 16) holds: v_permlane16_swap exchanges the odd rows of
+// its first operand with the even rows of its second, so with x in both the
+// second result holds, in each even row, the row above, and the first, in
+// each odd row, the row below.  No LDS round trip (a width-64 shuffle would
+// be an LDS permute).
+__device__ __forceinline__ float xor16_lanes(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) == 0 ? r[1] : r[0]);
+}
+
 // Four fp16 scales at byte offset voff.  Offsets always go in the per-lane
 // operand, which the buffer range check covers (the scalar offset operand is
 // left at zero everywhere in this library).
@@ -308,8 +319,8 @@ __device__ __attribute__((always_inline)) void decode_window_wg(const DecodeArgs
         sc[4 * tb + i] = s2;
         mx = fmaxf(mx, s2);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, xor16_lanes(mx));
+    mx = fmaxf(mx, swap_halves(mx));
     const float m_new = fmaxf(m_run, mx);      // finite: the tile holds a token
     const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
     float lsum = 0.f;
@@ -615,8 +626,8 @@ void decode_split_kernel(const DecodeArgs a) {
         mx = fmaxf(mx, s);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, xor16_lanes(mx));
+    mx = fmaxf(mx, swap_halves(mx));
     // lazy running max: the O rescale runs only when some row's max moved by
     // more than the slack (probabilities stay below 2^kRescaleSlack)
     const bool move = mx > m_run + kRescaleSlack;
