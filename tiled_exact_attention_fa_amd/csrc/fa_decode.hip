@@ -346,8 +346,8 @@ __device__ __attribute__((always_inline)) void decode_window_wg(const DecodeArgs
   }
 
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  l_tot += xor16_lanes(l_tot);
+  l_tot += swap_halves(l_tot);
   if (n < G) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -530,8 +530,8 @@ void decode_split_kernel(const DecodeArgs a) {
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(qv[e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = fmaxf(amax, xor16_lanes(amax));
+    amax = fmaxf(amax, swap_halves(amax));
     const int eq = amax > 0.f ? min(14 - exp_of(amax), 100) : 0;  // amax * 2^eq in [2^13, 2^14)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -570,8 +570,12 @@ void decode_split_kernel(const DecodeArgs a) {
       fold(vt0, vs_lo0, vs_hi0);
       for (int t = vt0 + 8 * 64; t < v1; t += 8 * 64) fold(t, load_scales4<SCVEC>(rvs, t), load_scales4<SCVEC>(rvs, t + 4));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    vmax = fmaxf(vmax, swap_halves(vmax));
+    vmax = fmaxf(vmax, xor16_lanes(vmax));
+    vmax = fmaxf(vmax, row16_xor<8>(vmax));
+    vmax = fmaxf(vmax, row16_xor<4>(vmax));
+    vmax = fmaxf(vmax, row16_xor<2>(vmax));
+    vmax = fmaxf(vmax, row16_xor<1>(vmax));
     // every wavefront's tiles spread over the whole chunk: take the chunk's maximum
     if (lane == 0) s_vmax[wave] = vmax;
     __syncthreads();
@@ -699,8 +703,8 @@ void decode_split_kernel(const DecodeArgs a) {
 
   // ---- wavefront partial: O_w = O_acc / (l 2^fw), lse2_w = m + log2 l ----
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  l_tot += xor16_lanes(l_tot);
+  l_tot += swap_halves(l_tot);
   if (n < G) {
     const float inv = l_tot > 0.f ? ldexpf(1.f / l_tot, -fw) : 0.f;
 #pragma unroll
