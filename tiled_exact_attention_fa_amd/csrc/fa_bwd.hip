@@ -182,8 +182,11 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf(static_cast<float>(o8[e]), static_cast<float>(d8[e]), s);
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  // the group's sum by DPP exchanges within the 16-lane row (no LDS permute)
+  s += row16_xor<8>(s);
+  s += row16_xor<4>(s);
+  s += row16_xor<2>(s);
+  s += row16_xor<1>(s);
   if (r < rows && c == 0) a.rowdot[r] = s;
 }
 
