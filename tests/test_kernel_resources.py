@@ -57,3 +57,14 @@ def test_no_kernel_spills():
         if r["scratch_bytes"] > limit or (limit == 0 and r["vgpr_spill"]):
             bad[name] = r
     assert not bad, f"kernels spilling to scratch: {json.dumps(bad, indent=1)}"
+
+
+def test_hot_kernels_keep_two_waves_per_simd():
+    # The prefill, backward and decode loops hide one wave's memory and
+    # vector latency behind the other wave of its SIMD; a kernel grown past
+    # 256 registers would run one wave per SIMD and lose that silently.
+    rep = _report()
+    hot = ("fwd_mfma16_kernel", "fwd_fp8_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "decode_split_kernel")
+    low = {name: r["waves_per_simd"] for name, r in rep.items()
+           if any(f in name for f in hot) and r["waves_per_simd"] < 2}
+    assert not low, f"kernels below two waves per SIMD: {low}"
